@@ -1,0 +1,216 @@
+/*
+ * Reference oracle for one layer of the hybrid-head decode-attention step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or constant with
+ * the HIP path.
+ *
+ * It is a plain, slow, obviously-correct evaluation of the definitions, in
+ * double precision, parallelised only over independent (sequence, KV head)
+ * pairs.  Sources (cited by title and section):
+ *   [Digest]  "LycheeDecode: Accelerating Long-Context LLM Inference via
+ *             Hybrid-Head Sparse Decoding" -- long-form paper digest
+ *             (paper-graph-ui), section 3.4 "Detailed, Sentence-Based
+ *             Technical Breakdown" (Eq. 1, Eq. 2, Eq. 3, the propagation and
+ *             layer-0 rules, the complete decoding loop = Algorithm 1, and
+ *             the hyper-parameter summary's GQA pooling rule).
+ *   [Notes]   papernotes.org notes on the same paper, "方法详解 / 关键设计"
+ *             items 1 and 2 (retrieval heads, sparse heads).
+ *
+ * Readings taken where the pages are silent (each one is also listed in the
+ * design notes of the repository):
+ *   R1  roles and critical-token sets are per KV head; all G query heads of
+ *       a KV head share them (budgets on the pages are counted in KV heads).
+ *   R2  the selection score of a KV head is the mean of its G query heads'
+ *       pre-softmax logits (= logits of the average-pooled query), ranked
+ *       descending; softmax is monotone, so this ranks A of Eq. 2.
+ *   R3  ties in the selection score go to the lower token index.
+ *   R4  S is stored as k int32 per (sequence, KV head), ascending; when the
+ *       context n is shorter than k only min(k, n) entries are valid and
+ *       the rest are -1.
+ *   R5  no causal mask, no forced sink / recent tokens; rows >= n are never
+ *       read; scale 1/sqrt(d) for both head kinds.
+ *   R6  query head h reads KV head floor(h / G).
+ *
+ * Parity status: pinned (see the header of oracle/__init__.py for the list
+ * of pins and the tests that hold them).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG -1
+#define ORACLE_ERR_S_RANGE -2
+#define ORACLE_ERR_NCTX -3
+#define ORACLE_ERR_MEM -4
+
+/* Element read: dtype 0 = IEEE fp32, dtype 1 = bfloat16 stored as uint16
+ * (the upper 16 bits of an fp32).  Both convert to double exactly. */
+static double elem(const void* base, int dtype, size_t i) {
+    if (dtype == 0) return (double)((const float*)base)[i];
+    uint32_t bits = ((uint32_t)((const uint16_t*)base)[i]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Dot product of query row (q_off) with cache row (k_off), both of length d,
+ * accumulated in double in index order. */
+static double dot_row(const void* q, size_t q_off, const void* kc, size_t k_off,
+                      int d, int dtype) {
+    double s = 0.0;
+    for (int t = 0; t < d; ++t) s += elem(q, dtype, q_off + t) * elem(kc, dtype, k_off + t);
+    return s;
+}
+
+/* Ordering for top-k [Digest 3.4 Eq. 2 with reading R3]: larger score first,
+ * equal scores by smaller index first.  A strict total order. */
+typedef struct { double s; int32_t j; } scored;
+static int cmp_desc_score_asc_index(const void* a, const void* b) {
+    const scored* x = (const scored*)a;
+    const scored* y = (const scored*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+static int cmp_int_asc(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+/* Softmax-weighted sum over a list of rows [Digest 3.4 Eq. 1 and Eq. 3]:
+ *   w_r = exp(z_r - max z),  out = sum_r (w_r / sum w) * V[row_r].
+ * rows == NULL means rows 0..cnt-1. */
+static void softmax_weighted_sum(const double* z, const int32_t* rows, int cnt,
+                                 const void* vc, size_t v_base, int d, int dtype,
+                                 double* out) {
+    double m = -INFINITY;
+    for (int r = 0; r < cnt; ++r) if (z[r] > m) m = z[r];
+    double Z = 0.0;
+    for (int r = 0; r < cnt; ++r) Z += exp(z[r] - m);
+    for (int t = 0; t < d; ++t) out[t] = 0.0;
+    for (int r = 0; r < cnt; ++r) {
+        double p = exp(z[r] - m) / Z;
+        size_t row = rows ? (size_t)rows[r] : (size_t)r;
+        for (int t = 0; t < d; ++t) out[t] += p * elem(vc, dtype, v_base + row * (size_t)d + t);
+    }
+}
+
+/*
+ * One layer of the step (the per-layer body of Algorithm 1 in [Digest 3.4],
+ * attention part only).
+ *
+ *   q        [B, Hq, d]           dtype
+ *   kc, vc   [B, Hkv, max_ctx, d] dtype
+ *   role     [Hkv]  1 = retrieval, 0 = sparse            (reading R1)
+ *   S_in     [B, Hkv, k] or NULL when every role is retrieval
+ *   S_out    [B, Hkv, k]          written for every head
+ *   out      [B, Hq, d]  double
+ *   n_ctx    [B]        1 <= n_ctx[b] <= max_ctx
+ *   scores   optional [B, Hkv, max_ctx] double: the pooled selection score of
+ *            every retrieval head (reading R2); untouched for sparse heads
+ *   nthreads OpenMP threads (<= 0: library default)
+ * Returns ORACLE_OK or a negative error code.
+ */
+int oracle_layer(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
+                 const void* q, const void* kc, const void* vc,
+                 const uint8_t* role, const int32_t* S_in, int32_t* S_out,
+                 double* out, const int32_t* n_ctx, int k, double* scores,
+                 int nthreads) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_ctx <= 0 || k <= 0) return ORACLE_ERR_ARG;
+    if (Hq % Hkv != 0 || (dtype != 0 && dtype != 1)) return ORACLE_ERR_ARG;
+    if (!q || !kc || !vc || !role || !S_out || !out || !n_ctx) return ORACLE_ERR_ARG;
+    for (int g = 0; g < Hkv; ++g)
+        if (!role[g] && !S_in) return ORACLE_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        if (n_ctx[b] < 1 || n_ctx[b] > max_ctx) return ORACLE_ERR_NCTX;
+
+    const int G = Hq / Hkv;
+    const double c = 1.0 / sqrt((double)d);          /* 1/sqrt(d_k), Eq. 1 and Eq. 3 */
+    int status = ORACLE_OK;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bg = 0; bg < B * Hkv; ++bg) {
+        const int b = bg / Hkv, g = bg % Hkv;
+        const int n = n_ctx[b];
+        const int ke = k < n ? k : n;                       /* reading R4 */
+        const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)max_ctx * d;
+        int32_t* s_out = S_out + ((size_t)b * Hkv + g) * k;
+
+        if (role[g]) {
+            /* Retrieval head: dense attention over all n tokens (Eq. 1), then
+             * S^(l+1) = argsTopK(A, k) (Eq. 2) on the GQA-pooled score. */
+            double* z = (double*)malloc(sizeof(double) * (size_t)n);
+            double* pooled = (double*)calloc((size_t)n, sizeof(double));
+            scored* order = (scored*)malloc(sizeof(scored) * (size_t)n);
+            if (!z || !pooled || !order) {
+                free(z); free(pooled); free(order);
+#pragma omp atomic write
+                status = ORACLE_ERR_MEM;
+                continue;
+            }
+            for (int i = 0; i < G; ++i) {
+                const int h = g * G + i;                    /* reading R6 */
+                const size_t q_off = ((size_t)b * Hq + h) * d;
+                for (int j = 0; j < n; ++j) {
+                    z[j] = c * dot_row(q, q_off, kc, kv_base + (size_t)j * d, d, dtype);
+                    pooled[j] += z[j];
+                }
+                softmax_weighted_sum(z, NULL, n, vc, kv_base, d, dtype, out + q_off);
+            }
+            for (int j = 0; j < n; ++j) {
+                pooled[j] /= (double)G;                     /* mean of the G logits, R2 */
+                order[j].s = pooled[j];
+                order[j].j = j;
+            }
+            if (scores) {
+                double* dst = scores + ((size_t)b * Hkv + g) * (size_t)max_ctx;
+                memcpy(dst, pooled, sizeof(double) * (size_t)n);
+            }
+            qsort(order, (size_t)n, sizeof(scored), cmp_desc_score_asc_index);
+            for (int r = 0; r < ke; ++r) s_out[r] = order[r].j;
+            qsort(s_out, (size_t)ke, sizeof(int32_t), cmp_int_asc);
+            for (int r = ke; r < k; ++r) s_out[r] = -1;
+            free(z); free(pooled); free(order);
+        } else {
+            /* Sparse head: attention over the inherited rows only (Eq. 3), and
+             * S^(l+1) = S^(l) unchanged. */
+            const int32_t* s_in = S_in + ((size_t)b * Hkv + g) * k;
+            int bad = 0;
+            for (int r = 0; r < ke; ++r)
+                if (s_in[r] < 0 || s_in[r] >= n) bad = 1;
+            if (bad) {
+#pragma omp atomic write
+                status = ORACLE_ERR_S_RANGE;
+                continue;
+            }
+            double* z = (double*)malloc(sizeof(double) * (size_t)ke);
+            if (!z) {
+#pragma omp atomic write
+                status = ORACLE_ERR_MEM;
+                continue;
+            }
+            for (int i = 0; i < G; ++i) {
+                const int h = g * G + i;
+                const size_t q_off = ((size_t)b * Hq + h) * d;
+                for (int r = 0; r < ke; ++r)
+                    z[r] = c * dot_row(q, q_off, kc, kv_base + (size_t)s_in[r] * d, d, dtype);
+                softmax_weighted_sum(z, s_in, ke, vc, kv_base, d, dtype, out + q_off);
+            }
+            if (s_out != s_in) memmove(s_out, s_in, sizeof(int32_t) * (size_t)k);
+            free(z);
+        }
+    }
+    return status;
+}

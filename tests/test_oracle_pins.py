@@ -1,0 +1,310 @@
+"""Pins that hold the oracle to facts other than its own code.
+
+Each test fixes the oracle against a closed form, an invariant, a special case
+or brute force, chosen so that a dropped term, a wrong sign, index, scale or
+operand, or pooling probabilities instead of logits, fails at least one.
+Passages: the long-form digest "LycheeDecode: Accelerating Long-Context LLM
+Inference via Hybrid-Head Sparse Decoding", section 3.4 (Eq. 1-3, S
+propagation, layer-0 rule, Algorithm 1, GQA pooling line).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from goldens import cases as golden_cases
+
+TIGHT = 1e-12
+
+
+def _f32_case(rng, B, Hq, Hkv, d, max_ctx, n=None, dyadic=False):
+    def draw(shape):
+        x = rng.standard_normal(shape)
+        if dyadic:                       # multiples of 2^-10: sums stay exact
+            x = np.round(x * 1024) / 1024
+        return x.astype(np.float32)
+    q = draw((B, Hq, d))
+    kc = draw((B, Hkv, max_ctx, d))
+    vc = draw((B, Hkv, max_ctx, d))
+    n_ctx = np.full(B, max_ctx if n is None else n, dtype=np.int32)
+    return q, kc, vc, n_ctx
+
+
+# ---------------------------------------------------------------- worked examples
+
+@pytest.mark.parametrize("case", golden_cases(), ids=lambda c: c["name"])
+def test_golden_worked_examples(case):
+    """Hand-derived closed forms (tests/golden/*.json), S chained over layers."""
+    S = None
+    n_ctx = np.array(case["n_ctx"], dtype=np.int32)
+    for li, lay in enumerate(case["layers"]):
+        out, S, _ = oracle.layer(lay["q"], lay["k"], lay["v"], lay["role"], S, n_ctx, case["k"])
+        np.testing.assert_allclose(out, lay["expect_out"], rtol=0, atol=TIGHT,
+                                   err_msg=f"{case['file']} layer {li}")
+        np.testing.assert_array_equal(S, lay["expect_S"], err_msg=f"{case['file']} layer {li}")
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_identical_keys_give_mean_of_values_and_lowest_indices(G):
+    """All keys equal -> uniform weights -> out = mean of V rows; every score
+    ties, so S = {0..k-1} (lower index wins)."""
+    rng = np.random.default_rng(7)
+    Hkv, d, n, k = 2, 64, 300, 37
+    q, kc, vc, n_ctx = _f32_case(rng, 1, Hkv * G, Hkv, d, n)
+    kc[:] = kc[:, :, :1, :]
+    out, S, _ = oracle.layer(q, kc, vc, np.ones(Hkv, np.uint8), None, n_ctx, k)
+    for h in range(Hkv * G):
+        expect = vc[0, h // G].astype(np.float64).mean(axis=0)
+        np.testing.assert_allclose(out[0, h], expect, rtol=0, atol=TIGHT)
+    np.testing.assert_array_equal(S, np.broadcast_to(np.arange(k, dtype=np.int32), S.shape))
+
+
+def test_planted_dominant_key_selected_and_returned():
+    """A key aligned with the group's queries with logit gap D >= 40 over all
+    others: it is selected, and |out - V[j*]| <= 2 (n-1) e^-D max|V|."""
+    rng = np.random.default_rng(11)
+    G, d, n, k = 4, 64, 1000, 16
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = (u[None, :] + 0.05 * rng.standard_normal((G, d))).astype(np.float32)[None]
+    kc = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    vc = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    jstar = 617
+    kc[0, 0, jstar] = (500.0 * u).astype(np.float32)
+    out, S, _ = oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, np.array([n], np.int32), k)
+    c = 1 / math.sqrt(d)
+    z = c * np.einsum("hd,nd->hn", q[0].astype(np.float64), kc[0, 0].astype(np.float64))
+    gap = min(z[h, jstar] - np.max(np.delete(z[h], jstar)) for h in range(G))
+    assert gap >= 40.0, "precondition: planted gap"
+    assert jstar in S[0, 0]
+    bound = 2 * (n - 1) * math.exp(-gap) * np.abs(vc).max()
+    for h in range(G):
+        assert np.abs(out[0, h] - vc[0, 0, jstar]).max() <= max(bound, 1e-15)
+
+
+def test_constant_value_rows_reproduce_the_constant():
+    """Weights sum to one: V rows all equal to w give out = w, for both kinds."""
+    rng = np.random.default_rng(3)
+    q, kc, vc, n_ctx = _f32_case(rng, 1, 8, 2, 64, 500)
+    w = rng.standard_normal(64).astype(np.float32)
+    vc[:] = w
+    out, S, _ = oracle.layer(q, kc, vc, np.ones(2, np.uint8), None, n_ctx, 40)
+    np.testing.assert_allclose(out[0], np.broadcast_to(w.astype(np.float64), (8, 64)), rtol=0, atol=1e-12)
+    out2, _, _ = oracle.layer(q, kc, vc, np.array([0, 0], np.uint8), S, n_ctx, 40)
+    np.testing.assert_allclose(out2[0], np.broadcast_to(w.astype(np.float64), (8, 64)), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- brute force
+
+def _brute_force_topk(s, k):
+    """Max score-sum subset; among those the lexicographically smallest sorted
+    index tuple.  Equals 'larger score first, then lower index'."""
+    best_sum, best = None, None
+    for comb in itertools.combinations(range(len(s)), k):
+        tot = sum(s[j] for j in comb)
+        if best_sum is None or tot > best_sum or (tot == best_sum and comb < best):
+            best_sum, best = tot, comb
+    return list(best)
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_topk_matches_brute_force_with_ties(G):
+    """Integer-valued logits full of ties (d = 4, q = 2 e_i so logit = K[j, i]);
+    with G = 2 the pooled score is the mean of the two heads' logits."""
+    rng = np.random.default_rng(100 + G)
+    for trial in range(150):
+        n = int(rng.integers(1, 13))
+        k = int(rng.integers(1, 6))
+        q = np.zeros((1, G, 4), np.float32)
+        for h in range(G):
+            q[0, h, h] = 2.0
+        kc = np.zeros((1, 1, n, 4), np.float32)
+        kc[0, 0, :, :G] = rng.integers(-2, 3, size=(n, G))
+        vc = rng.standard_normal((1, 1, n, 4)).astype(np.float32)
+        _, S, _ = oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, np.array([n], np.int32), k)
+        pooled = [sum(float(kc[0, 0, j, h]) for h in range(G)) / G for j in range(n)]
+        ke = min(k, n)
+        expect = _brute_force_topk(pooled, ke) + [-1] * (k - ke)
+        assert S[0, 0].tolist() == expect, (trial, pooled, k)
+
+
+# ---------------------------------------------------------------- special cases
+
+def test_sparse_over_all_positions_equals_dense():
+    """S = all n positions (k = n): Eq. 3 reduces to Eq. 1."""
+    rng = np.random.default_rng(5)
+    n = 257
+    q, kc, vc, n_ctx = _f32_case(rng, 2, 8, 2, 64, n)
+    dense, _, _ = oracle.layer(q, kc, vc, np.ones(2, np.uint8), None, n_ctx, n)
+    S = np.broadcast_to(np.arange(n, dtype=np.int32), (2, 2, n)).copy()
+    sparse, S_out, _ = oracle.layer(q, kc, vc, np.zeros(2, np.uint8), S, n_ctx, n)
+    np.testing.assert_allclose(sparse, dense, rtol=0, atol=TIGHT)
+    np.testing.assert_array_equal(S_out, S)
+
+
+def test_masked_softmax_identity():
+    """Sparse attention over S equals dense attention after every key outside S
+    is moved to logit <= -1000 (exp underflows to exactly 0 in fp64)."""
+    rng = np.random.default_rng(9)
+    G, d, n, k = 4, 64, 400, 50
+    base = rng.standard_normal(d)
+    q = (base[None] + 0.1 * rng.standard_normal((G, d))).astype(np.float32)[None]
+    kc = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    vc = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    S = np.sort(rng.choice(n, size=k, replace=False)).astype(np.int32)[None, None]
+    out_sparse, _, _ = oracle.layer(q, kc, vc, np.zeros(1, np.uint8), S, np.array([n], np.int32), k)
+    qbar = q[0].astype(np.float64).mean(axis=0)
+    far = (-1e5 * qbar / np.dot(qbar, qbar)).astype(np.float32)
+    k2 = kc.copy()
+    outside = np.setdiff1d(np.arange(n), S[0, 0])
+    k2[0, 0, outside] = far
+    z_far = (q[0].astype(np.float64) @ far.astype(np.float64)) / math.sqrt(d)
+    assert np.all(z_far <= -1000), "precondition: pushed keys are far below"
+    out_dense, _, _ = oracle.layer(q, k2, vc, np.ones(1, np.uint8), None, np.array([n], np.int32), k)
+    np.testing.assert_allclose(out_sparse, out_dense, rtol=0, atol=TIGHT)
+
+
+def test_gqa_head_map_matches_expanded_cache():
+    """Query head h reads KV head floor(h/G): running GQA equals running MHA on
+    a cache with each KV head repeated G times (outputs)."""
+    rng = np.random.default_rng(21)
+    G, Hkv, d, n = 4, 2, 64, 333
+    q, kc, vc, n_ctx = _f32_case(rng, 1, G * Hkv, Hkv, d, n)
+    out_gqa, _, _ = oracle.layer(q, kc, vc, np.ones(Hkv, np.uint8), None, n_ctx, 8)
+    kx = np.repeat(kc, G, axis=1)
+    vx = np.repeat(vc, G, axis=1)
+    out_mha, _, _ = oracle.layer(q, kx, vx, np.ones(G * Hkv, np.uint8), None, n_ctx, 8)
+    np.testing.assert_allclose(out_gqa, out_mha, rtol=0, atol=TIGHT)
+
+
+def test_pooled_score_is_mean_of_head_logits_and_single_head_is_own():
+    """With G identical query heads the pooled score equals each head's logit,
+    so S is the top-k of that one head (checked against G = 1)."""
+    rng = np.random.default_rng(22)
+    d, n, k = 64, 500, 33
+    q1, kc, vc, n_ctx = _f32_case(rng, 1, 1, 1, d, n)
+    q4 = np.repeat(q1, 4, axis=1)
+    _, S1, s1 = oracle.layer(q1, kc, vc, np.ones(1, np.uint8), None, n_ctx, k, want_scores=True)
+    _, S4, s4 = oracle.layer(q4, kc, vc, np.ones(1, np.uint8), None, n_ctx, k, want_scores=True)
+    np.testing.assert_array_equal(S1, S4)
+    np.testing.assert_allclose(s4, s1, rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_outputs_lie_in_the_value_hull():
+    rng = np.random.default_rng(13)
+    q, kc, vc, n_ctx = _f32_case(rng, 1, 8, 2, 64, 700)
+    out, S, _ = oracle.layer(q, kc, vc, np.ones(2, np.uint8), None, n_ctx, 64)
+    for h in range(8):
+        v = vc[0, h // 4].astype(np.float64)
+        assert np.all(out[0, h] >= v.min(axis=0) - 1e-12) and np.all(out[0, h] <= v.max(axis=0) + 1e-12)
+    out2, _, _ = oracle.layer(q, kc, vc, np.zeros(2, np.uint8), S, n_ctx, 64)
+    for h in range(8):
+        v = vc[0, h // 4][S[0, h // 4]].astype(np.float64)
+        assert np.all(out2[0, h] >= v.min(axis=0) - 1e-12) and np.all(out2[0, h] <= v.max(axis=0) + 1e-12)
+
+
+def test_logit_shift_invariance():
+    """Adding one vector w to every key shifts each head's logits by a constant
+    (q_h.w/sqrt(d)): outputs unchanged, pooled ranking unchanged.  Dyadic
+    inputs keep K + w exact in fp32."""
+    rng = np.random.default_rng(17)
+    q, kc, vc, n_ctx = _f32_case(rng, 1, 8, 2, 64, 600, dyadic=True)
+    w = np.round(rng.standard_normal(64) * 4).astype(np.float32)
+    out, S, _ = oracle.layer(q, kc, vc, np.ones(2, np.uint8), None, n_ctx, 50)
+    out2, S2, _ = oracle.layer(q, kc + w, vc, np.ones(2, np.uint8), None, n_ctx, 50)
+    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-11)
+    np.testing.assert_array_equal(S2, S)
+
+
+def test_row_permutation_equivariance():
+    """Permuting cache rows by pi leaves outputs unchanged and maps S by pi."""
+    rng = np.random.default_rng(19)
+    n, k = 512, 40
+    q, kc, vc, n_ctx = _f32_case(rng, 1, 8, 2, 64, n)
+    pi = rng.permutation(n)
+    out, S, _ = oracle.layer(q, kc, vc, np.ones(2, np.uint8), None, n_ctx, k)
+    out2, S2, _ = oracle.layer(q, kc[:, :, pi], vc[:, :, pi], np.ones(2, np.uint8), None, n_ctx, k)
+    np.testing.assert_allclose(out2, out, rtol=0, atol=TIGHT)
+    for g in range(2):
+        assert sorted(pi[S2[0, g]].tolist()) == S[0, g].tolist()
+
+
+def test_batch_rows_are_independent():
+    """A batch of two sequences with different contexts equals two runs of one."""
+    rng = np.random.default_rng(23)
+    max_ctx, k = 300, 20
+    q, kc, vc, _ = _f32_case(rng, 2, 8, 2, 64, max_ctx)
+    n_ctx = np.array([300, 171], np.int32)
+    kc[1, :, 171:] = np.nan
+    vc[1, :, 171:] = np.nan
+    role = np.array([1, 0], np.uint8)
+    S_in = np.stack([np.stack([np.arange(k), np.arange(k) * 3]) for _ in range(2)]).astype(np.int32)
+    out, S, _ = oracle.layer(q, kc, vc, role, S_in, n_ctx, k)
+    for b in range(2):
+        o1, s1, _ = oracle.layer(q[b:b + 1], kc[b:b + 1], vc[b:b + 1], role, S_in[b:b + 1], n_ctx[b:b + 1], k)
+        np.testing.assert_array_equal(out[b:b + 1], o1)
+        np.testing.assert_array_equal(S[b:b + 1], s1)
+    assert np.all(np.isfinite(out))
+
+
+# ---------------------------------------------------------------- propagation
+
+def test_sparse_head_forwards_S_bitwise_and_retrieval_ignores_S_in():
+    rng = np.random.default_rng(29)
+    q, kc, vc, n_ctx = _f32_case(rng, 1, 8, 2, 64, 256)
+    S_in = np.stack([np.sort(rng.choice(256, 16, replace=False)) for _ in range(2)])[None].astype(np.int32)
+    _, S_out, _ = oracle.layer(q, kc, vc, np.array([0, 1], np.uint8), S_in, n_ctx, 16)
+    np.testing.assert_array_equal(S_out[0, 0], S_in[0, 0])
+    garbage = S_in.copy()
+    garbage[0, 1] = np.arange(16)[::-1]
+    _, S_out2, _ = oracle.layer(q, kc, vc, np.array([0, 1], np.uint8), garbage, n_ctx, 16)
+    np.testing.assert_array_equal(S_out2[0, 1], S_out[0, 1])
+
+
+def test_all_sparse_chain_returns_layer0_S():
+    """Layers 1..L-1 all sparse: S after the last layer is the layer-0 S."""
+    w = synth.WORKLOADS["tiny_gqa"].replace(layers=4, n_retrieval=0)
+    layers = []
+    roles = synth.roles(w)
+    assert roles[1:].sum() == 0
+    for l in range(w.layers):
+        x = synth.layer_inputs(w, l)
+        layers.append((x["q"], x["k"], x["v"], roles[l]))
+    outs, Ss = oracle.step(layers, synth.n_ctx(w), w.k)
+    for S in Ss[1:]:
+        np.testing.assert_array_equal(S, Ss[0])
+
+
+def test_short_context_pads_with_minus_one():
+    rng = np.random.default_rng(31)
+    q, kc, vc, _ = _f32_case(rng, 1, 4, 1, 64, 40)
+    n_ctx = np.array([9], np.int32)
+    kc[0, 0, 9:] = np.nan
+    vc[0, 0, 9:] = np.nan
+    out, S, _ = oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, n_ctx, 16)
+    assert S[0, 0, :9].tolist() == list(range(9)) and S[0, 0, 9:].tolist() == [-1] * 7
+    assert np.all(np.isfinite(out))
+
+
+# ---------------------------------------------------------------- error paths
+
+def test_oracle_rejects_bad_arguments():
+    rng = np.random.default_rng(37)
+    q, kc, vc, n_ctx = _f32_case(rng, 1, 4, 1, 64, 32)
+    with pytest.raises(ValueError):
+        oracle.layer(q, kc, vc, np.zeros(1, np.uint8), None, n_ctx, 4)       # sparse without S
+    with pytest.raises(ValueError):
+        oracle.layer(q, kc, vc, np.zeros(1, np.uint8), np.array([[[0, 1, 2, 32]]], np.int32), n_ctx, 4)
+    with pytest.raises(ValueError):
+        oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, np.array([33], np.int32), 4)
+    with pytest.raises(ValueError):
+        oracle.step([(q, kc, vc, np.zeros(1, np.uint8))], n_ctx, 4)
