@@ -1,0 +1,300 @@
+// C ABI of the hybrid-head decode-attention step: argument validation (pure
+// host code), workspace carve-up, and the per-layer launch sequence
+//   attention (all heads, pooled)  ->  top-k select (retrieval heads only).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+#include <string>
+
+#include "../../include/lychee.h"
+#include "common.hpp"
+
+using namespace lychee;
+
+struct lychee_handle {
+    lychee_dims dims;
+    void* ws_base;
+    size_t ws_bytes;
+    Workspace ws;
+    hipStream_t stream;
+    int device;
+    int grid;            // persistent attention workgroups per launch
+    hipEvent_t ev_start;
+    hipEvent_t ev_stop;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lychee_status fail(lychee_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+lychee_status ok() {
+    g_last_error.clear();
+    return LYCHEE_OK;
+}
+
+lychee_status check_dims(const lychee_dims* d) {
+    if (!d) return fail(LYCHEE_ERR_INVALID_ARG, "dims is NULL");
+    if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->max_ctx < 1 ||
+        d->k_max < 1)
+        return fail(LYCHEE_ERR_INVALID_ARG, "dims must be positive (batch=%d Hq=%d Hkv=%d d=%d max_ctx=%d k_max=%d)",
+                    d->batch, d->n_q_heads, d->n_kv_heads, d->head_dim, d->max_ctx, d->k_max);
+    if (d->n_q_heads % d->n_kv_heads != 0)
+        return fail(LYCHEE_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", d->n_q_heads,
+                    d->n_kv_heads);
+    if (d->dtype != LYCHEE_F32 && d->dtype != LYCHEE_BF16)
+        return fail(LYCHEE_ERR_INVALID_ARG, "dtype %d is not LYCHEE_F32 or LYCHEE_BF16", d->dtype);
+    const int G = d->n_q_heads / d->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(LYCHEE_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", G);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(LYCHEE_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+    if (d->n_kv_heads > kMaxKvHeads)
+        return fail(LYCHEE_ERR_UNSUPPORTED, "n_kv_heads must be <= %d (got %d)", kMaxKvHeads, d->n_kv_heads);
+    if ((long long)d->batch * d->n_kv_heads > kMaxBH)
+        return fail(LYCHEE_ERR_UNSUPPORTED, "batch * n_kv_heads must be <= %d (got %lld)", kMaxBH,
+                    (long long)d->batch * d->n_kv_heads);
+    if (d->max_ctx > kMaxCtx)
+        return fail(LYCHEE_ERR_UNSUPPORTED, "max_ctx must be <= %d (got %d)", kMaxCtx, d->max_ctx);
+    if (d->k_max > d->max_ctx)
+        return fail(LYCHEE_ERR_INVALID_ARG, "k_max (%d) must be <= max_ctx (%d)", d->k_max, d->max_ctx);
+    return ok();
+}
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range span(const void* p, size_t bytes) {
+    const uintptr_t a = (uintptr_t)p;
+    return Range{a, a + bytes};
+}
+
+size_t elem_bytes(const lychee_dims* d) { return d->dtype == LYCHEE_BF16 ? 2u : 4u; }
+
+// Checks shared by the hybrid and dense entry points.
+lychee_status check_common(const lychee_dims* d, const void* q, const void* kc, const void* vc, const float* out,
+                           const int32_t* n_ctx) {
+    lychee_status s = check_dims(d);
+    if (s != LYCHEE_OK) return s;
+    if (!q || !kc || !vc || !out || !n_ctx) return fail(LYCHEE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    if (((uintptr_t)q | (uintptr_t)kc | (uintptr_t)vc) & 15u)
+        return fail(LYCHEE_ERR_INVALID_ARG, "q, k_cache and v_cache must be 16-byte aligned");
+    if (((uintptr_t)out | (uintptr_t)n_ctx) & 3u)
+        return fail(LYCHEE_ERR_INVALID_ARG, "out and n_ctx must be 4-byte aligned");
+    const size_t es = elem_bytes(d);
+    const size_t nq = (size_t)d->batch * d->n_q_heads * d->head_dim;
+    const size_t nkv = (size_t)d->batch * d->n_kv_heads * d->max_ctx * d->head_dim;
+    const Range r_out = span(out, nq * 4);
+    if (overlap(r_out, span(q, nq * es)) || overlap(r_out, span(kc, nkv * es)) || overlap(r_out, span(vc, nkv * es)) ||
+        overlap(r_out, span(n_ctx, (size_t)d->batch * 4)))
+        return fail(LYCHEE_ERR_INVALID_ARG, "out overlaps an input");
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lychee_status_str(lychee_status s) {
+    switch (s) {
+        case LYCHEE_OK: return "ok";
+        case LYCHEE_ERR_INVALID_ARG: return "invalid argument";
+        case LYCHEE_ERR_UNSUPPORTED: return "unsupported configuration";
+        case LYCHEE_ERR_HIP: return "HIP runtime error";
+        case LYCHEE_ERR_WORKSPACE: return "workspace too small or misaligned";
+        case LYCHEE_ERR_DEVICE_CHECK: return "device-side contract violation";
+    }
+    return "unknown status";
+}
+
+const char* lychee_last_error(void) { return g_last_error.c_str(); }
+
+size_t lychee_workspace_bytes(const lychee_dims* dims) {
+    if (check_dims(dims) != LYCHEE_OK) return 0;
+    return carve_workspace(nullptr, dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, dims->max_ctx,
+                           dims->k_max)
+        .total_bytes;
+}
+
+lychee_status lychee_validate_layer(const lychee_dims* d, const void* q, const void* kc, const void* vc,
+                                    const uint8_t* role_mask, const int32_t* S_in, const int32_t* S_out,
+                                    const float* out, const int32_t* n_ctx, int32_t k) {
+    lychee_status s = check_common(d, q, kc, vc, out, n_ctx);
+    if (s != LYCHEE_OK) return s;
+    if (!role_mask) return fail(LYCHEE_ERR_INVALID_ARG, "role_mask is NULL");
+    if (!S_out) return fail(LYCHEE_ERR_INVALID_ARG, "S_out is NULL");
+    if (k < 1 || k > d->k_max) return fail(LYCHEE_ERR_INVALID_ARG, "k must be in [1, k_max=%d] (got %d)", d->k_max, k);
+    bool any_sparse = false;
+    for (int g = 0; g < d->n_kv_heads; ++g) any_sparse |= (role_mask[g] == 0);
+    if (any_sparse && !S_in)
+        return fail(LYCHEE_ERR_INVALID_ARG, "S_in is NULL but role_mask has sparse heads (only layer 0 may omit S)");
+    if (((uintptr_t)S_out | (uintptr_t)S_in) & 3u)
+        return fail(LYCHEE_ERR_INVALID_ARG, "S_in and S_out must be 4-byte aligned");
+    const size_t sbytes = (size_t)d->batch * d->n_kv_heads * k * 4;
+    const Range r_so = span(S_out, sbytes);
+    if (S_in && S_in != S_out && overlap(r_so, span(S_in, sbytes)))
+        return fail(LYCHEE_ERR_INVALID_ARG, "S_out partially overlaps S_in (must be equal or disjoint)");
+    const size_t es = elem_bytes(d);
+    const size_t nq = (size_t)d->batch * d->n_q_heads * d->head_dim;
+    const size_t nkv = (size_t)d->batch * d->n_kv_heads * d->max_ctx * d->head_dim;
+    if (overlap(r_so, span(q, nq * es)) || overlap(r_so, span(kc, nkv * es)) || overlap(r_so, span(vc, nkv * es)) ||
+        overlap(r_so, span(out, nq * 4)) || overlap(r_so, span(n_ctx, (size_t)d->batch * 4)))
+        return fail(LYCHEE_ERR_INVALID_ARG, "S_out overlaps another argument");
+    if (S_in && overlap(span(S_in, sbytes), span(out, nq * 4)))
+        return fail(LYCHEE_ERR_INVALID_ARG, "out overlaps S_in");
+    return ok();
+}
+
+lychee_status lychee_create(const lychee_dims* dims, void* workspace, size_t workspace_bytes, void* stream,
+                            lychee_handle** out_handle) {
+    if (!out_handle) return fail(LYCHEE_ERR_INVALID_ARG, "out_handle is NULL");
+    *out_handle = nullptr;
+    lychee_status s = check_dims(dims);
+    if (s != LYCHEE_OK) return s;
+    const size_t need = lychee_workspace_bytes(dims);
+    if (!workspace || ((uintptr_t)workspace & 255u))
+        return fail(LYCHEE_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(LYCHEE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                hipSuccess)
+        return fail(LYCHEE_ERR_HIP, "cannot query the current HIP device");
+    lychee_handle* h = new lychee_handle();
+    h->dims = *dims;
+    h->ws_base = workspace;
+    h->ws_bytes = workspace_bytes;
+    h->ws = carve_workspace(workspace, dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, dims->max_ctx,
+                            dims->k_max);
+    h->stream = (hipStream_t)stream;
+    h->device = dev;
+    int grid = cus * 2;
+    if (grid > kMaxWG) grid = kMaxWG;
+    if (grid < 1) grid = 1;
+    h->grid = grid;
+    h->ev_start = nullptr;
+    h->ev_stop = nullptr;
+    if (hipMemsetAsync(h->ws.zero_begin, 0, h->ws.zero_bytes, h->stream) != hipSuccess) {
+        delete h;
+        return fail(LYCHEE_ERR_HIP, "clearing the workspace counters failed");
+    }
+    *out_handle = h;
+    return ok();
+}
+
+lychee_status lychee_set_stream(lychee_handle* h, void* stream) {
+    if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");
+    h->stream = (hipStream_t)stream;
+    return ok();
+}
+
+lychee_status lychee_set_profile_events(lychee_handle* h, void* start, void* stop) {
+    if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");
+    if ((start == nullptr) != (stop == nullptr))
+        return fail(LYCHEE_ERR_INVALID_ARG, "pass both events or neither");
+    h->ev_start = (hipEvent_t)start;
+    h->ev_stop = (hipEvent_t)stop;
+    return ok();
+}
+
+static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, const void* vc,
+                               const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out, float* out,
+                               const int32_t* n_ctx, int32_t k, bool hybrid) {
+    const lychee_dims& d = h->dims;
+    uint64_t bits = 0;
+    int n_retr = 0;
+    for (int g = 0; g < d.n_kv_heads; ++g) {
+        if (!hybrid || role_mask[g]) {
+            bits |= 1ull << g;
+            ++n_retr;
+        }
+    }
+    AttendParams ap{};
+    ap.q = q;
+    ap.kc = kc;
+    ap.vc = vc;
+    ap.S_in = S_in;
+    ap.S_out = S_out;
+    ap.out = out;
+    ap.n_ctx = n_ctx;
+    ap.ws = h->ws;
+    ap.role_bits = bits;
+    ap.B = d.batch;
+    ap.Hkv = d.n_kv_heads;
+    ap.max_ctx = d.max_ctx;
+    ap.k = hybrid ? k : 1;
+    ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+    const int G = d.n_q_heads / d.n_kv_heads;
+    if (h->ev_start && hipEventRecord(h->ev_start, h->stream) != hipSuccess)
+        return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
+    hipError_t e = launch_attend(ap, d.dtype, d.head_dim, G, hybrid, h->grid, h->stream);
+    if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+    if (h->ev_stop && hipEventRecord(h->ev_stop, h->stream) != hipSuccess)
+        return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
+    if (hybrid && n_retr > 0) {
+        SelectParams sp{};
+        sp.n_ctx = n_ctx;
+        sp.S_out = S_out;
+        sp.ws = h->ws;
+        sp.role_bits = bits;
+        sp.B = d.batch;
+        sp.Hkv = d.n_kv_heads;
+        sp.max_ctx = d.max_ctx;
+        sp.k = k;
+        sp.k_max = d.k_max;
+        sp.n_retrieval = n_retr;
+        e = launch_select(sp, h->stream);
+        if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "select launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+lychee_status lychee_decode_layer(lychee_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                                  const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out, float* out,
+                                  const int32_t* n_ctx, int32_t k) {
+    if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");
+    lychee_status s = lychee_validate_layer(&h->dims, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k);
+    if (s != LYCHEE_OK) return s;
+    return run_layer(h, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k, true);
+}
+
+lychee_status lychee_dense_decode_layer(lychee_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                                        float* out, const int32_t* n_ctx) {
+    if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");
+    lychee_status s = check_common(&h->dims, q, k_cache, v_cache, out, n_ctx);
+    if (s != LYCHEE_OK) return s;
+    return run_layer(h, q, k_cache, v_cache, nullptr, nullptr, nullptr, out, n_ctx, 1, false);
+}
+
+lychee_status lychee_check_device_errors(lychee_handle* h) {
+    if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");
+    uint32_t flag = 0;
+    if (hipStreamSynchronize(h->stream) != hipSuccess) return fail(LYCHEE_ERR_HIP, "stream synchronize failed");
+    if (hipMemcpy(&flag, h->ws.err, sizeof flag, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(LYCHEE_ERR_HIP, "reading the device error flag failed");
+    if (flag) {
+        if (hipMemset(h->ws.err, 0, sizeof flag) != hipSuccess)
+            return fail(LYCHEE_ERR_HIP, "clearing the device error flag failed");
+        return fail(LYCHEE_ERR_DEVICE_CHECK, "device error flag 0x%x (1: S_in entry outside [0, n_ctx); 2: select count mismatch)",
+                    flag);
+    }
+    return ok();
+}
+
+void lychee_destroy(lychee_handle* h) { delete h; }
+
+}  // extern "C"

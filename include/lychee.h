@@ -1,0 +1,150 @@
+/*
+ * lychee.h -- C ABI of the hybrid-head decode-attention step (gfx950 / MI355X).
+ *
+ * One call computes the attention part of one decoder layer for one decode
+ * step, as defined on the long-form digest "LycheeDecode: Accelerating
+ * Long-Context LLM Inference via Hybrid-Head Sparse Decoding"
+ * (paper-graph-ui), section 3.4:
+ *   - retrieval heads: dense single-query attention over all cached tokens
+ *     (Eq. 1) and S^(l+1) = argsTopK(A, k) (Eq. 2);
+ *   - sparse heads: attention over only the k rows named by the inherited set
+ *     S^(l) (Eq. 3), and S^(l+1) = S^(l);
+ *   - layer 0 is all retrieval (so the first call of a step passes S_in = NULL);
+ *   - with grouped-query attention the query heads of a KV head are average-
+ *     pooled before token selection (hyper-parameter summary).
+ * The split-K partials + log-sum-exp combine and the pooling of retrieval and
+ * sparse work into one set of equal-size work units follow the kernel
+ * description of the same section ("Custom Hybrid-Head Block-Sparse Decoding
+ * Kernel"), re-designed for CDNA4.
+ *
+ * Conventions
+ *   - Pointers are device pointers unless marked (host).
+ *   - Roles and critical-token sets are per KV head: query head h uses KV head
+ *     h / G (G = n_q_heads / n_kv_heads) and shares that head's role and S.
+ *   - Selection score of KV head g at token j: mean over its G query heads of
+ *     the pre-softmax logit q_h.K_j / sqrt(d); larger first, ties to the lower
+ *     token index.  S rows are ascending; when n_ctx[b] < k only the first
+ *     n_ctx[b] entries are valid and the rest are -1.
+ *   - Ownership: the caller owns every tensor and the workspace.  The library
+ *     never allocates or frees device memory; a handle holds host state only.
+ *   - Asynchrony: calls enqueue on the handle's stream and return at once.
+ *     No call in the decode path synchronises or copies to the host, so a
+ *     sequence of calls can be captured into a HIP graph.
+ *   - Errors: an integer status, never an exception.  Argument checks happen
+ *     on the host, before anything is enqueued.  A detail string is kept per
+ *     thread (lychee_last_error).
+ *   - Workspace invariant: the library's counters and histograms inside the
+ *     workspace are zero between calls; every call restores them.  Calls on
+ *     one workspace must be ordered (one stream, or explicit dependencies).
+ *   - Supported: head_dim 64 or 128; G in {1, 2, 4, 8}; n_kv_heads <= 64;
+ *     batch * n_kv_heads <= 1024; max_ctx <= 262144; dtype fp32 or bf16.
+ */
+#ifndef LYCHEE_H
+#define LYCHEE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LYCHEE_OK = 0,
+    LYCHEE_ERR_INVALID_ARG = -1,   /* null pointer, bad size, overlap, role/S mismatch */
+    LYCHEE_ERR_UNSUPPORTED = -2,   /* valid request outside the compiled variants */
+    LYCHEE_ERR_HIP = -3,           /* a HIP runtime call or kernel launch failed */
+    LYCHEE_ERR_WORKSPACE = -4,     /* workspace too small or misaligned */
+    LYCHEE_ERR_DEVICE_CHECK = -5   /* device-side contract violation seen (S_in entry out of range) */
+} lychee_status;
+
+typedef enum { LYCHEE_F32 = 0, LYCHEE_BF16 = 1 } lychee_dtype;
+
+/* Problem dimensions fixed for the life of a handle. */
+typedef struct {
+    int32_t batch;        /* B */
+    int32_t n_q_heads;    /* Hq */
+    int32_t n_kv_heads;   /* Hkv, divides Hq */
+    int32_t head_dim;     /* d */
+    int32_t max_ctx;      /* rows per (sequence, KV head) in the cache */
+    int32_t k_max;        /* largest critical-token budget k that will be passed */
+    int32_t dtype;        /* lychee_dtype of q, k_cache and v_cache */
+} lychee_dims;
+
+typedef struct lychee_handle lychee_handle;
+
+/* (host) Bytes of device workspace a handle with these dims needs; 0 if the
+ * dims are invalid or unsupported (see lychee_last_error). */
+size_t lychee_workspace_bytes(const lychee_dims* dims);
+
+/* Bind dims, a caller-owned device workspace (>= lychee_workspace_bytes,
+ * 256-byte aligned) and a HIP stream (hipStream_t passed as void*; NULL = the
+ * null stream) into a handle.  Enqueues one clear of the workspace's counter
+ * region on the stream (so do not call it inside graph capture). */
+lychee_status lychee_create(const lychee_dims* dims, void* workspace, size_t workspace_bytes,
+                            void* stream, lychee_handle** out_handle);
+
+/* One layer of the hybrid-head step (the per-layer attention of Algorithm 1
+ * in section 3.4 of the digest; Eq. 1, 2, 3 and the propagation rules).
+ *   q          [B, Hq, d]               dtype
+ *   k_cache    [B, Hkv, max_ctx, d]     dtype; rows >= n_ctx[b] are never read
+ *   v_cache    [B, Hkv, max_ctx, d]     dtype
+ *   role_mask  (host) [Hkv] uint8, nonzero = retrieval head, 0 = sparse head
+ *   S_in       [B, Hkv, k] int32 from the previous layer's S_out; may be NULL
+ *              only when every role is retrieval (layer 0).  Entries of a
+ *              sparse head's row must lie in [0, n_ctx[b]) for the first
+ *              min(k, n_ctx[b]) positions; other entries are ignored.
+ *   S_out      [B, Hkv, k] int32; retrieval rows get the new set (ascending,
+ *              -1 padded), sparse rows a copy of S_in's row.  S_out may equal
+ *              S_in (in place); any other overlap is rejected.
+ *   out        [B, Hq, d] fp32, fully overwritten
+ *   n_ctx      [B] int32 on the device, 1 <= n_ctx[b] <= max_ctx
+ *   k          1 <= k <= k_max
+ * Entries of S_in outside [0, n_ctx[b]) are skipped (never read through) and
+ * latch a flag reported by lychee_check_device_errors. */
+lychee_status lychee_decode_layer(lychee_handle* h,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out,
+                                  float* out, const int32_t* n_ctx, int32_t k);
+
+/* Dense all-heads decode attention over the same layout (every head attends
+ * to all n_ctx[b] tokens, Eq. 1 without selection): the baseline the hybrid
+ * step is compared with.  Same argument meanings as above. */
+lychee_status lychee_dense_decode_layer(lychee_handle* h, const void* q, const void* k_cache,
+                                        const void* v_cache, float* out, const int32_t* n_ctx);
+
+/* (host) Validate the arguments of lychee_decode_layer for these dims without
+ * touching the device: the same checks lychee_decode_layer runs first. */
+lychee_status lychee_validate_layer(const lychee_dims* dims,
+                                    const void* q, const void* k_cache, const void* v_cache,
+                                    const uint8_t* role_mask, const int32_t* S_in,
+                                    const int32_t* S_out, const float* out,
+                                    const int32_t* n_ctx, int32_t k);
+
+/* Rebind the handle to another stream (hipStream_t as void*). */
+lychee_status lychee_set_stream(lychee_handle* h, void* stream);
+
+/* Optional timing hook: when both are non-NULL (hipEvent_t as void*), every
+ * following decode/dense call records `start` right before its attention
+ * kernel and `stop` right after it, on the handle's stream.  NULL disables. */
+lychee_status lychee_set_profile_events(lychee_handle* h, void* start, void* stop);
+
+/* Synchronise the stream, read and clear the device-side error flag.
+ * Returns LYCHEE_ERR_DEVICE_CHECK if any call since the last check skipped an
+ * out-of-range S_in entry. */
+lychee_status lychee_check_device_errors(lychee_handle* h);
+
+/* Release the handle (host memory only). */
+void lychee_destroy(lychee_handle* h);
+
+/* Static string for a status code. */
+const char* lychee_status_str(lychee_status s);
+
+/* Detail message of the last failing call on this thread ("" if none). */
+const char* lychee_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LYCHEE_H */

@@ -59,6 +59,7 @@ class Workload:
     qk_scaled: bool = True         # q, K ~ N(0,1)/sqrt(d) when True, N(0,1) when False
     hh_frac: float = 0.0
     tie_frac: float = 0.0
+    ctx_list: tuple | None = None   # explicit per-sequence contexts (edge cases)
 
     @property
     def group(self) -> int:
@@ -104,6 +105,9 @@ def bf16_bits_to_f32(x: np.ndarray) -> np.ndarray:
 
 
 def n_ctx(w: Workload) -> np.ndarray:
+    if w.ctx_list is not None:
+        assert len(w.ctx_list) == w.batch and max(w.ctx_list) <= w.max_ctx
+        return np.asarray(w.ctx_list, dtype=np.int32)
     if w.ctx_range is None:
         return np.full(w.batch, w.max_ctx, dtype=np.int32)
     lo, hi = w.ctx_range

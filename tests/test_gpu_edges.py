@@ -1,0 +1,157 @@
+"""Edge cases of the HIP path against the oracle (GPU): ragged and tiny
+contexts around k, k = 1, every supported head_dim / group / dtype variant,
+in-place S, identical keys (LDS and global resolution paths of the top-k),
+determinism, out-of-range S entries, the dense baseline, the maximum
+context, and many sequences."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import log, make_handle, run_layer, to_device
+from parity import OUT_TOL, compare_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(name, seed, B, L, Hq, Hkv, d, max_ctx, k, dtype, n_retr, ctx_list=None, **kw):
+    return synth.Workload(name, seed, B, L, Hq, Hkv, d, max_ctx, k, dtype, n_retr, ctx_list=ctx_list, **kw)
+
+
+def _chain(w, n_layers=None, inplace=False):
+    import torch
+    handle = make_handle(w)
+    roles = synth.roles(w)
+    lens = synth.n_ctx(w)
+    n_ctx_dev = torch.from_numpy(lens).cuda()
+    S_prev_dev, S_prev = None, None
+    for l in range(n_layers or w.layers):
+        log(f"[{w.name}] layer {l} roles={roles[l].tolist()} n={lens.tolist()[:8]} k={w.k}")
+        x = synth.layer_inputs(w, l)
+        S_out_dev = S_prev_dev if (inplace and S_prev_dev is not None) else None
+        out, S, S_dev = run_layer(handle, x, roles[l], S_prev_dev, n_ctx_dev, w.k, S_out_dev=S_out_dev)
+        compare_layer(out, S, x, roles[l], S_prev, lens, w.k, w.dtype)
+        S_prev_dev, S_prev = S_dev, S
+    handle.check_device_errors()
+
+
+@pytest.mark.parametrize("k", [1, 16, 17, 64])
+def test_ragged_contexts_around_k(k):
+    ctx = (1, k - 1 if k > 1 else 2, k, k + 1, 600)
+    _chain(_w(f"ragged_k{k}", 50 + k, 5, 3, 32, 8, 128, 600, k, "bf16", 6, ctx_list=ctx, hh_frac=0.01))
+
+
+@pytest.mark.parametrize("dtype,d,Hq,Hkv", [
+    ("f32", 128, 32, 8), ("bf16", 64, 16, 8), ("bf16", 128, 64, 8), ("bf16", 128, 8, 8),
+    ("f32", 64, 16, 8), ("bf16", 64, 8, 1),
+])
+def test_every_variant(dtype, d, Hq, Hkv):
+    w = _w(f"var_{dtype}_{d}_{Hq}_{Hkv}", 70, 2, 3, Hq, Hkv, d, 3000, 100, dtype, max(1, Hkv // 2),
+           ctx_list=(3000, 1777), hh_frac=0.01)
+    _chain(w)
+
+
+def test_in_place_S():
+    _chain(_w("inplace", 80, 2, 5, 32, 8, 128, 5000, 300, "bf16", 8, ctx_list=(5000, 2345), hh_frac=0.01),
+           inplace=True)
+
+
+def test_all_sparse_then_all_retrieval_layers():
+    import torch
+    w = _w("roles", 81, 1, 4, 32, 8, 128, 4000, 256, "bf16", 0, ctx_list=(4000,), hh_frac=0.01)
+    roles = [np.ones(8, np.uint8), np.zeros(8, np.uint8), np.ones(8, np.uint8), np.zeros(8, np.uint8)]
+    handle = make_handle(w)
+    lens = synth.n_ctx(w)
+    n_ctx_dev = torch.from_numpy(lens).cuda()
+    S_dev, S = None, None
+    for l in range(4):
+        x = synth.layer_inputs(w, l)
+        out, S_new, S_dev_new = run_layer(handle, x, roles[l], S_dev, n_ctx_dev, w.k)
+        compare_layer(out, S_new, x, roles[l], S, lens, w.k, w.dtype)
+        if l == 1:
+            np.testing.assert_array_equal(S_new, S)
+        S_dev, S = S_dev_new, S_new
+
+
+@pytest.mark.parametrize("n,k", [(3000, 100), (3000, 3000), (20000, 64), (20000, 5000)])
+def test_identical_keys_select_lowest_indices(n, k):
+    """Every score ties: S must be exactly {0..k-1}; out = mean of V rows.
+    n = 20000 exceeds the LDS candidate buffer and takes the global passes."""
+    import torch
+    w = _w(f"ident_{n}_{k}", 90, 1, 1, 8, 2, 128, n, k, "bf16", 0, ctx_list=(n,))
+    x = synth.layer_inputs(w, 0)
+    x["k"][:] = x["k"][:, :, :1, :]
+    handle = make_handle(w)
+    n_ctx_dev = torch.from_numpy(synth.n_ctx(w)).cuda()
+    log(f"[identical] n={n} k={k}")
+    out, S, _ = run_layer(handle, x, np.ones(2, np.uint8), None, n_ctx_dev, k)
+    ke = min(k, n)
+    for g in range(2):
+        np.testing.assert_array_equal(S[0, g, :ke], np.arange(ke))
+    compare_layer(out, S, x, np.ones(2, np.uint8), None, synth.n_ctx(w), k, "bf16")
+    handle.check_device_errors()
+
+
+def test_bitwise_determinism():
+    import torch
+    w = _w("determinism", 95, 2, 2, 32, 8, 128, 20000, 512, "bf16", 4, ctx_list=(20000, 12345), hh_frac=0.01)
+    handle = make_handle(w)
+    n_ctx_dev = torch.from_numpy(synth.n_ctx(w)).cuda()
+    roles = synth.roles(w)
+    runs = []
+    for rep in range(2):
+        x0 = synth.layer_inputs(w, 0)
+        o0, S0, S0d = run_layer(handle, x0, roles[0], None, n_ctx_dev, w.k)
+        x1 = synth.layer_inputs(w, 1)
+        o1, S1, _ = run_layer(handle, x1, roles[1], S0d, n_ctx_dev, w.k)
+        runs.append((o0, S0, o1, S1))
+    for a, b in zip(runs[0], runs[1]):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b)
+
+
+def test_out_of_range_S_entries_are_skipped_and_reported():
+    import torch
+    import hybrid_head_sparse_amd as hhs
+    w = _w("bad_S", 96, 1, 2, 8, 2, 128, 1000, 16, "bf16", 0, ctx_list=(1000,))
+    handle = make_handle(w)
+    n_ctx_dev = torch.from_numpy(synth.n_ctx(w)).cuda()
+    x = synth.layer_inputs(w, 1)
+    S_in = np.tile(np.arange(16, dtype=np.int32) * 7, (1, 2, 1))
+    S_in[0, 0, 3] = -5
+    S_in[0, 1, 9] = 1003
+    S_dev = torch.from_numpy(S_in).cuda()
+    out, S, _ = run_layer(handle, x, np.zeros(2, np.uint8), S_dev, n_ctx_dev, 16)
+    assert np.all(np.isfinite(out))
+    with pytest.raises(hhs.LycheeError) as ei:
+        handle.check_device_errors()
+    assert ei.value.status == hhs.LYCHEE_ERR_DEVICE_CHECK
+    handle.check_device_errors()      # the flag was cleared
+
+
+def test_dense_baseline_matches_oracle():
+    import torch
+    for w in (synth.WORKLOADS["tiny_gqa"],
+              _w("dense_bf16", 97, 2, 1, 32, 8, 128, 9000, 64, "bf16", 0, ctx_list=(9000, 4321))):
+        handle = make_handle(w)
+        lens = synth.n_ctx(w)
+        x = synth.layer_inputs(w, 0)
+        dt = w.dtype
+        q, kc, vc = to_device(x["q"], dt), to_device(x["k"], dt), to_device(x["v"], dt)
+        out = torch.full((w.batch, w.n_q_heads, w.head_dim), float("nan"), device="cuda")
+        handle.dense_decode_layer(q, kc, vc, out, torch.from_numpy(lens).cuda())
+        torch.cuda.synchronize()
+        ref, _, _ = oracle.layer(x["q"], x["k"], x["v"], np.ones(w.n_kv_heads, np.uint8), None, lens, 1)
+        assert np.abs(out.cpu().numpy() - ref).max() <= OUT_TOL[dt]
+
+
+def test_maximum_context():
+    w = _w("max_ctx", 98, 1, 2, 8, 2, 128, 1 << 18, 4096, "bf16", 0, ctx_list=(1 << 18,), hh_frac=0.01)
+    _chain(w)
+
+
+def test_many_sequences():
+    w = _w("many_seq", 99, 64, 3, 32, 8, 128, 2000, 32, "bf16", 8, ctx_range=(1, 2000), hh_frac=0.01)
+    _chain(w)
