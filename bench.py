@@ -1,0 +1,295 @@
+"""Benchmark of the hybrid-head decode-attention step on one MI355X.
+
+One step = every layer of the workload's decode step (layer 0 all retrieval,
+S chained layer to layer through the C ABI), on seeded synthetic inputs
+resident in HBM, captured once into a HIP graph and replayed.  Reported next
+to the dense all-heads decode step on the same GPU and the CPU oracle.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama3_128k]
+
+Prints one JSON line.  Algorithmic bytes per step (what the method must move;
+workspace traffic excluded):
+    sum_l [ R_l sum_b 2 n_b d s + (Hkv - R_l) sum_b (2 k_eff d s + 4 k_eff)
+            + R_l sum_b 4 k_eff + B Hq d (s + 4) ]
+with R_l retrieval KV heads in layer l, s bytes per cache element, k_eff =
+min(k, n_b) (S_out aliases nothing extra: sparse rows are read once, written
+once by the copy and counted as the 4 k_eff read).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+import synth
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attend_llama3_128k_counters.json")
+ATTEND_SRC = os.path.join(ROOT, "hybrid_head_sparse_amd", "csrc", "attend.hip")
+
+
+def algorithmic_bytes(w: synth.Workload, roles: np.ndarray, lens: np.ndarray):
+    """Per-layer algorithmic bytes of the hybrid step and of the dense step."""
+    s = 2 if w.dtype == "bf16" else 4
+    d = w.head_dim
+    hyb, dense = [], []
+    qo = w.batch * w.n_q_heads * d * (s + 4)
+    for l in range(w.layers):
+        R = int(roles[l].sum())
+        tot = qo
+        for b in range(w.batch):
+            n = int(lens[b])
+            ke = min(w.k, n)
+            tot += R * (2 * n * d * s + 4 * ke)
+            tot += (w.n_kv_heads - R) * (2 * ke * d * s + 4 * ke)
+        hyb.append(tot)
+        dense.append(qo + w.n_kv_heads * sum(2 * int(n) * d * s for n in lens))
+    return hyb, dense
+
+
+def load_inputs(w, roles, lens, keep_host_layers: int, threads: int):
+    """Generate every layer on the host and move it to the GPU; keep host
+    copies of the first `keep_host_layers` layers for the CPU baseline."""
+    import torch
+    dev, host = [], []
+    for l in range(w.layers):
+        x = synth.layer_inputs(w, l, threads=threads)
+        if w.dtype == "bf16":
+            conv = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            conv = lambda a: torch.from_numpy(a).cuda()
+        dev.append({key: conv(x[key]) for key in ("q", "k", "v")})
+        if l < keep_host_layers:
+            host.append(x)
+        print(f"[bench] layer {l} resident", file=sys.stderr, flush=True)
+    return dev, host
+
+
+def cpu_baseline(w, roles, lens, host_layers, budget_s: float, threads: int):
+    """Time the oracle (as it stands) on the first layers of the step, chained
+    through S, until `budget_s` of CPU work or the layers kept run out;
+    extrapolate to the whole step by pooled work units (n per retrieval head,
+    k_eff per sparse head)."""
+    import oracle
+    units = []
+    for l in range(w.layers):
+        R = int(roles[l].sum())
+        units.append(sum(R * int(n) + (w.n_kv_heads - R) * min(w.k, int(n)) for n in lens))
+    S = None
+    t_total, done = 0.0, 0
+    for l, x in enumerate(host_layers):
+        t0 = time.perf_counter()
+        _, S, _ = oracle.layer(x["q"], x["k"], x["v"], roles[l], S, lens, w.k, threads=threads)
+        t_total += time.perf_counter() - t0
+        done = l + 1
+        if t_total >= budget_s:
+            break
+    frac = sum(units[:done]) / sum(units)
+    est_us = t_total / frac * 1e6
+    return {"value": est_us, "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"layers 0..{done - 1} of {w.layers} (chained S), {t_total:.2f} s measured, "
+                      f"scaled by pooled work units ({frac:.4f} of the step); inputs generated outside the timing"}
+
+
+def counters_traffic():
+    """HBM traffic of the attention kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source (else None)."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    with open(COUNTERS_FILE) as f:
+        c = json.load(f)
+    sha = hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()
+    if c.get("attend_source_sha256") != sha:
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_128k", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); the sharding plan is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hybrid_head_sparse_amd as hhs
+
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    roles = synth.roles(w)
+    lens = synth.n_ctx(w)
+    threads = min(16, os.cpu_count() or 1)
+    keep = 0 if args.no_cpu_baseline else min(w.layers, 8)
+    dev, host = load_inputs(w, roles, lens, keep, threads)
+    B, Hq, Hkv, d, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.k
+    n_ctx = torch.from_numpy(lens).cuda()
+    S = [torch.full((B, Hkv, k), -1, dtype=torch.int32, device="cuda") for _ in range(w.layers)]
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device="cuda") for _ in range(w.layers)]
+    dense_outs = [torch.empty((B, Hq, d), dtype=torch.float32, device="cuda") for _ in range(w.layers)]
+    h = hhs.Handle(B, Hq, Hkv, d, w.max_ctx, k, w.dtype)
+
+    def step():
+        for l in range(w.layers):
+            x = dev[l]
+            h.decode_layer(x["q"], x["k"], x["v"], roles[l], S[l - 1] if l else None, S[l], outs[l], n_ctx, k)
+
+    def dense_step():
+        for l in range(w.layers):
+            x = dev[l]
+            h.dense_decode_layer(x["q"], x["k"], x["v"], dense_outs[l], n_ctx)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()                               # warm the kernels on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            h.set_stream(torch.cuda.current_stream())
+            fn()
+        h.set_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return g
+
+    def timed(g, steps, warmup):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        total_ms = t0.elapsed_time(t1)
+        # per-replay distribution in a second pass
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) for a, b in evs)
+        return total_ms / steps, per
+
+    # eager reference run, then the graph; every replay must reproduce it bitwise
+    step()
+    torch.cuda.synchronize()
+    h.check_device_errors()
+    ref_out = [o.clone() for o in outs]
+    ref_S = [s_.clone() for s_ in S]
+    g_step = capture(step)
+    ms_per_step, per = timed(g_step, args.steps, args.warmup)
+    for l in range(w.layers):
+        assert torch.equal(outs[l], ref_out[l]) and torch.equal(S[l], ref_S[l]), f"graph replay differs at layer {l}"
+
+    # attention-kernel launch durations (HIP events on the handle's stream, eager steps)
+    att_ms = [[] for _ in range(w.layers)]
+    ev_pairs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(w.layers)] for _ in range(args.steps)]
+    for rep in ev_pairs:
+        for a, b in rep:
+            a.record()
+            b.record()
+    torch.cuda.synchronize()
+    for rep in ev_pairs:
+        for l in range(w.layers):
+            a, b = rep[l]
+            h.set_profile_events(a, b)
+            x = dev[l]
+            h.decode_layer(x["q"], x["k"], x["v"], roles[l], S[l - 1] if l else None, S[l], outs[l], n_ctx, k)
+    h.set_profile_events(None, None)
+    torch.cuda.synchronize()
+    for rep in ev_pairs:
+        for l in range(w.layers):
+            a, b = rep[l]
+            att_ms[l].append(a.elapsed_time(b))
+
+    hyb_bytes, dense_bytes = algorithmic_bytes(w, roles, lens)
+    step_bytes = sum(hyb_bytes)
+    att_mean = [statistics.mean(v) for v in att_ms]
+    att_all_bytes = sum(hyb_bytes)                    # per step, over all attention launches
+    att_all_ms = sum(att_mean)
+    achieved = att_all_bytes / (att_all_ms * 1e-3) / 1e9
+    l0_ms = att_mean[0]
+    l0_achieved = hyb_bytes[0] / (l0_ms * 1e-3) / 1e9
+
+    dense_res = None
+    if not args.no_dense:
+        dense_step()
+        torch.cuda.synchronize()
+        g_dense = capture(dense_step)
+        dense_ms, dense_per = timed(g_dense, args.steps, args.warmup)
+        dense_res = {"us_per_step": dense_ms * 1e3, "p10_us": dense_per[len(dense_per) // 10] * 1e3,
+                     "p90_us": dense_per[(9 * len(dense_per)) // 10] * 1e3,
+                     "algorithmic_bytes": sum(dense_bytes),
+                     "achieved_GBps": sum(dense_bytes) / (dense_ms * 1e-3) / 1e9}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, roles, lens, host, args.cpu_budget, threads)
+
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    n_retr = int(roles.sum())
+    result = {
+        "metric": "decode-attn us/step + achieved HBM GB/s, Llama3-8B shape, 128K ctx, k=4096",
+        "value": ms_per_step * 1e3,
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "layers": w.layers, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": d, "n_ctx": [int(v) for v in lens] if B > 1 else int(lens[0]), "k": k,
+                   "kv_cache": w.dtype, "retrieval_kv_head_instances": n_retr,
+                   "sparse_kv_head_instances": w.layers * Hkv - n_retr},
+        "achieved_GBps": step_gbps,
+        "frac_of_hbm_peak": step_gbps / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": step_bytes,
+        "p10_us": per[len(per) // 10] * 1e3,
+        "p50_us": per[len(per) // 2] * 1e3,
+        "p90_us": per[(9 * len(per)) // 10] * 1e3,
+        "dense_baseline": dense_res,
+        "speedup_vs_dense": (dense_res["us_per_step"] / (ms_per_step * 1e3)) if dense_res else None,
+        "roofline": {"kernel": "attend_kernel (hybrid, all launches of the step)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": counters_traffic(),
+                     "bytes_per_launch": att_all_bytes / w.layers, "avg_launch_us": att_all_ms / w.layers * 1e3},
+        "roofline_all_retrieval_layer": {"kernel": "attend_kernel (hybrid), layer 0: every KV head retrieval",
+                                         "achieved": l0_achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                         "frac": l0_achieved / HBM_PEAK_GBPS, "bytes_per_launch": hyb_bytes[0],
+                                         "avg_launch_us": l0_ms * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -3,6 +3,7 @@
 //   attention (all heads, pooled)  ->  top-k select (retrieval heads only).
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <cmath>
@@ -182,7 +183,14 @@ lychee_status lychee_create(const lychee_dims* dims, void* workspace, size_t wor
                             dims->k_max);
     h->stream = (hipStream_t)stream;
     h->device = dev;
-    int grid = cus * 2;
+    // persistent attention workgroups: LYCHEE_ATTEND_WG_PER_CU per compute unit
+    // (a tuning knob; default 2, the occupancy of the bf16 d=128 variants)
+    int per_cu = 2;
+    if (const char* env = getenv("LYCHEE_ATTEND_WG_PER_CU")) {
+        const int v = atoi(env);
+        if (v >= 1 && v <= 8) per_cu = v;
+    }
+    int grid = cus * per_cu;
     if (grid > kMaxWG) grid = kMaxWG;
     if (grid < 1) grid = 1;
     h->grid = grid;

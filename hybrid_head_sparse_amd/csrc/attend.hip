@@ -153,47 +153,84 @@ __device__ __forceinline__ float safe_scale(float m, float M) {
     return (m == -INFINITY) ? 0.0f : fast_exp2(m - M);
 }
 
-// Merge `count` records spaced `RS` floats apart into one (m, l, o) per head.
+// Merge `count` records spaced RS floats apart into one (m, l, o) per head.
 // If `out` is non-null the normalised output o / l is written there (query
 // heads contiguous, D floats each); otherwise the merged record goes to `dst`.
+// Every global read is batched (independent loads issued together), so a
+// merge costs one or two memory round trips rather than one per record.
 template <int D, int G>
-__device__ void merge_records(const float* recs, int count, float* dst, float* out) {
+__device__ void merge_records(const float* recs, int count, float* dst, float* out, float* s_ml) {
     constexpr int RS = G * (D + 2);
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    constexpr int NML = 2 * G;
+    constexpr int kBatch = 16;
+    const int tid = threadIdx.x;
+    const int tot = count * NML;
+    for (int base = 0; base < tot; base += kAttendThreads * 4) {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = min(base + tid + kAttendThreads * j, tot - 1);
+            v[j] = coherent_load(&recs[(size_t)(i / NML) * RS + (i % NML)]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = base + tid + kAttendThreads * j;
+            if (i < tot) s_ml[i] = v[j];
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += kAttendThreads) {
         const int h = idx / D, t = idx - h * D;
         float M = -INFINITY;
-        for (int r = 0; r < count; ++r) M = fmaxf(M, recs[(size_t)r * RS + h]);
+        for (int r = 0; r < count; ++r) M = fmaxf(M, s_ml[r * NML + h]);
         float L = 0.0f, O = 0.0f;
-        for (int r = 0; r < count; ++r) {
-            const float* rc = recs + (size_t)r * RS;
-            const float s = safe_scale(rc[h], M);
-            L += rc[G + h] * s;
-            O += rc[2 * G + h * D + t] * s;
+        for (int r0 = 0; r0 < count; r0 += kBatch) {
+            float ov[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int r = min(r0 + j, count - 1);
+                ov[j] = coherent_load(&recs[(size_t)r * RS + 2 * G + h * D + t]);
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int r = r0 + j;
+                if (r < count) {
+                    const float sc = safe_scale(s_ml[r * NML + h], M);
+                    L += s_ml[r * NML + G + h] * sc;
+                    O += ov[j] * sc;
+                }
+            }
         }
         if (out) {
             out[(size_t)h * D + t] = (L > 0.0f) ? O / L : 0.0f;
         } else {
-            dst[2 * G + h * D + t] = O;
+            coherent_store(&dst[2 * G + h * D + t], O);
             if (t == 0) {
-                dst[h] = M;
-                dst[G + h] = L;
+                coherent_store(&dst[h], M);
+                coherent_store(&dst[G + h], L);
             }
         }
     }
+    __syncthreads();
 }
+
+constexpr int kIdxChunk = 2048;   // sparse S positions staged in LDS per pass
 
 template <typename T, int D, int G, bool HYBRID>
 __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendParams p) {
     using Ge = Geo<T, D, G>;
     constexpr int EPL = Ge::EPL, NDW = Ge::NDW, NK = Ge::NK, KPW = Ge::KPW, RS = Ge::RS;
     constexpr int LOG2G = Ge::LOG2G;
+    constexpr uint32_t STRIDE = kWaves * KPW;          // positions per workgroup tile round
 
     __shared__ uint32_t s_pref[kMaxBH + 1];
     __shared__ uint32_t s_hist[HYBRID ? kHistBins : 1];
+    __shared__ int32_t s_idx[HYBRID ? kIdxChunk : 1];
     __shared__ __attribute__((aligned(16))) float s_p[kWaves][4][16];
     __shared__ float s_wo[kWaves][G][D];
     __shared__ float s_wm[kWaves][G];
     __shared__ float s_wl[kWaves][G];
+    __shared__ float s_ml[kLevel2Max * 2 * G];
     __shared__ uint32_t s_part[kAttendThreads / 64];
     __shared__ int s_flag;
 
@@ -205,29 +242,33 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     const int Hq = p.Hkv * G;
 
     // ---- units per (b, g) and their exclusive prefix (every workgroup redoes
-    // this; BH <= 1024 so it is a few hundred cycles) ----
+    // this; BH <= 1024 so it is one batched load and a block scan) ----
     {
         constexpr int PER = kMaxBH / kAttendThreads;   // 4 entries per thread
         uint32_t u[PER];
+        int nv[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int bg = min(tid * PER + i, BH - 1);
+            nv[i] = p.n_ctx[bg / p.Hkv];
+        }
         uint32_t tot = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int bg = tid * PER + i;
             uint32_t units = 0;
             if (bg < BH) {
-                const int b = bg / p.Hkv, g = bg - b * p.Hkv;
-                const int n = p.n_ctx[b];
+                const int g = bg % p.Hkv;
                 const bool retr = !HYBRID || ((p.role_bits >> g) & 1ull);
-                units = retr ? (uint32_t)n : (uint32_t)min(p.k, n);
+                units = retr ? (uint32_t)nv[i] : (uint32_t)min(p.k, nv[i]);
             }
             u[i] = units;
             tot += units;
         }
-        // inclusive wave scan of tot
         uint32_t inc = tot;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            uint32_t y = __shfl_up(inc, off);
+            const uint32_t y = __shfl_up(inc, off);
             if (lane >= off) inc += y;
         }
         if (lane == 63) s_part[wave] = inc;
@@ -238,7 +279,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int bg = tid * PER + i;
-            if (bg <= BH && bg < kMaxBH + 1) s_pref[bg] = run;
+            if (bg <= BH) s_pref[bg] = run;
             run += u[i];
         }
         if (tid == kAttendThreads - 1 && BH == kMaxBH) s_pref[kMaxBH] = run;
@@ -300,9 +341,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
         }
         const size_t kv_row0 = (size_t)bg * (size_t)p.max_ctx;
-        const uint32_t* kbase = reinterpret_cast<const uint32_t*>(p.kc);
-        const uint32_t* vbase = reinterpret_cast<const uint32_t*>(p.vc);
-        const int32_t* Srow = retr ? nullptr : p.S_in + (size_t)bg * p.k;
+        const uint32_t* kbase = reinterpret_cast<const uint32_t*>(p.kc) + (kv_row0 * D + (size_t)x * EPL) * T::kBytes / 4;
+        const uint32_t* vbase = reinterpret_cast<const uint32_t*>(p.vc) + (kv_row0 * D + (size_t)x * EPL) * T::kBytes / 4;
+        constexpr size_t kRowDw = (size_t)D * T::kBytes / 4;   // dwords per cache row
         float* score_row = (HYBRID && retr) ? p.ws.scores + (size_t)bg * p.ws.sstride : nullptr;
 
         float m_run = -INFINITY, l_run = 0.0f;
@@ -313,28 +354,38 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
         bool bad_index = false;
 
-        for (uint32_t tb = seg_lo + (uint32_t)wave * KPW; tb < seg_hi; tb += kWaves * KPW) {
+        // Load the K/V fragments of the tile starting at position tb of [r_lo, r_hi).
+        // Loads are unconditional: positions past r_hi (and invalid S entries)
+        // are clamped to a valid row and masked out of the softmax, so the
+        // compiler can keep the next tile's loads in flight during compute.
+        auto load_tile = [&](uint32_t tb, uint32_t r_lo, uint32_t r_hi, const int32_t* sidx, Frag<NDW>* kf,
+                             Frag<NDW>* vf, int& tok_mine, bool& vmine) {
             const uint32_t rb = tb + (uint32_t)row * NK;
-            Frag<NDW> kf[NK], vf[NK];
-            bool vmine = false;
-            int tok_mine = 0;
 #pragma unroll
             for (int i = 0; i < NK; ++i) {
-                const uint32_t pk = rb + (uint32_t)(i ^ xh);
-                const uint32_t pv = rb + (uint32_t)i;
-                int tk = -1, tv = -1;
-                if (pk < seg_hi) tk = retr ? (int)pk : Srow[pk];
-                if (pv < seg_hi) tv = retr ? (int)pv : Srow[pv];
-                const bool okk = (unsigned)tk < (unsigned)n;
-                const bool okv = (unsigned)tv < (unsigned)n;
-                if (pk < seg_hi && !okk) bad_index = true;
-                if (i == 0) { vmine = okk; tok_mine = tk; }
-                if (okk) load_frag<NDW>(kf[i], kbase + ((kv_row0 + (size_t)tk) * D + (size_t)x * EPL) * T::kBytes / 4);
-                else zero_frag<NDW>(kf[i]);
-                if (okv) load_frag<NDW>(vf[i], vbase + ((kv_row0 + (size_t)tv) * D + (size_t)x * EPL) * T::kBytes / 4);
-                else zero_frag<NDW>(vf[i]);
+                const uint32_t pk = min(rb + (uint32_t)(i ^ xh), r_hi - 1);
+                const uint32_t pv = min(rb + (uint32_t)i, r_hi - 1);
+                int tk, tv;
+                if (sidx) {
+                    tk = sidx[pk - r_lo];
+                    tv = sidx[pv - r_lo];
+                    const bool okk = (unsigned)tk < (unsigned)n;
+                    if (!okk) bad_index = true;
+                    if (i == 0) vmine = okk && (rb + (uint32_t)xh < r_hi);
+                    tk = okk ? tk : 0;
+                    tv = ((unsigned)tv < (unsigned)n) ? tv : 0;
+                } else {
+                    tk = (int)pk;
+                    tv = (int)pv;
+                    if (i == 0) vmine = rb + (uint32_t)xh < r_hi;
+                }
+                if (i == 0) tok_mine = tk;
+                load_frag<NDW>(kf[i], kbase + (size_t)tk * kRowDw);
+                load_frag<NDW>(vf[i], vbase + (size_t)tv * kRowDw);
             }
+        };
 
+        auto compute_tile = [&](const Frag<NDW>* kf, const Frag<NDW>* vf, int tok_mine, bool vmine) {
             // 16 partial dots: slot s = i'*G + h' holds (key i'^xh, head h'^xl)
             float a[16];
 #pragma unroll
@@ -349,11 +400,11 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             for (int s = 0; s < 4; ++s) r4[s] = r8[s] + dpp<kDppRowHalfMirror>(r8[7 - s]);
 #pragma unroll
             for (int s = 0; s < 2; ++s) r2[s] = r4[s] + dpp<kDppQuadXor2>(r4[s ^ 2]);
-            const float dfull = r2[0] + dpp<kDppQuadXor1>(r2[1]);   // key rb + xh, head xl
+            const float dfull = r2[0] + dpp<kDppQuadXor1>(r2[1]);   // key (row base + xh), head xl
 
             if constexpr (HYBRID) {
                 if (retr) {
-                    float pooled = dfull;           // sum over the G heads of key rb + xh
+                    float pooled = dfull;           // sum over the G heads of this key
                     if constexpr (G >= 2) pooled += dpp<kDppQuadXor1>(pooled);
                     if constexpr (G >= 4) pooled += dpp<kDppQuadXor2>(pooled);
                     if constexpr (G >= 8) pooled += dpp<kDppRowHalfMirror>(pooled);
@@ -403,6 +454,61 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     for (int h = 0; h < G; ++h) o[h][e] = __builtin_fmaf(pw[i * G + h], ve, o[h][e]);
                 }
             }
+        };
+
+        // Two-deep software pipeline over the tiles of [r_lo, r_hi): wave w
+        // owns tiles starting at r_lo + w*KPW, stepping by STRIDE.
+        auto stream_range = [&](uint32_t r_lo, uint32_t r_hi, const int32_t* sidx) {
+            uint32_t tb = r_lo + (uint32_t)wave * KPW;
+            if (tb >= r_hi) return;
+            Frag<NDW> kA[NK], vA[NK], kB[NK], vB[NK];
+            int tokA = 0, tokB = 0;
+            bool vmA = false, vmB = false;
+            load_tile(tb, r_lo, r_hi, sidx, kA, vA, tokA, vmA);
+            for (;;) {
+                const uint32_t t1 = tb + STRIDE;
+                load_tile(t1, r_lo, r_hi, sidx, kB, vB, tokB, vmB);
+                compute_tile(kA, vA, tokA, vmA);
+                if (t1 >= r_hi) break;
+                const uint32_t t2 = t1 + STRIDE;
+                load_tile(t2, r_lo, r_hi, sidx, kA, vA, tokA, vmA);
+                compute_tile(kB, vB, tokB, vmB);
+                if (t2 >= r_hi) break;
+                tb = t2;
+            }
+        };
+
+        if (!HYBRID || retr) {
+            stream_range(seg_lo, seg_hi, nullptr);
+        } else {
+            // sparse head: stage the S entries of the range in LDS (one batched
+            // load per chunk), forward them to S_out, then gather-stream
+            const int32_t* Srow = p.S_in + (size_t)bg * p.k;
+            int32_t* Sout = (p.S_out != p.S_in) ? p.S_out + (size_t)bg * p.k : nullptr;
+            constexpr int PER = kIdxChunk / kAttendThreads;
+            for (uint32_t c_lo = seg_lo; c_lo < seg_hi; c_lo += kIdxChunk) {
+                const uint32_t c_hi = min(seg_hi, c_lo + (uint32_t)kIdxChunk);
+                __syncthreads();
+                int32_t v[PER];
+#pragma unroll
+                for (int j = 0; j < PER; ++j) v[j] = Srow[min(c_lo + tid + (uint32_t)(kAttendThreads * j), c_hi - 1)];
+#pragma unroll
+                for (int j = 0; j < PER; ++j) {
+                    const uint32_t pos = c_lo + tid + (uint32_t)(kAttendThreads * j);
+                    if (pos < c_hi) {
+                        s_idx[pos - c_lo] = v[j];
+                        if (Sout) Sout[pos] = v[j];
+                    }
+                }
+                __syncthreads();
+                stream_range(c_lo, c_hi, s_idx);
+            }
+            // entries past min(k, n) (the -1 padding of a short context) belong
+            // to the workgroup that finishes the head
+            if (Sout && h1 <= hi) {
+                const uint32_t ke = h1 - h0;
+                for (uint32_t i = ke + tid; i < (uint32_t)p.k; i += kAttendThreads) Sout[i] = Srow[i];
+            }
         }
         if (bad_index) atomicOr(p.ws.err, 1u);
 
@@ -451,16 +557,15 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 O += s_wo[wv][h][t] * s;
                 L += s_wl[wv][h] * s;
             }
-            rec[2 * G + h * D + t] = O;
+            coherent_store(&rec[2 * G + h * D + t], O);
             if (t == 0) {
-                rec[h] = Mw;
-                rec[G + h] = L;
+                coherent_store(&rec[h], Mw);
+                coherent_store(&rec[G + h], L);
             }
         }
 
         if constexpr (HYBRID) {
             if (retr) {
-                __syncthreads();
                 uint32_t* gh = p.ws.hist + (size_t)bg * kHistBins;
                 for (int i = tid; i < kHistBins; i += kAttendThreads) {
                     const uint32_t c = s_hist[i];
@@ -479,45 +584,36 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         const int c = (w - wf) / kCombineFanIn;
         const int nc = (nw + kCombineFanIn - 1) / kCombineFanIn;
         const int csize = min(kCombineFanIn, nw - c * kCombineFanIn);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        wait_stores_complete();
         __syncthreads();
         if (tid == 0) {
             uint32_t* ctr = p.ws.cnt1 + (size_t)bg * kLevel2Max + c;
-            const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t old = counter_add(ctr, 1u);
             const int last = (int)(old + 1u == (uint32_t)csize);
-            if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (last) counter_reset(ctr);
             s_flag = last;
         }
         __syncthreads();
         if (s_flag) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             const float* grp = p.ws.rec1 + (size_t)(wf + c * kCombineFanIn + bg) * RS;
-            const float* fin = grp;
-            int fin_count = csize;
-            bool write_out = true;
-            if (nc > 1) {
+            float* out_bg = p.out + ((size_t)b * Hq + (size_t)g * G) * D;
+            if (nc == 1) {
+                merge_records<D, G>(grp, csize, nullptr, out_bg, s_ml);
+            } else {
                 float* r2 = p.ws.rec2 + ((size_t)bg * kLevel2Max + c) * RS;
-                merge_records<D, G>(grp, csize, r2, nullptr);
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                merge_records<D, G>(grp, csize, r2, nullptr, s_ml);
+                wait_stores_complete();
                 __syncthreads();
                 if (tid == 0) {
                     uint32_t* ctr = p.ws.cnt2 + bg;
-                    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                    const uint32_t old = counter_add(ctr, 1u);
                     const int last = (int)(old + 1u == (uint32_t)nc);
-                    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (last) counter_reset(ctr);
                     s_flag = last;
                 }
                 __syncthreads();
-                write_out = s_flag != 0;
-                if (write_out) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                fin = p.ws.rec2 + (size_t)bg * kLevel2Max * RS;
-                fin_count = nc;
-            }
-            if (write_out) {
-                merge_records<D, G>(fin, fin_count, nullptr, p.out + ((size_t)b * Hq + (size_t)g * G) * D);
-                if (HYBRID && !retr && p.S_out != p.S_in) {
-                    for (int i = tid; i < p.k; i += kAttendThreads)
-                        p.S_out[(size_t)bg * p.k + i] = p.S_in[(size_t)bg * p.k + i];
+                if (s_flag) {
+                    merge_records<D, G>(p.ws.rec2 + (size_t)bg * kLevel2Max * RS, nc, nullptr, out_bg, s_ml);
                 }
             }
         }

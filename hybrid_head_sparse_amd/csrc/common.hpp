@@ -30,6 +30,31 @@ constexpr int kSelectThreads = 256;
 constexpr int kSelectSeg = 4096;              // scores scanned per select workgroup
 constexpr int kCandLds = 8192;                // candidates resolved in LDS; more go through global passes first
 
+// Cross-workgroup hand-off without cache-wide maintenance.  Data one
+// workgroup leaves for another inside the same launch is written with
+// device-coherent stores (agent-scope relaxed atomic stores: "sc1" stores that
+// reach the device coherence point instead of staying dirty in one XCD's L2)
+// and read back with device-coherent loads.  The producer waits for its stores
+// to complete (vmcnt(0)) before the barrier that precedes its counter atomic,
+// so whoever observes the counter can read the data.  This replaces release /
+// acquire fences, whose buffer_wbl2 / buffer_inv are L2-wide and were measured
+// to dominate the launch when every workgroup executes them.
+template <typename V>
+__device__ __forceinline__ void coherent_store(V* p, V v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ V coherent_load(const V* p) {
+    return __hip_atomic_load(const_cast<V*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t counter_add(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void counter_reset(uint32_t* p) {
+    __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 maps as +0.
 __host__ __device__ inline uint32_t float_key(float f) {
     uint32_t u = __builtin_bit_cast(uint32_t, f);

@@ -35,6 +35,12 @@ constexpr int kWords = kMaxCtx / 32;                   // bitmap words
 constexpr int kWordsPerThread = kWords / kThr;         // 32
 constexpr int kCandPerThread = kCandLds / kThr;        // 32
 
+__device__ __forceinline__ unsigned long long pack_cand(uint32_t key, uint32_t idx) {
+    return ((unsigned long long)idx << 32) | key;
+}
+__device__ __forceinline__ uint2 unpack_cand(unsigned long long v) {
+    return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
     return ((uint64_t)(key & ((1u << kLowBits) - 1u)) << kIdxBits) | (uint64_t)(kIdxMask - idx);
 }
@@ -102,6 +108,7 @@ __global__ void __launch_bounds__(kThr) select_kernel(const SelectParams p) {
     __shared__ uint32_t s_bits[kWords];
     __shared__ uint64_t s_comp[kCandLds];
     __shared__ uint32_t s_h[256];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistBins];
     __shared__ uint32_t s_wave[kThr / 64];
     __shared__ uint32_t s_res[4];
     __shared__ uint32_t s_base[2];
@@ -133,10 +140,20 @@ __global__ void __launch_bounds__(kThr) select_kernel(const SelectParams p) {
     uint32_t* selcnt = p.ws.selcnt + (size_t)bg * 4;
     const float* scores = p.ws.scores + (size_t)bg * p.ws.sstride;
     int32_t* above = p.ws.above + (size_t)bg * p.k_max;
-    uint2* cand = p.ws.cand + (size_t)bg * p.max_ctx;
+    unsigned long long* cand = reinterpret_cast<unsigned long long*>(p.ws.cand) + (size_t)bg * p.max_ctx;
 
-    // ---- 1. threshold digit of the first 12 bits ----
-    find_crossing([&](int i) { return hist[i]; }, kHistBins, ke, s_wave, s_res);
+    // ---- 1. threshold digit of the first 12 bits (histogram staged in LDS
+    // with one batched load) ----
+    {
+        constexpr int V4 = kHistBins / 4 / kThr;   // uint4 per thread
+        uint4 hv[V4];
+#pragma unroll
+        for (int j = 0; j < V4; ++j) hv[j] = reinterpret_cast<const uint4*>(hist)[tid + kThr * j];
+#pragma unroll
+        for (int j = 0; j < V4; ++j) reinterpret_cast<uint4*>(s_hist)[tid + kThr * j] = hv[j];
+        __syncthreads();
+    }
+    find_crossing([&](int i) { return s_hist[i]; }, kHistBins, ke, s_wave, s_res);
     const uint32_t T = s_res[0];
     const uint32_t n_above_digit = s_res[1];
 
@@ -188,10 +205,10 @@ __global__ void __launch_bounds__(kThr) select_kernel(const SelectParams p) {
                 const uint32_t cl = (cls >> (2 * slot)) & 3u;
                 const uint32_t j = (uint32_t)(j0 + 4 * (tid + kThr * c) + e);
                 if (cl == 1u) {
-                    if (pa < (uint32_t)p.k_max) above[pa] = (int32_t)j;
+                    if (pa < (uint32_t)p.k_max) coherent_store(&above[pa], (int32_t)j);
                     ++pa;
                 } else if (cl == 2u) {
-                    if (pc < (uint32_t)p.max_ctx) cand[pc] = make_uint2(keys[slot], j);
+                    if (pc < (uint32_t)p.max_ctx) coherent_store(&cand[pc], pack_cand(keys[slot], j));
                     ++pc;
                 }
             }
@@ -199,36 +216,51 @@ __global__ void __launch_bounds__(kThr) select_kernel(const SelectParams p) {
     }
 
     // ---- arrival ----
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    wait_stores_complete();
     __syncthreads();
     if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&selcnt[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = counter_add(&selcnt[0], 1u);
         const int last = (int)(old + 1u == (uint32_t)nseg);
-        if (last) __hip_atomic_store(&selcnt[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last) counter_reset(&selcnt[0]);
         s_flag = last;
     }
     __syncthreads();
     if (!s_flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     // ---- 3. the last workgroup resolves the head ----
     const int W = (n + 31) >> 5;
     for (int i = tid; i < W; i += kThr) s_bits[i] = 0u;
-    const uint32_t n_above = min(selcnt[1], (uint32_t)p.k_max);
-    uint32_t c_left = min(selcnt[2], (uint32_t)p.max_ctx);
+    const uint32_t n_above = min(coherent_load(&selcnt[1]), (uint32_t)p.k_max);
+    uint32_t c_left = min(coherent_load(&selcnt[2]), (uint32_t)p.max_ctx);
     uint32_t r_left = ke - n_above_digit;
     __syncthreads();
-    for (uint32_t i = tid; i < n_above; i += kThr) {
-        const uint32_t j = (uint32_t)above[i];
-        atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+    for (uint32_t base = 0; base < n_above; base += kThr * kPerThread) {
+        int32_t av[kPerThread];
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) av[e] = coherent_load(&above[min(base + tid + (uint32_t)(kThr * e), n_above - 1)]);
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+            if (base + tid + (uint32_t)(kThr * e) < n_above) {
+                const uint32_t j = (uint32_t)av[e];
+                atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+            }
+        }
     }
 
     int shift = kCompBits;         // bits of the composite not yet resolved: [0, shift)
     bool done = false;
     if (r_left == c_left) {
-        for (uint32_t i = tid; i < c_left; i += kThr) {
-            const uint32_t j = cand[i].y;
-            atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+        for (uint32_t base = 0; base < c_left; base += kThr * kPerThread) {
+            uint2 cv[kPerThread];
+#pragma unroll
+            for (int e = 0; e < kPerThread; ++e) cv[e] = unpack_cand(coherent_load(&cand[min(base + tid + (uint32_t)(kThr * e), c_left - 1)]));
+#pragma unroll
+            for (int e = 0; e < kPerThread; ++e) {
+                if (base + tid + (uint32_t)(kThr * e) < c_left) {
+                    const uint32_t j = cv[e].y;
+                    atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+                }
+            }
         }
         done = true;
     }
@@ -244,9 +276,14 @@ __global__ void __launch_bounds__(kThr) select_kernel(const SelectParams p) {
         shift -= bits;
         for (int i = tid; i < 256; i += kThr) s_h[i] = 0u;
         __syncthreads();
-        for (uint32_t i = tid; i < c_left; i += kThr) {
-            const uint2 cd = cand[i];
-            atomicAdd(&s_h[comp_digit(composite(cd.x, cd.y), shift, bits)], 1u);
+        for (uint32_t base = 0; base < c_left; base += kThr * kPerThread) {
+            uint2 cv[kPerThread];
+#pragma unroll
+            for (int e = 0; e < kPerThread; ++e) cv[e] = unpack_cand(coherent_load(&cand[min(base + tid + (uint32_t)(kThr * e), c_left - 1)]));
+#pragma unroll
+            for (int e = 0; e < kPerThread; ++e)
+                if (base + tid + (uint32_t)(kThr * e) < c_left)
+                    atomicAdd(&s_h[comp_digit(composite(cv[e].x, cv[e].y), shift, bits)], 1u);
         }
         __syncthreads();
         find_crossing([&](int i) { return s_h[i]; }, 1 << bits, r_left, s_wave, s_res);
@@ -260,7 +297,7 @@ __global__ void __launch_bounds__(kThr) select_kernel(const SelectParams p) {
 #pragma unroll
             for (int e = 0; e < kPerThread; ++e) {
                 const uint32_t i = c0 + tid + (uint32_t)(kThr * e);
-                mine[e] = (i < c_left) ? cand[i] : make_uint2(0u, 0u);
+                mine[e] = unpack_cand(coherent_load(&cand[min(i, c_left - 1)]));
                 dg[e] = (i < c_left) ? comp_digit(composite(mine[e].x, mine[e].y), shift, bits) : 0xFFFFFFFFu;
             }
             __syncthreads();
@@ -271,10 +308,10 @@ __global__ void __launch_bounds__(kThr) select_kernel(const SelectParams p) {
                     const uint32_t j = mine[e].y;
                     atomicOr(&s_bits[j >> 5], 1u << (j & 31));
                 } else if (dg[e] == D) {
-                    cand[atomicAdd(&s_ctr, 1u)] = mine[e];
+                    coherent_store(&cand[atomicAdd(&s_ctr, 1u)], pack_cand(mine[e].x, mine[e].y));
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+            wait_stores_complete();
             __syncthreads();
         }
         r_left -= gt;
@@ -282,9 +319,17 @@ __global__ void __launch_bounds__(kThr) select_kernel(const SelectParams p) {
         if (r_left == 0u) {
             done = true;
         } else if (r_left == c_left) {
-            for (uint32_t i = tid; i < c_left; i += kThr) {
-                const uint32_t j = cand[i].y;
-                atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+            for (uint32_t base = 0; base < c_left; base += kThr * kPerThread) {
+                uint2 cv[kPerThread];
+#pragma unroll
+                for (int e = 0; e < kPerThread; ++e) cv[e] = unpack_cand(coherent_load(&cand[min(base + tid + (uint32_t)(kThr * e), c_left - 1)]));
+#pragma unroll
+                for (int e = 0; e < kPerThread; ++e) {
+                    if (base + tid + (uint32_t)(kThr * e) < c_left) {
+                        const uint32_t j = cv[e].y;
+                        atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+                    }
+                }
             }
             done = true;
         }
@@ -293,9 +338,15 @@ __global__ void __launch_bounds__(kThr) select_kernel(const SelectParams p) {
 
     if (!done) {
         // resolve in LDS
-        for (uint32_t i = tid; i < c_left; i += kThr) {
-            const uint2 cd = cand[i];
-            s_comp[i] = composite(cd.x, cd.y);
+        for (uint32_t base = 0; base < c_left; base += kThr * kPerThread) {
+            uint2 cv[kPerThread];
+#pragma unroll
+            for (int e = 0; e < kPerThread; ++e) cv[e] = unpack_cand(coherent_load(&cand[min(base + tid + (uint32_t)(kThr * e), c_left - 1)]));
+#pragma unroll
+            for (int e = 0; e < kPerThread; ++e) {
+                const uint32_t i = base + tid + (uint32_t)(kThr * e);
+                if (i < c_left) s_comp[i] = composite(cv[e].x, cv[e].y);
+            }
         }
         __syncthreads();
         while (!done) {
