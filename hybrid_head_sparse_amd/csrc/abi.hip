@@ -1,6 +1,6 @@
 // C ABI of the hybrid-head decode-attention step: argument validation (pure
-// host code), workspace carve-up, and the per-layer launch sequence
-//   attention (all heads, pooled)  ->  top-k select (retrieval heads only).
+// host code), workspace carve-up, and the per-layer launch (one kernel: pooled
+// attention over all heads with the retrieval heads' top-k fused in).
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -224,13 +224,8 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
                                const int32_t* n_ctx, int32_t k, bool hybrid) {
     const lychee_dims& d = h->dims;
     uint64_t bits = 0;
-    int n_retr = 0;
-    for (int g = 0; g < d.n_kv_heads; ++g) {
-        if (!hybrid || role_mask[g]) {
-            bits |= 1ull << g;
-            ++n_retr;
-        }
-    }
+    for (int g = 0; g < d.n_kv_heads; ++g)
+        if (!hybrid || role_mask[g]) bits |= 1ull << g;
     AttendParams ap{};
     ap.q = q;
     ap.kc = kc;
@@ -253,21 +248,6 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
     if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
     if (h->ev_stop && hipEventRecord(h->ev_stop, h->stream) != hipSuccess)
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
-    if (hybrid && n_retr > 0) {
-        SelectParams sp{};
-        sp.n_ctx = n_ctx;
-        sp.S_out = S_out;
-        sp.ws = h->ws;
-        sp.role_bits = bits;
-        sp.B = d.batch;
-        sp.Hkv = d.n_kv_heads;
-        sp.max_ctx = d.max_ctx;
-        sp.k = k;
-        sp.k_max = d.k_max;
-        sp.n_retrieval = n_retr;
-        e = launch_select(sp, h->stream);
-        if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "select launch failed: %s", hipGetErrorString(e));
-    }
     return ok();
 }
 

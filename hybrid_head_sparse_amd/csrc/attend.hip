@@ -1,32 +1,49 @@
-// Pooled split-K decode attention for retrieval and sparse heads (gfx950).
+// One layer of the hybrid-head decode step in one launch (gfx950).
 //
-// Computes, for every (sequence b, KV head g) of one layer, the single-query
-// attention of its G query heads:
+// For every (sequence b, KV head g) of the layer this kernel computes the
+// single-query attention of the G query heads that share the KV head:
 //   retrieval head: over all n_b cached tokens (Eq. 1 of section 3.4 of the
-//     LycheeDecode long-form digest), plus the GQA-pooled selection score of
-//     every token (the hyper-parameter summary's pooling rule) written for the
-//     top-k pass, and a histogram of its first radix digit;
-//   sparse head: over the min(k, n_b) rows named by S_in (Eq. 3); S is
-//     forwarded unchanged.
-// All (head, unit) work -- a unit is one streamed key row or one gathered S
-// row -- is concatenated into one pool and cut into equal contiguous ranges,
-// one per persistent workgroup, as the digest's workload-pooling description
-// asks (equal-size splits spread homogeneously over thread blocks).  Each
-// range yields one partial (m, l, o) record per head it touches; the records
-// of a head are merged with the log-sum-exp rule by the last workgroup to
-// finish (two-level, so no workgroup ever merges more than 16 records), again
-// as the digest's kernel description has it (partials + LSE combine), but
-// fused into the same launch instead of a separate reduction kernel.
+//     LycheeDecode long-form digest), and S^(l+1) = argsTopK(A, k) (Eq. 2) on
+//     the GQA-pooled logit (the hyper-parameter summary's pooling rule);
+//   sparse head: over the min(k, n_b) rows named by S_in (Eq. 3), forwarding S
+//     unchanged.
 //
-// CDNA4 mapping: a key row (d elements) is spread over 16 lanes (one DPP row)
-// so every lane issues one coalesced 8-32 byte load per row; the G query heads
-// of the group share each loaded row.  Each lane forms 16 partial dot products
-// (NK = 16/G keys x G heads) and a 4-step DPP reduce-scatter leaves lane x of
-// the row with the full dot product of (key x/G, head x%G).  The per-lane key
-// and query-head orders are permuted (key i^(x/G), head h^(x%G)) so that the
-// reduce-scatter needs no per-lane selects.  The online-softmax running max is
-// kept per DPP row and only moved when a tile exceeds it by 2^8 (lazy
-// rescaling), so the common path has no cross-lane max broadcast.
+// Work pooling.  All (head, row) work -- a row is one streamed key of a
+// retrieval head or one gathered S row of a sparse head -- is laid on one cost
+// axis (a gathered row weighs 7/4 of a streamed one) and cut into equal
+// contiguous ranges, one per persistent workgroup, as the digest's kernel
+// description asks (equal-size splits spread over all thread blocks).  Each
+// range yields one partial (m, l, o) record per head it touches; the last
+// workgroup of each group of 32 merges the group's records by the
+// log-sum-exp rule and the last group merger writes the output (partials +
+// LSE combine, fused into the same launch).
+//
+// Selection without a second pass over the scores.  While streaming, every
+// retrieval workgroup keeps the order-preserving 32-bit keys of its pooled
+// logits in LDS and counts their first 12-bit digit.  When its range is done
+// it adds its counts to the head's global histogram, reads the histogram
+// back, and takes the digit T' that holds the k-th largest key among the keys
+// counted so far.  Counts only grow, so T' is a lower bound of the final
+// threshold digit T; the workgroup appends only its keys with digit >= T' to
+// the head's candidate list.  The last workgroup of the head reads the final
+// histogram (T and the count above it), keeps candidates above T, resolves
+// the ones in digit T by radix select on the rest of the key and then the
+// token index (larger key first, lower index first: a strict total order, so
+// the result is exact and unique), marks the winners in an LDS bitmap of the
+// context and writes them in ascending order.
+//
+// CDNA4 mapping of the streaming loop: a key row is spread over 16 lanes (one
+// DPP row), each lane issuing one 8-32 byte load per row; the G query heads of
+// the group share each loaded row.  Each lane forms 16 partial dot products
+// (16/G keys x G heads) and a 4-step DPP reduce-scatter leaves lane x with the
+// full dot product of (key x/G, head x%G); the per-lane key and head orders
+// are permuted (key i^(x/G), head h^(x%G)) so the reduce-scatter needs no
+// selects.  The running max is kept per DPP row and only moved when a tile
+// exceeds it by 2^8 (lazy rescaling).  Loads are unconditional (clamped and
+// masked) so a two-deep software pipeline keeps the next tile in flight.
+//
+// Cross-workgroup hand-off uses device-coherent stores/loads and relaxed
+// counters (see common.hpp): no L2-wide write-back or invalidate.
 #include "common.hpp"
 
 namespace lychee {
@@ -153,60 +170,105 @@ __device__ __forceinline__ float safe_scale(float m, float M) {
     return (m == -INFINITY) ? 0.0f : fast_exp2(m - M);
 }
 
-// Merge `count` records spaced RS floats apart into one (m, l, o) per head.
-// If `out` is non-null the normalised output o / l is written there (query
-// heads contiguous, D floats each); otherwise the merged record goes to `dst`.
-// Every global read is batched (independent loads issued together), so a
-// merge costs one or two memory round trips rather than one per record.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// Records merged by one call: one or two per lane of a wavefront.
+constexpr int kMergeMax = 128;
+static_assert(kLevel2Max <= kMergeMax && kCombineFanIn <= kMergeMax, "merge fan-in exceeds two records per lane");
+
+// LDS floats merge_records needs: per head a scale per record, then M and L.
+template <int G>
+constexpr int merge_lds_floats() { return G * kMergeMax + 2 * G; }
+
+// Merge `count` (<= kMergeMax) records (RS floats apart, written by other
+// workgroups with device-coherent stores) into one (m, l, o) per head.
+// Wavefront w owns heads w, w+4, ..: its lanes load (m, l) of one or two
+// records each, reduce M = max m and L = sum l 2^(m - M) across the wavefront,
+// and leave the per-record scales 2^(m - M) in LDS.  The o loads of the first
+// 32/OPT records are issued before that and land while it runs; the output
+// pass then reads the scales as wavefront-uniform (broadcast) LDS words.  If
+// `out` is non-null the normalised output o / l is written there (query heads
+// contiguous, D floats each); otherwise the merged record goes to `dst` with
+// device-coherent stores.
 template <int D, int G>
 __device__ void merge_records(const float* recs, int count, float* dst, float* out, float* s_ml) {
     constexpr int RS = G * (D + 2);
-    constexpr int NML = 2 * G;
-    constexpr int kBatch = 16;
-    const int tid = threadIdx.x;
-    const int tot = count * NML;
-    for (int base = 0; base < tot; base += kAttendThreads * 4) {
-        float v[4];
+    constexpr int OPT = (G * D + kAttendThreads - 1) / kAttendThreads;   // outputs per thread
+    constexpr int CH = 32 / OPT;                                        // records per load batch
+    constexpr int HPW = (G + kWaves - 1) / kWaves;                      // heads per wavefront
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float* s_sc = s_ml;                     // [G][kMergeMax]
+    float* s_M = s_ml + G * kMergeMax;      // [G]
+    float* s_L = s_M + G;                   // [G]
+    const int r0i = min(lane, count - 1), r1i = min(lane + 64, count - 1);
+    float mv[HPW][2], lv[HPW][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = min(base + tid + kAttendThreads * j, tot - 1);
-            v[j] = coherent_load(&recs[(size_t)(i / NML) * RS + (i % NML)]);
-        }
+    for (int i = 0; i < HPW; ++i) {
+        const int h = min(wave + kWaves * i, G - 1);
+        mv[i][0] = coherent_load(&recs[(size_t)r0i * RS + h]);
+        lv[i][0] = coherent_load(&recs[(size_t)r0i * RS + G + h]);
+        mv[i][1] = coherent_load(&recs[(size_t)r1i * RS + h]);
+        lv[i][1] = coherent_load(&recs[(size_t)r1i * RS + G + h]);
+    }
+    float ov[OPT][CH];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = base + tid + kAttendThreads * j;
-            if (i < tot) s_ml[i] = v[j];
+    for (int q = 0; q < OPT; ++q) {
+        const int idx = min(tid + kAttendThreads * q, G * D - 1);
+        const int h = idx / D, t = idx - h * D;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) ov[q][j] = coherent_load(&recs[(size_t)min(j, count - 1) * RS + 2 * G + h * D + t]);
+    }
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+        const int h = wave + kWaves * i;
+        if (h < G) {
+            const float m0 = lane < count ? mv[i][0] : -INFINITY;
+            const float m1 = lane + 64 < count ? mv[i][1] : -INFINITY;
+            const float M = wave_max(fmaxf(m0, m1));
+            const float c0 = safe_scale(m0, M), c1 = safe_scale(m1, M);
+            const float L = wave_sum((lane < count ? lv[i][0] * c0 : 0.0f) + (lane + 64 < count ? lv[i][1] * c1 : 0.0f));
+            s_sc[h * kMergeMax + lane] = c0;
+            s_sc[h * kMergeMax + 64 + lane] = c1;
+            if (lane == 0) {
+                s_M[h] = M;
+                s_L[h] = L;
+            }
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += kAttendThreads) {
+#pragma unroll
+    for (int q = 0; q < OPT; ++q) {
+        const int idx = tid + kAttendThreads * q;
+        if (idx >= G * D) break;
         const int h = idx / D, t = idx - h * D;
-        float M = -INFINITY;
-        for (int r = 0; r < count; ++r) M = fmaxf(M, s_ml[r * NML + h]);
-        float L = 0.0f, O = 0.0f;
-        for (int r0 = 0; r0 < count; r0 += kBatch) {
-            float ov[kBatch];
+        const float* sc = s_sc + h * kMergeMax;
+        float O = 0.0f;
+        for (int r0 = 0; r0 < count; r0 += CH) {
+            if (r0 > 0) {   // more records than one batch: load the next batch
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int r = min(r0 + j, count - 1);
-                ov[j] = coherent_load(&recs[(size_t)r * RS + 2 * G + h * D + t]);
+                for (int j = 0; j < CH; ++j)
+                    ov[q][j] = coherent_load(&recs[(size_t)min(r0 + j, count - 1) * RS + 2 * G + h * D + t]);
             }
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const int r = r0 + j;
-                if (r < count) {
-                    const float sc = safe_scale(s_ml[r * NML + h], M);
-                    L += s_ml[r * NML + G + h] * sc;
-                    O += ov[j] * sc;
-                }
-            }
+            for (int j = 0; j < CH; ++j)     // scales of records past count are zero
+                O += ov[q][j] * sc[r0 + j];
         }
+        const float L = s_L[h];
         if (out) {
             out[(size_t)h * D + t] = (L > 0.0f) ? O / L : 0.0f;
         } else {
             coherent_store(&dst[2 * G + h * D + t], O);
             if (t == 0) {
-                coherent_store(&dst[h], M);
+                coherent_store(&dst[h], s_M[h]);
                 coherent_store(&dst[G + h], L);
             }
         }
@@ -214,7 +276,90 @@ __device__ void merge_records(const float* recs, int count, float* dst, float* o
     __syncthreads();
 }
 
-constexpr int kIdxChunk = 2048;   // sparse S positions staged in LDS per pass
+// ---------------------------------------------------------------- selection helpers
+
+constexpr int kLowBits = 32 - kHistBits;                 // key bits below the first digit
+constexpr uint32_t kIdxMask = (1u << kIdxBits) - 1u;
+constexpr int kCompBits = kLowBits + kIdxBits;           // composite: low key bits, then inverted index
+constexpr int kWords = kMaxCtx / 32;                     // context bitmap words
+constexpr int kBitsLds = kWords + kWords / 32;           // one pad word per 32: thread-contiguous
+                                                         // words fall in distinct LDS banks
+__device__ __forceinline__ int bit_slot(int word) { return word + (word >> 5); }
+constexpr int kHistPerThread = kHistBins / kAttendThreads;
+constexpr int kCandPerThread = kCandLds / kAttendThreads;
+
+__device__ __forceinline__ unsigned long long pack_cand(uint32_t key, uint32_t idx) {
+    return ((unsigned long long)idx << 32) | key;
+}
+__device__ __forceinline__ unsigned long long composite(uint32_t key, uint32_t idx) {
+    return ((unsigned long long)(key & ((1u << kLowBits) - 1u)) << kIdxBits) | (unsigned long long)(kIdxMask - idx);
+}
+__device__ __forceinline__ uint32_t comp_index(unsigned long long c) { return kIdxMask - (uint32_t)(c & kIdxMask); }
+__device__ __forceinline__ uint32_t comp_digit(unsigned long long c, int shift, int bits) {
+    return (uint32_t)(c >> shift) & ((1u << bits) - 1u);
+}
+
+// Block-wide exclusive prefix sum of one value per thread.
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+    }
+    __syncthreads();
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    uint32_t base = 0, tot = 0;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) {
+        if (wv < wave) base += s_wave[wv];
+        tot += s_wave[wv];
+    }
+    *total = tot;
+    return base + inc - v;
+}
+
+// Crossing of a histogram spread over the block, PER bins per thread held in
+// `cnt` (thread t holds the bins of descending rank t*PER .. t*PER+PER-1, i.e.
+// bin nbins-1-rank): finds D with (count above D) < need <= (count >= D).
+// Result in s_res[0] (digit), s_res[1] (count above D); if the whole
+// histogram holds fewer than `need`, D = 0 and the count above it is returned.
+template <int PER>
+__device__ void block_crossing(const uint32_t (&cnt)[PER], int nbins, uint32_t need, uint32_t* s_wave,
+                               uint32_t* s_res) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) sum += cnt[i];
+    uint32_t tot;
+    const uint32_t before = block_exclusive_scan(sum, s_wave, &tot);
+    const int r0 = (int)threadIdx.x * PER;
+    if (tot < need) {
+        // fewer than `need` counted: every digit qualifies (D = 0); the owner of
+        // bin 0 (descending rank nbins-1) reports the count above it
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (r0 + i == nbins - 1) {
+                s_res[0] = 0u;
+                s_res[1] = tot - cnt[i];
+            }
+        }
+    } else if (before < need && need <= before + sum) {
+        uint32_t acc = before;
+        bool found = false;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (!found && acc + cnt[i] >= need) {
+                s_res[0] = (uint32_t)(nbins - 1 - (r0 + i));
+                s_res[1] = acc;
+                found = true;
+            }
+            acc += cnt[i];
+        }
+    }
+    __syncthreads();
+}
 
 template <typename T, int D, int G, bool HYBRID>
 __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendParams p) {
@@ -223,16 +368,37 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     constexpr int LOG2G = Ge::LOG2G;
     constexpr uint32_t STRIDE = kWaves * KPW;          // positions per workgroup tile round
 
+    struct StreamLds {
+        uint32_t hist[HYBRID ? kHistBins : 1];
+        uint32_t gbuf[HYBRID ? kHistBins : 1];      // the head's global histogram as read back
+        uint32_t keys[HYBRID ? kKeyCap : 1];
+        int32_t idx[HYBRID ? kIdxChunk : 1];
+        float pw[kWaves][4][16];
+        float wo[kWaves][G][D];
+        float wm[kWaves][G];
+        float wl[kWaves][G];
+        float ml[merge_lds_floats<G>()];
+    };
+    struct SelectLds {
+        uint32_t bits[HYBRID ? kBitsLds : 1];
+        union {
+            unsigned long long comp[HYBRID ? kCandLds : 1];   // threshold-digit candidates
+            uint32_t h12[HYBRID ? kHistBins : 1];              // the head's final first-digit histogram
+        };
+        uint32_t h[256];
+    };
+    union Lds {
+        StreamLds st;
+        SelectLds se;
+    };
+    __shared__ __attribute__((aligned(16))) Lds u;
     __shared__ uint32_t s_pref[kMaxBH + 1];
-    __shared__ uint32_t s_hist[HYBRID ? kHistBins : 1];
-    __shared__ int32_t s_idx[HYBRID ? kIdxChunk : 1];
-    __shared__ __attribute__((aligned(16))) float s_p[kWaves][4][16];
-    __shared__ float s_wo[kWaves][G][D];
-    __shared__ float s_wm[kWaves][G];
-    __shared__ float s_wl[kWaves][G];
-    __shared__ float s_ml[kLevel2Max * 2 * G];
-    __shared__ uint32_t s_part[kAttendThreads / 64];
-    __shared__ int s_flag;
+    __shared__ uint32_t s_bound[kMaxWG + 1];   // cost position where each workgroup's range starts
+    __shared__ int32_t s_nctx[kMaxBH];
+    __shared__ uint32_t s_wave[kWaves];
+    __shared__ uint32_t s_res[4];
+    __shared__ uint32_t s_ctr;
+    __shared__ int s_flag[2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -241,94 +407,362 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     const int BH = p.B * p.Hkv;
     const int Hq = p.Hkv * G;
 
-    // ---- units per (b, g) and their exclusive prefix (every workgroup redoes
-    // this; BH <= 1024 so it is one batched load and a block scan) ----
+    // ---- prologue: contexts, pool cost per (b, g) and its exclusive prefix ----
     {
         constexpr int PER = kMaxBH / kAttendThreads;   // 4 entries per thread
-        uint32_t u[PER];
-        int nv[PER];
+        int nb[PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int bg = min(tid * PER + i, BH - 1);
-            nv[i] = p.n_ctx[bg / p.Hkv];
-        }
+        for (int i = 0; i < PER; ++i) nb[i] = p.n_ctx[min(tid * PER + i, p.B - 1)];
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (tid * PER + i < p.B) s_nctx[tid * PER + i] = nb[i];
+        __syncthreads();
+        uint32_t u_[PER];
         uint32_t tot = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int bg = tid * PER + i;
-            uint32_t units = 0;
+            uint32_t cost = 0;
             if (bg < BH) {
-                const int g = bg % p.Hkv;
+                const int b = bg / p.Hkv, g = bg - b * p.Hkv;
+                const int n = s_nctx[b];
                 const bool retr = !HYBRID || ((p.role_bits >> g) & 1ull);
-                units = retr ? (uint32_t)nv[i] : (uint32_t)min(p.k, nv[i]);
+                cost = retr ? kCostRetrieval * (uint32_t)n : kCostSparse * (uint32_t)min(p.k, n);
             }
-            u[i] = units;
-            tot += units;
+            u_[i] = cost;
+            tot += cost;
         }
-        uint32_t inc = tot;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(inc, off);
-            if (lane >= off) inc += y;
-        }
-        if (lane == 63) s_part[wave] = inc;
-        __syncthreads();
-        uint32_t base = 0;
-        for (int wv = 0; wv < wave; ++wv) base += s_part[wv];
-        uint32_t run = base + inc - tot;
+        uint32_t total;
+        uint32_t run = block_exclusive_scan(tot, s_wave, &total);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int bg = tid * PER + i;
             if (bg <= BH) s_pref[bg] = run;
-            run += u[i];
+            run += u_[i];
         }
         if (tid == kAttendThreads - 1 && BH == kMaxBH) s_pref[kMaxBH] = run;
-        if (HYBRID) {
-            for (int i = tid; i < kHistBins; i += kAttendThreads) s_hist[i] = 0u;
-        }
         __syncthreads();
     }
 
     const uint32_t U = s_pref[BH];
     int P = (int)gridDim.x;
     {
-        const uint32_t pmax = (U + kMinUnitsPerWG - 1) / kMinUnitsPerWG;
+        const uint32_t pmax = U / kMinCostPerWG;
         if ((uint32_t)P > pmax) P = (int)(pmax < 1 ? 1 : pmax);
     }
     const int w = blockIdx.x;
     if (w >= P) return;
-    auto range_lo = [&](int ww) -> uint32_t {
-        if (ww >= P) return U;
-        return (uint32_t)(((uint64_t)ww * U / (uint64_t)P) & ~(uint64_t)(kUnitAlign - 1));
-    };
-    auto wg_of = [&](uint32_t unit) -> int {
-        int ww = (int)(((uint64_t)unit * (uint64_t)P) / (uint64_t)U);
-        if (ww >= P) ww = P - 1;
-        while (ww > 0 && range_lo(ww) > unit) --ww;
-        while (ww + 1 < P && range_lo(ww + 1) <= unit) ++ww;
-        return ww;
-    };
-    const uint32_t lo = range_lo(w), hi = range_lo(w + 1);
 
-    // first (b, g) whose unit range contains lo
-    int bg = 0;
-    {
-        int a = 0, z = BH - 1;
+    auto is_retr = [&](int hb) -> bool { return !HYBRID || ((p.role_bits >> (hb % p.Hkv)) & 1ull); };
+    auto cost_of = [&](int hb) -> uint32_t { return is_retr(hb) ? kCostRetrieval : kCostSparse; };
+    auto head_of = [&](uint32_t c) -> int {     // last (b, g) whose cost range starts at or before c
+        int cnt = 0;                              // (wave-parallel: the starts are increasing)
+        for (int base = 0; base < BH; base += 64) {
+            const int i = base + lane;
+            cnt += __popcll(__ballot(i < BH && s_pref[i] <= c));
+        }
+        return cnt - 1;
+    };
+    // Workgroup boundaries: the equal split of the cost axis, moved up to the
+    // next row boundary of the head it falls in (so every range holds whole
+    // rows).  Every workgroup tabulates all P+1 of them once, in parallel.
+    for (int ww = tid; ww <= P; ww += kAttendThreads) {
+        uint32_t bnd;
+        if (ww == 0) {
+            bnd = 0u;
+        } else if (ww >= P) {
+            bnd = U;
+        } else {
+            const uint32_t raw = (uint32_t)((uint64_t)ww * U / (uint64_t)P);
+            int a = 0, z = BH - 1;                 // head holding raw (serial search per thread)
+            while (a < z) {
+                const int mid = (a + z + 1) >> 1;
+                if (s_pref[mid] <= raw) a = mid; else z = mid - 1;
+            }
+            const uint32_t h0 = s_pref[a], h1 = s_pref[a + 1], c = cost_of(a);
+            bnd = min(h0 + c * ((raw - h0 + c - 1) / c), h1);
+        }
+        s_bound[ww] = bnd;
+    }
+    __syncthreads();
+    auto wg_of = [&](uint32_t cpos) -> int {    // workgroup whose range holds cost position cpos
+        int a = 0, z = P - 1;
         while (a < z) {
             const int mid = (a + z + 1) >> 1;
-            if (s_pref[mid] <= lo) a = mid; else z = mid - 1;
+            if (s_bound[mid] <= cpos) a = mid; else z = mid - 1;
         }
-        bg = a;
-    }
+        return a;
+    };
+    const uint32_t lo = s_bound[w], hi = s_bound[w + 1];
 
-    for (; bg < BH && s_pref[bg] < hi; ++bg) {
+    // Classify the NB candidates this thread holds (slot e is candidate
+    // base + tid + 256 e of C): first digit above T_ -> bitmap; equal -> the
+    // composite is appended to u.se.comp after the c_eq already there (one
+    // block scan orders the appends; no per-candidate LDS atomics).
+    auto classify_batch = [&](auto& vals, uint32_t base, uint32_t C, uint32_t T_, uint32_t& c_eq) {
+        constexpr int NB = (int)(sizeof(vals) / sizeof(vals[0]));
+        static_assert(NB <= 64, "mask holds 64 slots");
+        unsigned long long eqm = 0;
+#pragma unroll
+        for (int e = 0; e < NB; ++e) {
+            const bool valid = base + tid + (uint32_t)(kAttendThreads * e) < C;
+            const uint32_t key = (uint32_t)vals[e], j = (uint32_t)(vals[e] >> 32);
+            const uint32_t dg = key >> kLowBits;
+            if (valid && dg > T_) atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31));
+            if (valid && dg == T_) eqm |= 1ull << e;
+        }
+        uint32_t tot;
+        uint32_t pos = c_eq + block_exclusive_scan((uint32_t)__popcll(eqm), s_wave, &tot);
+#pragma unroll
+        for (int e = 0; e < NB; ++e) {
+            if ((eqm >> e) & 1ull) {
+                if (pos < (uint32_t)kCandLds) u.se.comp[pos] = composite((uint32_t)vals[e], (uint32_t)(vals[e] >> 32));
+                ++pos;
+            }
+        }
+        c_eq += tot;
+    };
+
+    // Exact top-k of one retrieval head: the final first-digit histogram gives
+    // the threshold digit T and the count above it; every key with digit >= T
+    // is in the candidate list.  Writes S_out's row and restores the head's
+    // zeroed histogram and candidate count.
+    auto resolve_topk = [&](int hb, int n, uint32_t ke) {
+        int32_t* srow = p.S_out + (size_t)hb * p.k;
+        uint32_t* gh = p.ws.hist + (size_t)hb * kHistBins;
+        const unsigned long long* cand = p.ws.cand + (size_t)hb * p.max_ctx;
+        const int W = (n + 31) >> 5;
+        __syncthreads();
+        if (ke == (uint32_t)n) {
+            for (int i = tid; i < p.k; i += kAttendThreads) srow[i] = (i < n) ? i : -1;
+        } else {
+            constexpr int RC = 64;     // candidates loaded per thread with the count (16384 per head)
+            constexpr int kB = 16;     // batch of later candidates
+            const uint32_t C = max(1u, min(coherent_load(&p.ws.candcnt[hb]), (uint32_t)p.max_ctx));
+            unsigned long long cv[RC];
+#pragma unroll
+            for (int e = 0; e < RC; ++e)     // issued with the count, filtered by it afterwards
+                cv[e] = coherent_load(&cand[min(tid + (uint32_t)(kAttendThreads * e), (uint32_t)p.max_ctx - 1u)]);
+            {
+                uint32_t gv[kHistPerThread];
+#pragma unroll
+                for (int j = 0; j < kHistPerThread; ++j) gv[j] = coherent_load(&gh[tid + kAttendThreads * j]);
+#pragma unroll
+                for (int j = 0; j < kHistPerThread; ++j) u.se.h12[tid + kAttendThreads * j] = gv[j];
+            }
+            for (int i = tid; i <= bit_slot(W - 1); i += kAttendThreads) u.se.bits[i] = 0u;
+            __syncthreads();
+            uint32_t hc[kHistPerThread];
+            {
+                // thread t takes descending ranks 16t.. = bins 4095-16t down to 4080-16t
+                const uint4* hv = reinterpret_cast<const uint4*>(u.se.h12 + kHistBins - kHistPerThread * (tid + 1));
+#pragma unroll
+                for (int c = 0; c < kHistPerThread / 4; ++c) {
+                    const uint4 v4 = hv[c];
+                    hc[kHistPerThread - 1 - 4 * c] = v4.x;
+                    hc[kHistPerThread - 2 - 4 * c] = v4.y;
+                    hc[kHistPerThread - 3 - 4 * c] = v4.z;
+                    hc[kHistPerThread - 4 - 4 * c] = v4.w;
+                }
+            }
+            block_crossing<kHistPerThread>(hc, kHistBins, ke, s_wave, s_res);
+            const uint32_t T_ = s_res[0];
+            const uint32_t c_above = s_res[1];
+            uint32_t c_eq = 0;
+            classify_batch(cv, 0u, C, T_, c_eq);
+            for (uint32_t base = kAttendThreads * RC; base < C; base += kAttendThreads * kB) {
+                unsigned long long bv[kB];
+#pragma unroll
+                for (int e = 0; e < kB; ++e) bv[e] = coherent_load(&cand[min(base + tid + (uint32_t)(kAttendThreads * e), C - 1)]);
+                classify_batch(bv, base, C, T_, c_eq);
+            }
+            __syncthreads();
+            uint32_t c_left = c_eq;
+            uint32_t r_left = ke - c_above;
+            int shift = kCompBits;
+            bool done = (r_left == 0u);
+            if (!done && c_left > (uint32_t)kCandLds) {
+                // Too many ties with the threshold digit for LDS: narrow by passes
+                // over the candidate list, each fixing the next 8 bits (prefix) of
+                // the composite of the k-th element.
+                unsigned long long prefix = 0;
+                while (!done && c_left > (uint32_t)kCandLds && shift > 0) {
+                    const int bits = shift >= 8 ? 8 : shift;
+                    const int nshift = shift - bits;
+                    for (int i = tid; i < 256; i += kAttendThreads) u.se.h[i] = 0u;
+                    __syncthreads();
+                    for (uint32_t base = 0; base < C; base += kAttendThreads * kB) {
+                        unsigned long long bv[kB];
+#pragma unroll
+                        for (int e = 0; e < kB; ++e) bv[e] = coherent_load(&cand[min(base + tid + (uint32_t)(kAttendThreads * e), C - 1)]);
+#pragma unroll
+                        for (int e = 0; e < kB; ++e) {
+                            if (base + tid + (uint32_t)(kAttendThreads * e) >= C) continue;
+                            const uint32_t key = (uint32_t)bv[e], j = (uint32_t)(bv[e] >> 32);
+                            if ((key >> kLowBits) != T_) continue;
+                            const unsigned long long cp = composite(key, j);
+                            if (shift < kCompBits && (cp >> shift) != prefix) continue;
+                            atomicAdd(&u.se.h[comp_digit(cp, nshift, bits)], 1u);
+                        }
+                    }
+                    __syncthreads();
+                    uint32_t hb1[1] = {tid < (1 << bits) ? u.se.h[(1 << bits) - 1 - tid] : 0u};
+                    block_crossing<1>(hb1, 1 << bits, r_left, s_wave, s_res);
+                    const uint32_t Dg = min(s_res[0], (1u << bits) - 1u), gt = s_res[1];
+                    const uint32_t keep = u.se.h[Dg];
+                    for (uint32_t base = 0; base < C; base += kAttendThreads * kB) {
+                        unsigned long long bv[kB];
+#pragma unroll
+                        for (int e = 0; e < kB; ++e) bv[e] = coherent_load(&cand[min(base + tid + (uint32_t)(kAttendThreads * e), C - 1)]);
+#pragma unroll
+                        for (int e = 0; e < kB; ++e) {
+                            if (base + tid + (uint32_t)(kAttendThreads * e) >= C) continue;
+                            const uint32_t key = (uint32_t)bv[e], j = (uint32_t)(bv[e] >> 32);
+                            if ((key >> kLowBits) != T_) continue;
+                            const unsigned long long cp = composite(key, j);
+                            if (shift < kCompBits && (cp >> shift) != prefix) continue;
+                            const uint32_t dg = comp_digit(cp, nshift, bits);
+                            if (dg > Dg || (r_left - gt == keep && dg == Dg))
+                                atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31));
+                        }
+                    }
+                    __syncthreads();
+                    r_left -= gt;
+                    c_left = keep;
+                    prefix = (prefix << bits) | Dg;
+                    shift = nshift;
+                    if (r_left == 0u || r_left == c_left) done = true;
+                }
+                if (!done) {
+                    // the k-th element's prefix group now fits in LDS: gather it
+                    uint32_t c_pre = 0;
+                    for (uint32_t base = 0; base < C; base += kAttendThreads * kB) {
+                        unsigned long long bv[kB];
+                        unsigned long long cpv[kB];
+#pragma unroll
+                        for (int e = 0; e < kB; ++e) bv[e] = coherent_load(&cand[min(base + tid + (uint32_t)(kAttendThreads * e), C - 1)]);
+                        unsigned long long m = 0;
+#pragma unroll
+                        for (int e = 0; e < kB; ++e) {
+                            const uint32_t key = (uint32_t)bv[e], j = (uint32_t)(bv[e] >> 32);
+                            cpv[e] = composite(key, j);
+                            if (base + tid + (uint32_t)(kAttendThreads * e) < C && (key >> kLowBits) == T_ &&
+                                (cpv[e] >> shift) == prefix)
+                                m |= 1ull << e;
+                        }
+                        uint32_t tot;
+                        uint32_t pos = c_pre + block_exclusive_scan((uint32_t)__popcll(m), s_wave, &tot);
+#pragma unroll
+                        for (int e = 0; e < kB; ++e) {
+                            if ((m >> e) & 1ull) {
+                                if (pos < (uint32_t)kCandLds) u.se.comp[pos] = cpv[e];
+                                ++pos;
+                            }
+                        }
+                        c_pre += tot;
+                    }
+                    __syncthreads();
+                    c_left = min(c_pre, (uint32_t)kCandLds);
+                }
+            }
+            if (!done && r_left == c_left) {   // the whole threshold group is selected
+                for (uint32_t i = tid; i < c_left; i += kAttendThreads) {
+                    const uint32_t j = comp_index(u.se.comp[i]);
+                    atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31));
+                }
+                done = true;
+            }
+            // radix select in LDS over the remaining composite bits
+            while (!done) {
+                if (shift == 0) {             // unreachable: composites are distinct
+                    if (tid == 0) atomicOr(p.ws.err, 2u);
+                    break;
+                }
+                const int bits = shift >= 8 ? 8 : shift;
+                shift -= bits;
+                for (int i = tid; i < 256; i += kAttendThreads) u.se.h[i] = 0u;
+                __syncthreads();
+                unsigned long long mine[kCandPerThread];
+                uint32_t dg[kCandPerThread];
+#pragma unroll
+                for (int e = 0; e < kCandPerThread; ++e) {
+                    const uint32_t i = tid + (uint32_t)(kAttendThreads * e);
+                    mine[e] = (i < c_left) ? u.se.comp[i] : 0ull;
+                    dg[e] = (i < c_left) ? comp_digit(mine[e], shift, bits) : 0xFFFFFFFFu;
+                    if (i < c_left) atomicAdd(&u.se.h[dg[e]], 1u);
+                }
+                __syncthreads();
+                uint32_t hb1[1] = {tid < (1 << bits) ? u.se.h[(1 << bits) - 1 - tid] : 0u};
+                block_crossing<1>(hb1, 1 << bits, r_left, s_wave, s_res);
+                const uint32_t Dg = min(s_res[0], (1u << bits) - 1u), gt = s_res[1];
+                const uint32_t keep = u.se.h[Dg];
+                uint32_t m = 0;
+#pragma unroll
+                for (int e = 0; e < kCandPerThread; ++e) {
+                    if (dg[e] != 0xFFFFFFFFu && dg[e] > Dg) {
+                        const uint32_t j = comp_index(mine[e]);
+                        atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31));
+                    }
+                    if (dg[e] == Dg) m |= 1u << e;
+                }
+                uint32_t tot;
+                uint32_t pos = block_exclusive_scan((uint32_t)__popc(m), s_wave, &tot);
+#pragma unroll
+                for (int e = 0; e < kCandPerThread; ++e)
+                    if ((m >> e) & 1u) u.se.comp[pos++] = mine[e];
+                __syncthreads();
+                r_left -= gt;
+                c_left = keep;
+                if (r_left == 0u) {
+                    done = true;
+                } else if (r_left == c_left) {
+                    for (uint32_t i = tid; i < c_left; i += kAttendThreads) {
+                        const uint32_t j = comp_index(u.se.comp[i]);
+                        atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31));
+                    }
+                    done = true;
+                }
+                __syncthreads();
+            }
+            __syncthreads();
+            // Emit the bitmap in ascending order: every thread owns WPT
+            // consecutive words (padded slots: no bank conflicts), one block
+            // scan of the per-thread counts gives each its first position.
+            const int WPT = (W + kAttendThreads - 1) / kAttendThreads;
+            const int w0 = tid * WPT;
+            const int w1 = min(W, w0 + WPT);
+            uint32_t cnt = 0;
+            for (int i = w0; i < w1; ++i) cnt += __popc(u.se.bits[bit_slot(i)]);
+            uint32_t total;
+            uint32_t pos = block_exclusive_scan(cnt, s_wave, &total);
+            for (int i = w0; i < w1; ++i) {
+                uint32_t bw = u.se.bits[bit_slot(i)];
+                while (bw) {
+                    const int bit = __ffs(bw) - 1;
+                    bw &= bw - 1u;
+                    if (pos < ke) srow[pos] = i * 32 + bit;
+                    ++pos;
+                }
+            }
+            for (int i = (int)ke + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
+            if (tid == 0 && total != ke) atomicOr(p.ws.err, 2u);
+        }
+        // restore the zero invariant of the head's histogram and candidate count
+        for (int i = tid; i < kHistBins; i += kAttendThreads) gh[i] = 0u;
+        if (tid == 0) counter_reset(&p.ws.candcnt[hb]);
+        __syncthreads();
+    };
+
+    for (int bg = head_of(lo); bg < BH && s_pref[bg] < hi; ++bg) {
         const uint32_t h0 = s_pref[bg], h1 = s_pref[bg + 1];
         if (h1 <= lo || h1 == h0) continue;
-        const uint32_t seg_lo = max(lo, h0) - h0;
-        const uint32_t seg_hi = min(hi, h1) - h0;
         const int b = bg / p.Hkv, g = bg - b * p.Hkv;
-        const bool retr = !HYBRID || ((p.role_bits >> g) & 1ull);
-        const int n = p.n_ctx[b];
+        const bool retr = is_retr(bg);
+        const uint32_t cw = retr ? kCostRetrieval : kCostSparse;
+        const uint32_t seg_lo = (max(lo, h0) - h0) / cw;     // first row (position) of this head
+        const uint32_t seg_hi = (min(hi, h1) - h0) / cw;
+        const int n = s_nctx[b];
+        const uint32_t ke = (uint32_t)min(p.k, n);
 
         // query slices: register h' holds query head g*G + (h' ^ xl), elements x*EPL..
         Frag<NDW> qf[G];
@@ -344,7 +778,6 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         const uint32_t* kbase = reinterpret_cast<const uint32_t*>(p.kc) + (kv_row0 * D + (size_t)x * EPL) * T::kBytes / 4;
         const uint32_t* vbase = reinterpret_cast<const uint32_t*>(p.vc) + (kv_row0 * D + (size_t)x * EPL) * T::kBytes / 4;
         constexpr size_t kRowDw = (size_t)D * T::kBytes / 4;   // dwords per cache row
-        float* score_row = (HYBRID && retr) ? p.ws.scores + (size_t)bg * p.ws.sstride : nullptr;
 
         float m_run = -INFINITY, l_run = 0.0f;
         float o[G][EPL];
@@ -353,11 +786,12 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #pragma unroll
             for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
         bool bad_index = false;
+        uint32_t key_base = 0;         // position of u.st.keys[0] (retrieval selection keys)
 
-        // Load the K/V fragments of the tile starting at position tb of [r_lo, r_hi).
-        // Loads are unconditional: positions past r_hi (and invalid S entries)
-        // are clamped to a valid row and masked out of the softmax, so the
-        // compiler can keep the next tile's loads in flight during compute.
+        // Load the K/V fragments of the tile starting at position tb of
+        // [r_lo, r_hi).  Loads are unconditional: positions past r_hi (and
+        // invalid S entries) are clamped to a valid row and masked out of the
+        // softmax, so the next tile's loads stay in flight during compute.
         auto load_tile = [&](uint32_t tb, uint32_t r_lo, uint32_t r_hi, const int32_t* sidx, Frag<NDW>* kf,
                              Frag<NDW>* vf, int& tok_mine, bool& vmine) {
             const uint32_t rb = tb + (uint32_t)row * NK;
@@ -409,8 +843,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     if constexpr (G >= 4) pooled += dpp<kDppQuadXor2>(pooled);
                     if constexpr (G >= 8) pooled += dpp<kDppRowHalfMirror>(pooled);
                     if (xl == 0 && vmine) {
-                        score_row[tok_mine] = pooled;
-                        atomicAdd(&s_hist[float_key(pooled) >> (32 - kHistBits)], 1u);
+                        const uint32_t key = float_key(pooled);
+                        u.st.keys[(uint32_t)tok_mine - key_base] = key;
+                        atomicAdd(&u.st.hist[key >> kLowBits], 1u);
                     }
                 }
             }
@@ -433,11 +868,11 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             l_run += pr;
 
             // broadcast the row's 16 weights to every lane of the row
-            s_p[wave][row][x] = pr;
+            u.st.pw[wave][row][x] = pr;
             compiler_fence();
             float pw[16];
             {
-                const float4* src = reinterpret_cast<const float4*>(&s_p[wave][row][0]);
+                const float4* src = reinterpret_cast<const float4*>(&u.st.pw[wave][row][0]);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const float4 v4 = src[c];
@@ -478,8 +913,74 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
         };
 
-        if (!HYBRID || retr) {
+        if (!HYBRID) {
             stream_range(seg_lo, seg_hi, nullptr);
+        } else if (retr) {
+            uint32_t* gh = p.ws.hist + (size_t)bg * kHistBins;
+            unsigned long long* cand = p.ws.cand + (size_t)bg * p.max_ctx;
+            for (int i = tid; i < kHistBins; i += kAttendThreads) u.st.hist[i] = 0u;
+            for (uint32_t c_lo = seg_lo; c_lo < seg_hi; c_lo += kKeyCap) {
+                const uint32_t c_hi = min(seg_hi, c_lo + (uint32_t)kKeyCap);
+                key_base = c_lo;
+                __syncthreads();
+                stream_range(c_lo, c_hi, nullptr);
+                __syncthreads();
+                // Add this pass's digit counts to the head's histogram, wait for
+                // them to land, and read the histogram back (device-coherent,
+                // coalesced, staged through LDS).  It holds this workgroup's keys
+                // and whatever the others have added so far; counts only grow,
+                // so its crossing T' is a lower bound of the final threshold digit.
+                for (int i = tid; i < kHistBins; i += kAttendThreads) {
+                    const uint32_t c = u.st.hist[i];
+                    if (c) {
+                        atomicAdd(&gh[i], c);
+                        u.st.hist[i] = 0u;
+                    }
+                }
+                wait_stores_complete();
+                __syncthreads();
+                {
+                    uint32_t gv[kHistPerThread];
+#pragma unroll
+                    for (int j = 0; j < kHistPerThread; ++j) gv[j] = coherent_load(&gh[tid + kAttendThreads * j]);
+#pragma unroll
+                    for (int j = 0; j < kHistPerThread; ++j) u.st.gbuf[tid + kAttendThreads * j] = gv[j];
+                }
+                __syncthreads();
+                uint32_t hc[kHistPerThread];
+#pragma unroll
+                for (int i = 0; i < kHistPerThread; ++i) hc[i] = u.st.gbuf[kHistBins - 1 - (tid * kHistPerThread + i)];
+                block_crossing<kHistPerThread>(hc, kHistBins, ke, s_wave, s_res);
+                const uint32_t Tp = s_res[0];
+                // append this pass's keys with digit >= T'
+                const uint32_t len = c_hi - c_lo;
+                uint32_t mine = 0;
+                for (uint32_t i = tid; i < len; i += kAttendThreads) mine += (u.st.keys[i] >> kLowBits) >= Tp;
+                uint32_t total;
+                uint32_t at = block_exclusive_scan(mine, s_wave, &total);
+                if (tid == 0) s_ctr = total ? counter_add(&p.ws.candcnt[bg], total) : 0u;
+                __syncthreads();
+                at += s_ctr;
+                for (uint32_t i = tid; i < len; i += kAttendThreads) {
+                    const uint32_t key = u.st.keys[i];
+                    if ((key >> kLowBits) >= Tp) {
+                        if (at < (uint32_t)p.max_ctx) coherent_store(&cand[at], pack_cand(key, c_lo + i));
+                        ++at;
+                    }
+                }
+            }
+            // ---- selection arrival: the last workgroup of the head resolves it ----
+            const int nw_h = wg_of(h1 - 1) - wg_of(h0) + 1;
+            wait_stores_complete();
+            __syncthreads();
+            if (tid == 0) {
+                const uint32_t old_t = counter_add(&p.ws.topkcnt[bg], 1u);
+                const int last_t = (old_t + 1u == (uint32_t)nw_h);
+                if (last_t) counter_reset(&p.ws.topkcnt[bg]);
+                s_flag[1] = last_t;
+            }
+            __syncthreads();
+            if (s_flag[1]) resolve_topk(bg, n, ke);
         } else {
             // sparse head: stage the S entries of the range in LDS (one batched
             // load per chunk), forward them to S_out, then gather-stream
@@ -496,17 +997,16 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 for (int j = 0; j < PER; ++j) {
                     const uint32_t pos = c_lo + tid + (uint32_t)(kAttendThreads * j);
                     if (pos < c_hi) {
-                        s_idx[pos - c_lo] = v[j];
+                        u.st.idx[pos - c_lo] = v[j];
                         if (Sout) Sout[pos] = v[j];
                     }
                 }
                 __syncthreads();
-                stream_range(c_lo, c_hi, s_idx);
+                stream_range(c_lo, c_hi, u.st.idx);
             }
             // entries past min(k, n) (the -1 padding of a short context) belong
             // to the workgroup that finishes the head
             if (Sout && h1 <= hi) {
-                const uint32_t ke = h1 - h0;
                 for (uint32_t i = ke + tid; i < (uint32_t)p.k; i += kAttendThreads) Sout[i] = Srow[i];
             }
         }
@@ -532,14 +1032,15 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 o[h][e] = v;
             }
         }
+        __syncthreads();
         if (row == 0) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) s_wo[wave][h][x * EPL + e] = o[h][e];
+                for (int e = 0; e < EPL; ++e) u.st.wo[wave][h][x * EPL + e] = o[h][e];
             if (x < G) {
-                s_wm[wave][x] = M;
-                s_wl[wave][x] = lw;
+                u.st.wm[wave][x] = M;
+                u.st.wl[wave][x] = lw;
             }
         }
         __syncthreads();
@@ -549,13 +1050,13 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             const int h = idx / D, t = idx - h * D;
             float Mw = -INFINITY;
 #pragma unroll
-            for (int wv = 0; wv < kWaves; ++wv) Mw = fmaxf(Mw, s_wm[wv][h]);
+            for (int wv = 0; wv < kWaves; ++wv) Mw = fmaxf(Mw, u.st.wm[wv][h]);
             float O = 0.0f, L = 0.0f;
 #pragma unroll
             for (int wv = 0; wv < kWaves; ++wv) {
-                const float s = safe_scale(s_wm[wv][h], Mw);
-                O += s_wo[wv][h][t] * s;
-                L += s_wl[wv][h] * s;
+                const float s = safe_scale(u.st.wm[wv][h], Mw);
+                O += u.st.wo[wv][h][t] * s;
+                L += u.st.wl[wv][h] * s;
             }
             coherent_store(&rec[2 * G + h * D + t], O);
             if (t == 0) {
@@ -564,21 +1065,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
         }
 
-        if constexpr (HYBRID) {
-            if (retr) {
-                uint32_t* gh = p.ws.hist + (size_t)bg * kHistBins;
-                for (int i = tid; i < kHistBins; i += kAttendThreads) {
-                    const uint32_t c = s_hist[i];
-                    if (c) {
-                        atomicAdd(&gh[i], c);
-                        s_hist[i] = 0u;
-                    }
-                }
-            }
-        }
-
-        // ---- arrival: the last workgroup of a group of 16 merges their records;
-        // the last group merger produces the output ----
+        // ---- arrival: records to the group merger, candidates to the selector ----
         const int wf = wg_of(h0), wl = wg_of(h1 - 1);
         const int nw = wl - wf + 1;
         const int c = (w - wf) / kCombineFanIn;
@@ -591,17 +1078,17 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             const uint32_t old = counter_add(ctr, 1u);
             const int last = (int)(old + 1u == (uint32_t)csize);
             if (last) counter_reset(ctr);
-            s_flag = last;
+            s_flag[0] = last;
         }
         __syncthreads();
-        if (s_flag) {
+        if (s_flag[0]) {
             const float* grp = p.ws.rec1 + (size_t)(wf + c * kCombineFanIn + bg) * RS;
             float* out_bg = p.out + ((size_t)b * Hq + (size_t)g * G) * D;
             if (nc == 1) {
-                merge_records<D, G>(grp, csize, nullptr, out_bg, s_ml);
+                merge_records<D, G>(grp, csize, nullptr, out_bg, u.st.ml);
             } else {
                 float* r2 = p.ws.rec2 + ((size_t)bg * kLevel2Max + c) * RS;
-                merge_records<D, G>(grp, csize, r2, nullptr, s_ml);
+                merge_records<D, G>(grp, csize, r2, nullptr, u.st.ml);
                 wait_stores_complete();
                 __syncthreads();
                 if (tid == 0) {
@@ -609,14 +1096,13 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     const uint32_t old = counter_add(ctr, 1u);
                     const int last = (int)(old + 1u == (uint32_t)nc);
                     if (last) counter_reset(ctr);
-                    s_flag = last;
+                    s_flag[0] = last;
                 }
                 __syncthreads();
-                if (s_flag) {
-                    merge_records<D, G>(p.ws.rec2 + (size_t)bg * kLevel2Max * RS, nc, nullptr, out_bg, s_ml);
-                }
+                if (s_flag[0]) merge_records<D, G>(p.ws.rec2 + (size_t)bg * kLevel2Max * RS, nc, nullptr, out_bg, u.st.ml);
             }
         }
+
         __syncthreads();
     }
 }

@@ -18,17 +18,21 @@ constexpr int kIdxBits = 18;
 // ---------------------------------------------------------------- attention kernel
 constexpr int kAttendThreads = 256;   // 4 wavefronts of 64
 constexpr int kWaves = kAttendThreads / 64;
-constexpr int kUnitAlign = 16;        // workgroup range boundaries are multiples of 16 units
-constexpr int kMinUnitsPerWG = 64;    // never split the pool finer than this
-constexpr int kCombineFanIn = 16;     // level-1 combine groups of consecutive workgroups
+constexpr int kCombineFanIn = 32;     // level-1 combine groups of consecutive workgroups
 constexpr int kLevel2Max = kMaxWG / kCombineFanIn + 2;
+// Pool cost of one unit of work: a streamed key row (retrieval head) costs 4,
+// a gathered S row (sparse head) 7 -- gathers of scattered 256-byte rows run
+// at about 4/7 of the streaming rate, measured on the 128K workload.
+constexpr uint32_t kCostRetrieval = 4;
+constexpr uint32_t kCostSparse = 7;
+constexpr uint32_t kMinCostPerWG = 64 * kCostSparse;   // never split the pool finer than this
+constexpr int kIdxChunk = 2048;       // sparse S positions staged in LDS per pass
+constexpr int kKeyCap = 4096;         // retrieval selection keys kept in LDS per pass
 
 // ---------------------------------------------------------------- selection
-constexpr int kHistBits = 12;                 // first radix digit, histogrammed by the attention kernel
+constexpr int kHistBits = 12;                 // first radix digit, histogrammed while streaming
 constexpr int kHistBins = 1 << kHistBits;
-constexpr int kSelectThreads = 256;
-constexpr int kSelectSeg = 4096;              // scores scanned per select workgroup
-constexpr int kCandLds = 8192;                // candidates resolved in LDS; more go through global passes first
+constexpr int kCandLds = 4096;                // threshold-digit candidates resolved in LDS
 
 // Cross-workgroup hand-off without cache-wide maintenance.  Data one
 // workgroup leaves for another inside the same launch is written with
@@ -64,18 +68,16 @@ __host__ __device__ inline uint32_t float_key(float f) {
 
 // ---------------------------------------------------------------- workspace
 struct Workspace {
-    float* rec1;        // [(kMaxWG + BH) * RS]        level-1 partial records
-    float* rec2;        // [BH * kLevel2Max * RS]      level-2 partial records
-    float* scores;      // [BH * sstride]              pooled selection scores
-    int32_t sstride;    // score row stride (max_ctx rounded up to a multiple of 4)
-    int32_t* above;     // [BH * k_max]                indices above the threshold digit
-    uint2* cand;        // [BH * max_ctx]              (key, index) in the threshold digit
+    float* rec1;                 // [(kMaxWG + BH) * RS]      level-1 partial records
+    float* rec2;                 // [BH * kLevel2Max * RS]    level-2 partial records
+    unsigned long long* cand;    // [BH * max_ctx]            selection candidates (key | index << 32)
     // ---- zero-initialised region (restored to zero by every call) ----
-    uint32_t* cnt1;     // [BH * kLevel2Max]
-    uint32_t* cnt2;     // [BH]
-    uint32_t* hist;     // [BH * kHistBins]
-    uint32_t* selcnt;   // [BH * 4]: segments arrived, above count, candidate count
-    uint32_t* err;      // [4]
+    uint32_t* cnt1;              // [BH * kLevel2Max]         level-1 arrival counters
+    uint32_t* cnt2;              // [BH]                      level-2 arrival counters
+    uint32_t* candcnt;           // [BH]                      candidates appended
+    uint32_t* topkcnt;           // [BH]                      workgroups done appending
+    uint32_t* hist;              // [BH * kHistBins]          first-digit histogram of selection keys
+    uint32_t* err;               // [4]
     void* zero_begin;
     size_t zero_bytes;
     size_t total_bytes;
@@ -87,6 +89,7 @@ inline int record_floats(int G, int D) { return G * (D + 2); }
 
 // Carve a workspace for the given dims from `base` (nullptr -> sizes only).
 inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int max_ctx, int k_max) {
+    (void)k_max;
     const int BH = B * Hkv;
     const int G = Hq / Hkv;
     const size_t RS = (size_t)record_floats(G, D);
@@ -98,31 +101,27 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     };
     size_t o_rec1 = take(sizeof(float) * (size_t)(kMaxWG + BH) * RS);
     size_t o_rec2 = take(sizeof(float) * (size_t)BH * kLevel2Max * RS);
-    const int sstride = (max_ctx + 3) & ~3;
-    size_t o_scores = take(sizeof(float) * (size_t)BH * sstride);
-    size_t o_above = take(sizeof(int32_t) * (size_t)BH * k_max);
-    size_t o_cand = take(sizeof(uint2) * (size_t)BH * max_ctx);
+    size_t o_cand = take(sizeof(unsigned long long) * (size_t)BH * max_ctx);
     size_t z0 = off;
     size_t o_cnt1 = take(sizeof(uint32_t) * (size_t)BH * kLevel2Max);
     size_t o_cnt2 = take(sizeof(uint32_t) * (size_t)BH);
+    size_t o_cc = take(sizeof(uint32_t) * (size_t)BH);
+    size_t o_tc = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_hist = take(sizeof(uint32_t) * (size_t)BH * kHistBins);
-    size_t o_sel = take(sizeof(uint32_t) * (size_t)BH * 4);
     size_t o_err = take(sizeof(uint32_t) * 4);
     Workspace w{};
     char* p = (char*)base;
     w.total_bytes = off;
-    w.sstride = sstride;
     w.zero_bytes = off - z0;
     if (p) {
         w.rec1 = (float*)(p + o_rec1);
         w.rec2 = (float*)(p + o_rec2);
-        w.scores = (float*)(p + o_scores);
-        w.above = (int32_t*)(p + o_above);
-        w.cand = (uint2*)(p + o_cand);
+        w.cand = (unsigned long long*)(p + o_cand);
         w.cnt1 = (uint32_t*)(p + o_cnt1);
         w.cnt2 = (uint32_t*)(p + o_cnt2);
+        w.candcnt = (uint32_t*)(p + o_cc);
+        w.topkcnt = (uint32_t*)(p + o_tc);
         w.hist = (uint32_t*)(p + o_hist);
-        w.selcnt = (uint32_t*)(p + o_sel);
         w.err = (uint32_t*)(p + o_err);
         w.zero_begin = p + z0;
     }
@@ -144,17 +143,8 @@ struct AttendParams {
     float scale_log2;       // log2(e) / sqrt(d)
 };
 
-struct SelectParams {
-    const int32_t* n_ctx;
-    int32_t* S_out;
-    Workspace ws;
-    uint64_t role_bits;
-    int32_t B, Hkv, max_ctx, k, k_max, n_retrieval;
-};
-
-// Host launchers (defined next to their kernels).  dtype: 0 fp32, 1 bf16.
+// Host launcher (defined next to the kernel).  dtype: 0 fp32, 1 bf16.
 hipError_t launch_attend(const AttendParams& p, int dtype, int D, int G, bool hybrid, int grid,
                          hipStream_t stream);
-hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 
 }  // namespace lychee
