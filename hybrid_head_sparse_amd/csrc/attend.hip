@@ -299,23 +299,33 @@ __device__ __forceinline__ uint32_t comp_digit(unsigned long long c, int shift, 
     return (uint32_t)(c >> shift) & ((1u << bits) - 1u);
 }
 
+// Inclusive prefix sum across the 64 lanes of a wavefront: shifts within
+// each row of 16 lanes (1, 2, 4, 8), then the row broadcasts of lane 15 into
+// rows 1 and 3 and of lane 31 into rows 2 and 3.  Lanes whose DPP source is
+// outside the row or whose row is masked off add the `old` operand, 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return x;
+}
+
 // Block-wide exclusive prefix sum of one value per thread.
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t inc = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(inc, off);
-        if (lane >= off) inc += y;
-    }
+    const uint32_t inc = wave_inclusive_scan(v);
     __syncthreads();
     if (lane == 63) s_wave[wave] = inc;
     __syncthreads();
     uint32_t base = 0, tot = 0;
 #pragma unroll
     for (int wv = 0; wv < kWaves; ++wv) {
-        if (wv < wave) base += s_wave[wv];
-        tot += s_wave[wv];
+        const uint32_t c = s_wave[wv];
+        base += (wv < wave) ? c : 0u;
+        tot += c;
     }
     *total = tot;
     return base + inc - v;
@@ -382,7 +392,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     struct SelectLds {
         uint32_t bits[HYBRID ? kBitsLds : 1];
         union {
-            unsigned long long comp[HYBRID ? kCandLds : 1];   // threshold-digit candidates
+            unsigned long long comp[HYBRID ? kCandLds + kAttendThreads : 1];   // threshold-digit candidates
+                                                                               // (+ one spare slot per thread)
             uint32_t h12[HYBRID ? kHistBins : 1];              // the head's final first-digit histogram
         };
         uint32_t h[256];
@@ -495,33 +506,54 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     };
     const uint32_t lo = s_bound[w], hi = s_bound[w + 1];
 
-    // Classify the NB candidates this thread holds (slot e is candidate
-    // base + tid + 256 e of C): first digit above T_ -> bitmap; equal -> the
-    // composite is appended to u.se.comp after the c_eq already there (one
-    // block scan orders the appends; no per-candidate LDS atomics).
-    auto classify_batch = [&](auto& vals, uint32_t base, uint32_t C, uint32_t T_, uint32_t& c_eq) {
+    // Classify the candidates this thread holds (slot e is candidate
+    // base + tid + 256 e; slots from nslots on, or past C, hold none): key above
+    // the threshold digit's range -> bitmap; inside it -> the composite is
+    // appended to u.se.comp after the c_eq already there, ordered by one block
+    // scan.  Branch-free per slot: the bitmap OR and the append always
+    // execute, with a zero operand or this thread's spare slot past kCandLds.
+    auto classify_batch = [&](auto& vals, uint32_t nslots, uint32_t base, uint32_t C, uint32_t klo, uint32_t khi,
+                              uint32_t& c_eq) {
         constexpr int NB = (int)(sizeof(vals) / sizeof(vals[0]));
-        static_assert(NB <= 64, "mask holds 64 slots");
+        static_assert(NB % 8 == 0 && NB <= 64, "slots come in groups of 8, at most 64");
+        const uint32_t lim = C - base;
         unsigned long long eqm = 0;
 #pragma unroll
-        for (int e = 0; e < NB; ++e) {
-            const bool valid = base + tid + (uint32_t)(kAttendThreads * e) < C;
-            const uint32_t key = (uint32_t)vals[e], j = (uint32_t)(vals[e] >> 32);
-            const uint32_t dg = key >> kLowBits;
-            if (valid && dg > T_) atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31));
-            if (valid && dg == T_) eqm |= 1ull << e;
+        for (int g8 = 0; g8 < NB; g8 += 8) {
+            if ((uint32_t)g8 < nslots) {
+#pragma unroll
+                for (int e = g8; e < g8 + 8; ++e) {
+                    const uint32_t key = (uint32_t)vals[e];
+                    const uint32_t j = (uint32_t)(vals[e] >> 32) & kIdxMask;
+                    const bool valid = tid + (uint32_t)(kAttendThreads * e) < lim;
+                    const bool above = valid && key > khi;
+                    const bool eq = valid && ((key - klo) >> kLowBits) == 0u;
+                    atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], above ? (1u << (j & 31)) : 0u);
+                    eqm |= (unsigned long long)eq << e;
+                }
+            }
         }
         uint32_t tot;
         uint32_t pos = c_eq + block_exclusive_scan((uint32_t)__popcll(eqm), s_wave, &tot);
+        if (tot) {
 #pragma unroll
-        for (int e = 0; e < NB; ++e) {
-            if ((eqm >> e) & 1ull) {
-                if (pos < (uint32_t)kCandLds) u.se.comp[pos] = composite((uint32_t)vals[e], (uint32_t)(vals[e] >> 32));
-                ++pos;
+            for (int g8 = 0; g8 < NB; g8 += 8) {
+                if ((uint32_t)g8 < nslots) {
+#pragma unroll
+                    for (int e = g8; e < g8 + 8; ++e) {
+                        const bool is = (eqm >> e) & 1ull;
+                        const uint32_t at = (is && pos < (uint32_t)kCandLds) ? pos : (uint32_t)(kCandLds + tid);
+                        u.se.comp[at] = composite((uint32_t)vals[e], (uint32_t)(vals[e] >> 32) & kIdxMask);
+                        pos += is;
+                    }
+                }
             }
         }
         c_eq += tot;
     };
+
+    // Set the bitmap bit of index j.
+    auto mark = [&](uint32_t j) { atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31)); };
 
     // Exact top-k of one retrieval head: the final first-digit histogram gives
     // the threshold digit T and the count above it; every key with digit >= T
@@ -536,19 +568,25 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         if (ke == (uint32_t)n) {
             for (int i = tid; i < p.k; i += kAttendThreads) srow[i] = (i < n) ? i : -1;
         } else {
-            constexpr int RC = 64;     // candidates loaded per thread with the count (16384 per head)
+            constexpr int RC = 64;     // candidate slots per thread in the first load (16384 per head)
             constexpr int kB = 16;     // batch of later candidates
-            const uint32_t C = max(1u, min(coherent_load(&p.ws.candcnt[hb]), (uint32_t)p.max_ctx));
-            unsigned long long cv[RC];
-#pragma unroll
-            for (int e = 0; e < RC; ++e)     // issued with the count, filtered by it afterwards
-                cv[e] = coherent_load(&cand[min(tid + (uint32_t)(kAttendThreads * e), (uint32_t)p.max_ctx - 1u)]);
+            // round 1: the candidate count and the final histogram
+            uint32_t C = coherent_load(&p.ws.candcnt[hb]);
             {
                 uint32_t gv[kHistPerThread];
 #pragma unroll
                 for (int j = 0; j < kHistPerThread; ++j) gv[j] = coherent_load(&gh[tid + kAttendThreads * j]);
+                C = __builtin_amdgcn_readfirstlane(max(1u, min(C, (uint32_t)p.max_ctx)));
 #pragma unroll
                 for (int j = 0; j < kHistPerThread; ++j) u.se.h12[tid + kAttendThreads * j] = gv[j];
+            }
+            // round 2: the candidates (in flight while the threshold is found)
+            const uint32_t nslots = min((C + kAttendThreads - 1) / kAttendThreads, (uint32_t)RC);
+            unsigned long long cv[RC];
+#pragma unroll
+            for (int e = 0; e < RC; ++e) {
+                cv[e] = 0ull;
+                if ((uint32_t)e < nslots) cv[e] = coherent_load(&cand[min(tid + (uint32_t)(kAttendThreads * e), C - 1u)]);
             }
             for (int i = tid; i <= bit_slot(W - 1); i += kAttendThreads) u.se.bits[i] = 0u;
             __syncthreads();
@@ -568,13 +606,15 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             block_crossing<kHistPerThread>(hc, kHistBins, ke, s_wave, s_res);
             const uint32_t T_ = s_res[0];
             const uint32_t c_above = s_res[1];
+            const uint32_t klo = T_ << kLowBits;
+            const uint32_t khi = klo | ((1u << kLowBits) - 1u);
             uint32_t c_eq = 0;
-            classify_batch(cv, 0u, C, T_, c_eq);
+            classify_batch(cv, nslots, 0u, C, klo, khi, c_eq);
             for (uint32_t base = kAttendThreads * RC; base < C; base += kAttendThreads * kB) {
                 unsigned long long bv[kB];
 #pragma unroll
                 for (int e = 0; e < kB; ++e) bv[e] = coherent_load(&cand[min(base + tid + (uint32_t)(kAttendThreads * e), C - 1)]);
-                classify_batch(bv, base, C, T_, c_eq);
+                classify_batch(bv, (uint32_t)kB, base, C, klo, khi, c_eq);
             }
             __syncthreads();
             uint32_t c_left = c_eq;
@@ -672,8 +712,23 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 }
                 done = true;
             }
-            // radix select in LDS over the remaining composite bits
+            // radix select in LDS over the remaining composite bits; a group of
+            // at most 64 is finished by direct rank in one wavefront
             while (!done) {
+                if (c_left <= 64u) {
+                    if (wave == 0) {
+                        const unsigned long long mine = lane < (int)c_left ? u.se.comp[lane] : 0ull;
+                        uint32_t above = 0;
+                        for (uint32_t r = 0; r < c_left; ++r) {
+                            const uint32_t olo = __builtin_amdgcn_readlane((uint32_t)mine, r);
+                            const uint32_t ohi = __builtin_amdgcn_readlane((uint32_t)(mine >> 32), r);
+                            above += ((((unsigned long long)ohi << 32) | olo) > mine);
+                        }
+                        if (lane < (int)c_left && above < r_left) mark(comp_index(mine));
+                    }
+                    done = true;
+                    break;
+                }
                 if (shift == 0) {             // unreachable: composites are distinct
                     if (tid == 0) atomicOr(p.ws.err, 2u);
                     break;
@@ -684,12 +739,18 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 __syncthreads();
                 unsigned long long mine[kCandPerThread];
                 uint32_t dg[kCandPerThread];
+                const uint32_t nsl = (c_left + kAttendThreads - 1) / kAttendThreads;
 #pragma unroll
                 for (int e = 0; e < kCandPerThread; ++e) {
                     const uint32_t i = tid + (uint32_t)(kAttendThreads * e);
-                    mine[e] = (i < c_left) ? u.se.comp[i] : 0ull;
-                    dg[e] = (i < c_left) ? comp_digit(mine[e], shift, bits) : 0xFFFFFFFFu;
-                    if (i < c_left) atomicAdd(&u.se.h[dg[e]], 1u);
+                    mine[e] = 0ull;
+                    dg[e] = 0xFFFFFFFFu;
+                    if ((uint32_t)e < nsl) {
+                        mine[e] = u.se.comp[min(i, (uint32_t)kCandLds - 1u)];
+                        const bool valid = i < c_left;
+                        dg[e] = valid ? comp_digit(mine[e], shift, bits) : 0xFFFFFFFFu;
+                        atomicAdd(&u.se.h[valid ? dg[e] : 0u], valid ? 1u : 0u);
+                    }
                 }
                 __syncthreads();
                 uint32_t hb1[1] = {tid < (1 << bits) ? u.se.h[(1 << bits) - 1 - tid] : 0u};
@@ -699,17 +760,23 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 uint32_t m = 0;
 #pragma unroll
                 for (int e = 0; e < kCandPerThread; ++e) {
-                    if (dg[e] != 0xFFFFFFFFu && dg[e] > Dg) {
-                        const uint32_t j = comp_index(mine[e]);
-                        atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31));
+                    if ((uint32_t)e < nsl) {
+                        const bool sel = dg[e] != 0xFFFFFFFFu && dg[e] > Dg;
+                        const uint32_t j = comp_index(mine[e]) & kIdxMask;
+                        atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], sel ? (1u << (j & 31)) : 0u);
+                        m |= (uint32_t)(dg[e] == Dg) << e;
                     }
-                    if (dg[e] == Dg) m |= 1u << e;
                 }
                 uint32_t tot;
                 uint32_t pos = block_exclusive_scan((uint32_t)__popc(m), s_wave, &tot);
 #pragma unroll
-                for (int e = 0; e < kCandPerThread; ++e)
-                    if ((m >> e) & 1u) u.se.comp[pos++] = mine[e];
+                for (int e = 0; e < kCandPerThread; ++e) {
+                    if ((uint32_t)e < nsl) {
+                        const bool is = (m >> e) & 1u;
+                        u.se.comp[is ? pos : (uint32_t)(kCandLds + tid)] = mine[e];
+                        pos += is;
+                    }
+                }
                 __syncthreads();
                 r_left -= gt;
                 c_left = keep;
@@ -725,23 +792,36 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 __syncthreads();
             }
             __syncthreads();
-            // Emit the bitmap in ascending order: every thread owns WPT
-            // consecutive words (padded slots: no bank conflicts), one block
-            // scan of the per-thread counts gives each its first position.
-            const int WPT = (W + kAttendThreads - 1) / kAttendThreads;
-            const int w0 = tid * WPT;
-            const int w1 = min(W, w0 + WPT);
+            // Emit the bitmap in ascending order.  Wavefront v owns the words
+            // [v WPW, (v+1) WPW); it counts them, takes its first position from
+            // the counts of the wavefronts before it, then walks them 64 at a
+            // time, one word per lane: a wavefront scan of the words' bit counts
+            // gives each lane its positions, so a wavefront's stores are
+            // consecutive.
+            constexpr int kMaxSteps = kWords / (kWaves * 64);
+            const int WPW = ((W + kWaves * 64 - 1) / (kWaves * 64)) * 64;
+            const int wb = wave * WPW, we = min(W, wb + WPW);
             uint32_t cnt = 0;
-            for (int i = w0; i < w1; ++i) cnt += __popc(u.se.bits[bit_slot(i)]);
+#pragma unroll
+            for (int st = 0; st < kMaxSteps; ++st) {
+                const int i = wb + st * 64 + lane;
+                if (st * 64 < WPW) cnt += __popc(i < we ? u.se.bits[bit_slot(i)] : 0u);
+            }
             uint32_t total;
-            uint32_t pos = block_exclusive_scan(cnt, s_wave, &total);
-            for (int i = w0; i < w1; ++i) {
-                uint32_t bw = u.se.bits[bit_slot(i)];
+            uint32_t pos = block_exclusive_scan(cnt, s_wave, &total);   // this lane's words come first...
+            pos = __builtin_amdgcn_readfirstlane(pos);                   // ...lane 0's base is the wavefront's
+            for (int i0 = wb; i0 < we; i0 += 64) {
+                const int i = i0 + lane;
+                uint32_t bw = i < we ? u.se.bits[bit_slot(i)] : 0u;
+                const uint32_t c = __popc(bw);
+                const uint32_t incl = wave_inclusive_scan(c);
+                uint32_t at = pos + incl - c;
+                pos += __builtin_amdgcn_readlane(incl, 63);
                 while (bw) {
                     const int bit = __ffs(bw) - 1;
                     bw &= bw - 1u;
-                    if (pos < ke) srow[pos] = i * 32 + bit;
-                    ++pos;
+                    if (at < ke) srow[at] = i * 32 + bit;
+                    ++at;
                 }
             }
             for (int i = (int)ke + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
@@ -948,8 +1028,17 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 }
                 __syncthreads();
                 uint32_t hc[kHistPerThread];
+                {
+                    const uint4* hv = reinterpret_cast<const uint4*>(u.st.gbuf + kHistBins - kHistPerThread * (tid + 1));
 #pragma unroll
-                for (int i = 0; i < kHistPerThread; ++i) hc[i] = u.st.gbuf[kHistBins - 1 - (tid * kHistPerThread + i)];
+                    for (int c = 0; c < kHistPerThread / 4; ++c) {
+                        const uint4 v4 = hv[c];
+                        hc[kHistPerThread - 1 - 4 * c] = v4.x;
+                        hc[kHistPerThread - 2 - 4 * c] = v4.y;
+                        hc[kHistPerThread - 3 - 4 * c] = v4.z;
+                        hc[kHistPerThread - 4 - 4 * c] = v4.w;
+                    }
+                }
                 block_crossing<kHistPerThread>(hc, kHistBins, ke, s_wave, s_res);
                 const uint32_t Tp = s_res[0];
                 // append this pass's keys with digit >= T'
@@ -969,18 +1058,6 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     }
                 }
             }
-            // ---- selection arrival: the last workgroup of the head resolves it ----
-            const int nw_h = wg_of(h1 - 1) - wg_of(h0) + 1;
-            wait_stores_complete();
-            __syncthreads();
-            if (tid == 0) {
-                const uint32_t old_t = counter_add(&p.ws.topkcnt[bg], 1u);
-                const int last_t = (old_t + 1u == (uint32_t)nw_h);
-                if (last_t) counter_reset(&p.ws.topkcnt[bg]);
-                s_flag[1] = last_t;
-            }
-            __syncthreads();
-            if (s_flag[1]) resolve_topk(bg, n, ke);
         } else {
             // sparse head: stage the S entries of the range in LDS (one batched
             // load per chunk), forward them to S_out, then gather-stream
@@ -1101,6 +1178,20 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 __syncthreads();
                 if (s_flag[0]) merge_records<D, G>(p.ws.rec2 + (size_t)bg * kLevel2Max * RS, nc, nullptr, out_bg, u.st.ml);
             }
+        }
+
+        // ---- selection arrival (after the record, which the head's output
+        // waits for): the last workgroup of a retrieval head resolves its top-k ----
+        if (HYBRID && retr) {
+            if (tid == 0) {
+                const int nw_h = wl - wf + 1;
+                const uint32_t old_t = counter_add(&p.ws.topkcnt[bg], 1u);
+                const int last_t = (old_t + 1u == (uint32_t)nw_h);
+                if (last_t) counter_reset(&p.ws.topkcnt[bg]);
+                s_flag[1] = last_t;
+            }
+            __syncthreads();
+            if (s_flag[1]) resolve_topk(bg, n, ke);
         }
 
         __syncthreads();
