@@ -21,7 +21,8 @@ struct lychee_handle {
     Workspace ws;
     hipStream_t stream;
     int device;
-    int grid;            // persistent attention workgroups per launch
+    int cus;             // compute units of the device
+    int per_cu;          // persistent workgroups per compute unit
     hipEvent_t ev_start;
     hipEvent_t ev_stop;
 };
@@ -183,17 +184,17 @@ lychee_status lychee_create(const lychee_dims* dims, void* workspace, size_t wor
                             dims->k_max);
     h->stream = (hipStream_t)stream;
     h->device = dev;
-    // persistent attention workgroups: LYCHEE_ATTEND_WG_PER_CU per compute unit
-    // (a tuning knob; default 2, the occupancy of the bf16 d=128 variants)
-    int per_cu = 2;
+    // persistent attention workgroups per compute unit: one (the hybrid
+    // variants hold more than 256 VGPRs, so a second would only queue behind
+    // the first; the dense variants stream fastest with one as well), or
+    // LYCHEE_ATTEND_WG_PER_CU (1..8) when set
+    int per_cu = 1;
     if (const char* env = getenv("LYCHEE_ATTEND_WG_PER_CU")) {
         const int v = atoi(env);
         if (v >= 1 && v <= 8) per_cu = v;
     }
-    int grid = cus * per_cu;
-    if (grid > kMaxWG) grid = kMaxWG;
-    if (grid < 1) grid = 1;
-    h->grid = grid;
+    h->cus = cus;
+    h->per_cu = per_cu;
     h->ev_start = nullptr;
     h->ev_stop = nullptr;
     if (hipMemsetAsync(h->ws.zero_begin, 0, h->ws.zero_bytes, h->stream) != hipSuccess) {
@@ -244,7 +245,7 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
     const int G = d.n_q_heads / d.n_kv_heads;
     if (h->ev_start && hipEventRecord(h->ev_start, h->stream) != hipSuccess)
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
-    hipError_t e = launch_attend(ap, d.dtype, d.head_dim, G, hybrid, h->grid, h->stream);
+    hipError_t e = launch_attend(ap, d.dtype, d.head_dim, G, hybrid, h->cus, h->per_cu, h->stream);
     if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
     if (h->ev_stop && hipEventRecord(h->ev_stop, h->stream) != hipSuccess)
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");

@@ -1199,37 +1199,40 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 }
 
 template <typename T, int D, int G, bool HYBRID>
-hipError_t launch_one(const AttendParams& p, int grid, hipStream_t stream) {
+hipError_t launch_one(const AttendParams& p, int cus, int per_cu, hipStream_t stream) {
+    int grid = cus * per_cu;
+    if (grid > kMaxWG) grid = kMaxWG;
+    if (grid < 1) grid = 1;
     hipLaunchKernelGGL((attend_kernel<T, D, G, HYBRID>), dim3(grid), dim3(kAttendThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <typename T, int D, bool HYBRID>
-hipError_t launch_g(const AttendParams& p, int G, int grid, hipStream_t stream) {
+hipError_t launch_g(const AttendParams& p, int G, int cus, int per_cu, hipStream_t stream) {
     switch (G) {
-        case 1: return launch_one<T, D, 1, HYBRID>(p, grid, stream);
-        case 2: return launch_one<T, D, 2, HYBRID>(p, grid, stream);
-        case 4: return launch_one<T, D, 4, HYBRID>(p, grid, stream);
-        case 8: return launch_one<T, D, 8, HYBRID>(p, grid, stream);
+        case 1: return launch_one<T, D, 1, HYBRID>(p, cus, per_cu, stream);
+        case 2: return launch_one<T, D, 2, HYBRID>(p, cus, per_cu, stream);
+        case 4: return launch_one<T, D, 4, HYBRID>(p, cus, per_cu, stream);
+        case 8: return launch_one<T, D, 8, HYBRID>(p, cus, per_cu, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T, bool HYBRID>
-hipError_t launch_d(const AttendParams& p, int D, int G, int grid, hipStream_t stream) {
-    if (D == 64) return launch_g<T, 64, HYBRID>(p, G, grid, stream);
-    if (D == 128) return launch_g<T, 128, HYBRID>(p, G, grid, stream);
+hipError_t launch_d(const AttendParams& p, int D, int G, int cus, int per_cu, hipStream_t stream) {
+    if (D == 64) return launch_g<T, 64, HYBRID>(p, G, cus, per_cu, stream);
+    if (D == 128) return launch_g<T, 128, HYBRID>(p, G, cus, per_cu, stream);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_attend(const AttendParams& p, int dtype, int D, int G, bool hybrid, int grid,
+hipError_t launch_attend(const AttendParams& p, int dtype, int D, int G, bool hybrid, int cus, int per_cu,
                          hipStream_t stream) {
-    if (dtype == 1) return hybrid ? launch_d<BF16, true>(p, D, G, grid, stream)
-                                  : launch_d<BF16, false>(p, D, G, grid, stream);
-    if (dtype == 0) return hybrid ? launch_d<F32, true>(p, D, G, grid, stream)
-                                  : launch_d<F32, false>(p, D, G, grid, stream);
+    if (dtype == 1) return hybrid ? launch_d<BF16, true>(p, D, G, cus, per_cu, stream)
+                                  : launch_d<BF16, false>(p, D, G, cus, per_cu, stream);
+    if (dtype == 0) return hybrid ? launch_d<F32, true>(p, D, G, cus, per_cu, stream)
+                                  : launch_d<F32, false>(p, D, G, cus, per_cu, stream);
     return hipErrorInvalidValue;
 }
 

@@ -143,8 +143,9 @@ struct AttendParams {
     float scale_log2;       // log2(e) / sqrt(d)
 };
 
-// Host launcher (defined next to the kernel).  dtype: 0 fp32, 1 bf16.
-hipError_t launch_attend(const AttendParams& p, int dtype, int D, int G, bool hybrid, int grid,
+// Host launcher (defined next to the kernel).  dtype: 0 fp32, 1 bf16.  The
+// persistent grid is `cus` times `per_cu` workgroups (at most kMaxWG).
+hipError_t launch_attend(const AttendParams& p, int dtype, int D, int G, bool hybrid, int cus, int per_cu,
                          hipStream_t stream);
 
 }  // namespace lychee
