@@ -282,9 +282,6 @@ constexpr int kLowBits = 32 - kHistBits;                 // key bits below the f
 constexpr uint32_t kIdxMask = (1u << kIdxBits) - 1u;
 constexpr int kCompBits = kLowBits + kIdxBits;           // composite: low key bits, then inverted index
 constexpr int kWords = kMaxCtx / 32;                     // context bitmap words
-constexpr int kBitsLds = kWords + kWords / 32;           // one pad word per 32: thread-contiguous
-                                                         // words fall in distinct LDS banks
-__device__ __forceinline__ int bit_slot(int word) { return word + (word >> 5); }
 constexpr int kHistPerThread = kHistBins / kAttendThreads;
 constexpr int kCandPerThread = kCandLds / kAttendThreads;
 
@@ -390,7 +387,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         float ml[merge_lds_floats<G>()];
     };
     struct SelectLds {
-        uint32_t bits[HYBRID ? kBitsLds : 1];
+        uint32_t bits[HYBRID ? kWords : 4];   // selected-position bitmap (16-byte aligned: read 4 words per lane)
         union {
             unsigned long long comp[HYBRID ? kCandLds + kAttendThreads : 1];   // threshold-digit candidates
                                                                                // (+ one spare slot per thread)
@@ -477,6 +474,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     // Workgroup boundaries: the equal split of the cost axis, moved up to the
     // next row boundary of the head it falls in (so every range holds whole
     // rows).  Every workgroup tabulates all P+1 of them once, in parallel.
+    const uint32_t qU = U / (uint32_t)P, rU = U % (uint32_t)P;   // ww * rU < P^2 <= 2^22
     for (int ww = tid; ww <= P; ww += kAttendThreads) {
         uint32_t bnd;
         if (ww == 0) {
@@ -484,7 +482,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         } else if (ww >= P) {
             bnd = U;
         } else {
-            const uint32_t raw = (uint32_t)((uint64_t)ww * U / (uint64_t)P);
+            const uint32_t raw = (uint32_t)ww * qU + ((uint32_t)ww * rU) / (uint32_t)P;   // = floor(ww U / P)
             int a = 0, z = BH - 1;                 // head holding raw (serial search per thread)
             while (a < z) {
                 const int mid = (a + z + 1) >> 1;
@@ -528,7 +526,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     const bool valid = tid + (uint32_t)(kAttendThreads * e) < lim;
                     const bool above = valid && key > khi;
                     const bool eq = valid && ((key - klo) >> kLowBits) == 0u;
-                    atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], above ? (1u << (j & 31)) : 0u);
+                    atomicOr(&u.se.bits[j >> 5], above ? (1u << (j & 31)) : 0u);
                     eqm |= (unsigned long long)eq << e;
                 }
             }
@@ -553,16 +551,22 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     };
 
     // Set the bitmap bit of index j.
-    auto mark = [&](uint32_t j) { atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31)); };
+    auto mark = [&](uint32_t j) { atomicOr(&u.se.bits[j >> 5], 1u << (j & 31)); };
 
     // Exact top-k of one retrieval head: the final first-digit histogram gives
     // the threshold digit T and the count above it; every key with digit >= T
     // is in the candidate list.  Writes S_out's row and restores the head's
     // zeroed histogram and candidate count.
-    auto resolve_topk = [&](int hb, int n, uint32_t ke) {
+    auto resolve_topk = [&](int hb, int n, uint32_t ke, uint32_t C) {
         int32_t* srow = p.S_out + (size_t)hb * p.k;
-        uint32_t* gh = p.ws.hist + (size_t)hb * kHistBins;
         const unsigned long long* cand = p.ws.cand + (size_t)hb * p.max_ctx;
+        const uint32_t* sc = p.ws.score + (size_t)hb * p.max_ctx;
+        uint32_t* gh = p.ws.hist + (size_t)hb * kHistBins;
+        bool fb = false;           // reading every key instead of the candidates
+        // candidate i of the list in use: (key, index) packed like the appends
+        auto fetch = [&](uint32_t i) -> unsigned long long {
+            return fb ? pack_cand(coherent_load(&sc[i]), i) : coherent_load(&cand[i]);
+        };
         const int W = (n + 31) >> 5;
         __syncthreads();
         if (ke == (uint32_t)n) {
@@ -570,28 +574,43 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         } else {
             constexpr int RC = 64;     // candidate slots per thread in the first load (16384 per head)
             constexpr int kB = 16;     // batch of later candidates
-            // round 1: the candidate count and the final histogram
-            uint32_t C = coherent_load(&p.ws.candcnt[hb]);
-            {
-                uint32_t gv[kHistPerThread];
-#pragma unroll
-                for (int j = 0; j < kHistPerThread; ++j) gv[j] = coherent_load(&gh[tid + kAttendThreads * j]);
-                C = __builtin_amdgcn_readfirstlane(max(1u, min(C, (uint32_t)p.max_ctx)));
-#pragma unroll
-                for (int j = 0; j < kHistPerThread; ++j) u.se.h12[tid + kAttendThreads * j] = gv[j];
-            }
-            // round 2: the candidates (in flight while the threshold is found)
+            // one round of loads: the head's histogram, the candidates (C came
+            // with the arrival that made this workgroup the last one) and the
+            // largest bound used
+            C = max(1u, min(C, (uint32_t)p.max_ctx));
             const uint32_t nslots = min((C + kAttendThreads - 1) / kAttendThreads, (uint32_t)RC);
+            const uint32_t bmaxv = coherent_load(&p.ws.bmax[hb]);
+            uint32_t gv[kHistPerThread];
+#pragma unroll
+            for (int j = 0; j < kHistPerThread; ++j) gv[j] = coherent_load(&gh[tid + kAttendThreads * j]);
             unsigned long long cv[RC];
 #pragma unroll
             for (int e = 0; e < RC; ++e) {
                 cv[e] = 0ull;
                 if ((uint32_t)e < nslots) cv[e] = coherent_load(&cand[min(tid + (uint32_t)(kAttendThreads * e), C - 1u)]);
             }
-            for (int i = tid; i <= bit_slot(W - 1); i += kAttendThreads) u.se.bits[i] = 0u;
-            __syncthreads();
-            uint32_t hc[kHistPerThread];
+#pragma unroll
+            for (int j = 0; j < kHistPerThread; ++j) u.se.h12[tid + kAttendThreads * j] = gv[j];
             {
+                const int W4 = (W + 3) >> 2;
+                uint4* b4 = reinterpret_cast<uint4*>(u.se.bits);
+                for (int i = tid; i < W4; i += kAttendThreads) b4[i] = make_uint4(0u, 0u, 0u, 0u);
+            }
+            auto hist_rest = [&](uint32_t from, uint32_t cnt) {    // candidates [from, cnt) from memory
+                for (uint32_t base = from; base < cnt; base += kAttendThreads * kB) {
+                    unsigned long long bv[kB];
+#pragma unroll
+                    for (int e = 0; e < kB; ++e) bv[e] = fetch(min(base + tid + (uint32_t)(kAttendThreads * e), cnt - 1u));
+#pragma unroll
+                    for (int e = 0; e < kB; ++e) {
+                        const bool valid = base + tid + (uint32_t)(kAttendThreads * e) < cnt;
+                        atomicAdd(&u.se.h12[valid ? ((uint32_t)bv[e] >> kLowBits) : 0u], valid ? 1u : 0u);
+                    }
+                }
+            };
+            __syncthreads();
+            auto crossing12 = [&]() {
+                uint32_t hc[kHistPerThread];
                 // thread t takes descending ranks 16t.. = bins 4095-16t down to 4080-16t
                 const uint4* hv = reinterpret_cast<const uint4*>(u.se.h12 + kHistBins - kHistPerThread * (tid + 1));
 #pragma unroll
@@ -602,19 +621,38 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     hc[kHistPerThread - 3 - 4 * c] = v4.z;
                     hc[kHistPerThread - 4 - 4 * c] = v4.w;
                 }
+                block_crossing<kHistPerThread>(hc, kHistBins, ke, s_wave, s_res);
+            };
+            crossing12();
+            uint32_t T_ = s_res[0];
+            uint32_t c_above = s_res[1];
+            // Every pass added its counts and appended its keys from its bound
+            // up, and every bound is <= bmax.  If bmax <= T, the histogram is
+            // exact from T up and the candidates hold every key from T up, so T
+            // is the head's threshold digit.  Otherwise a pass held more than its
+            // margin of the head's top keys: count and use every key instead.
+            fb = bmaxv > T_;
+            uint32_t Cs = C;
+            if (fb) {
+                Cs = (uint32_t)n;
+                __syncthreads();
+                for (int i = tid; i < kHistBins; i += kAttendThreads) u.se.h12[i] = 0u;
+                __syncthreads();
+                hist_rest(0u, Cs);
+                __syncthreads();
+                crossing12();
+                T_ = s_res[0];
+                c_above = s_res[1];
             }
-            block_crossing<kHistPerThread>(hc, kHistBins, ke, s_wave, s_res);
-            const uint32_t T_ = s_res[0];
-            const uint32_t c_above = s_res[1];
             const uint32_t klo = T_ << kLowBits;
             const uint32_t khi = klo | ((1u << kLowBits) - 1u);
             uint32_t c_eq = 0;
-            classify_batch(cv, nslots, 0u, C, klo, khi, c_eq);
-            for (uint32_t base = kAttendThreads * RC; base < C; base += kAttendThreads * kB) {
+            if (!fb) classify_batch(cv, nslots, 0u, C, klo, khi, c_eq);
+            for (uint32_t base = fb ? 0u : kAttendThreads * RC; base < Cs; base += kAttendThreads * kB) {
                 unsigned long long bv[kB];
 #pragma unroll
-                for (int e = 0; e < kB; ++e) bv[e] = coherent_load(&cand[min(base + tid + (uint32_t)(kAttendThreads * e), C - 1)]);
-                classify_batch(bv, (uint32_t)kB, base, C, klo, khi, c_eq);
+                for (int e = 0; e < kB; ++e) bv[e] = fetch(min(base + tid + (uint32_t)(kAttendThreads * e), Cs - 1u));
+                classify_batch(bv, (uint32_t)kB, base, Cs, klo, khi, c_eq);
             }
             __syncthreads();
             uint32_t c_left = c_eq;
@@ -631,13 +669,13 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     const int nshift = shift - bits;
                     for (int i = tid; i < 256; i += kAttendThreads) u.se.h[i] = 0u;
                     __syncthreads();
-                    for (uint32_t base = 0; base < C; base += kAttendThreads * kB) {
+                    for (uint32_t base = 0; base < Cs; base += kAttendThreads * kB) {
                         unsigned long long bv[kB];
 #pragma unroll
-                        for (int e = 0; e < kB; ++e) bv[e] = coherent_load(&cand[min(base + tid + (uint32_t)(kAttendThreads * e), C - 1)]);
+                        for (int e = 0; e < kB; ++e) bv[e] = fetch(min(base + tid + (uint32_t)(kAttendThreads * e), Cs - 1u));
 #pragma unroll
                         for (int e = 0; e < kB; ++e) {
-                            if (base + tid + (uint32_t)(kAttendThreads * e) >= C) continue;
+                            if (base + tid + (uint32_t)(kAttendThreads * e) >= Cs) continue;
                             const uint32_t key = (uint32_t)bv[e], j = (uint32_t)(bv[e] >> 32);
                             if ((key >> kLowBits) != T_) continue;
                             const unsigned long long cp = composite(key, j);
@@ -650,20 +688,20 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     block_crossing<1>(hb1, 1 << bits, r_left, s_wave, s_res);
                     const uint32_t Dg = min(s_res[0], (1u << bits) - 1u), gt = s_res[1];
                     const uint32_t keep = u.se.h[Dg];
-                    for (uint32_t base = 0; base < C; base += kAttendThreads * kB) {
+                    for (uint32_t base = 0; base < Cs; base += kAttendThreads * kB) {
                         unsigned long long bv[kB];
 #pragma unroll
-                        for (int e = 0; e < kB; ++e) bv[e] = coherent_load(&cand[min(base + tid + (uint32_t)(kAttendThreads * e), C - 1)]);
+                        for (int e = 0; e < kB; ++e) bv[e] = fetch(min(base + tid + (uint32_t)(kAttendThreads * e), Cs - 1u));
 #pragma unroll
                         for (int e = 0; e < kB; ++e) {
-                            if (base + tid + (uint32_t)(kAttendThreads * e) >= C) continue;
+                            if (base + tid + (uint32_t)(kAttendThreads * e) >= Cs) continue;
                             const uint32_t key = (uint32_t)bv[e], j = (uint32_t)(bv[e] >> 32);
                             if ((key >> kLowBits) != T_) continue;
                             const unsigned long long cp = composite(key, j);
                             if (shift < kCompBits && (cp >> shift) != prefix) continue;
                             const uint32_t dg = comp_digit(cp, nshift, bits);
                             if (dg > Dg || (r_left - gt == keep && dg == Dg))
-                                atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31));
+                                atomicOr(&u.se.bits[j >> 5], 1u << (j & 31));
                         }
                     }
                     __syncthreads();
@@ -676,17 +714,17 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 if (!done) {
                     // the k-th element's prefix group now fits in LDS: gather it
                     uint32_t c_pre = 0;
-                    for (uint32_t base = 0; base < C; base += kAttendThreads * kB) {
+                    for (uint32_t base = 0; base < Cs; base += kAttendThreads * kB) {
                         unsigned long long bv[kB];
                         unsigned long long cpv[kB];
 #pragma unroll
-                        for (int e = 0; e < kB; ++e) bv[e] = coherent_load(&cand[min(base + tid + (uint32_t)(kAttendThreads * e), C - 1)]);
+                        for (int e = 0; e < kB; ++e) bv[e] = fetch(min(base + tid + (uint32_t)(kAttendThreads * e), Cs - 1u));
                         unsigned long long m = 0;
 #pragma unroll
                         for (int e = 0; e < kB; ++e) {
                             const uint32_t key = (uint32_t)bv[e], j = (uint32_t)(bv[e] >> 32);
                             cpv[e] = composite(key, j);
-                            if (base + tid + (uint32_t)(kAttendThreads * e) < C && (key >> kLowBits) == T_ &&
+                            if (base + tid + (uint32_t)(kAttendThreads * e) < Cs && (key >> kLowBits) == T_ &&
                                 (cpv[e] >> shift) == prefix)
                                 m |= 1ull << e;
                         }
@@ -708,7 +746,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             if (!done && r_left == c_left) {   // the whole threshold group is selected
                 for (uint32_t i = tid; i < c_left; i += kAttendThreads) {
                     const uint32_t j = comp_index(u.se.comp[i]);
-                    atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31));
+                    atomicOr(&u.se.bits[j >> 5], 1u << (j & 31));
                 }
                 done = true;
             }
@@ -763,7 +801,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     if ((uint32_t)e < nsl) {
                         const bool sel = dg[e] != 0xFFFFFFFFu && dg[e] > Dg;
                         const uint32_t j = comp_index(mine[e]) & kIdxMask;
-                        atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], sel ? (1u << (j & 31)) : 0u);
+                        atomicOr(&u.se.bits[j >> 5], sel ? (1u << (j & 31)) : 0u);
                         m |= (uint32_t)(dg[e] == Dg) << e;
                     }
                 }
@@ -785,51 +823,106 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 } else if (r_left == c_left) {
                     for (uint32_t i = tid; i < c_left; i += kAttendThreads) {
                         const uint32_t j = comp_index(u.se.comp[i]);
-                        atomicOr(&u.se.bits[bit_slot((int)(j >> 5))], 1u << (j & 31));
+                        atomicOr(&u.se.bits[j >> 5], 1u << (j & 31));
                     }
                     done = true;
                 }
                 __syncthreads();
             }
             __syncthreads();
-            // Emit the bitmap in ascending order.  Wavefront v owns the words
-            // [v WPW, (v+1) WPW); it counts them, takes its first position from
-            // the counts of the wavefronts before it, then walks them 64 at a
-            // time, one word per lane: a wavefront scan of the words' bit counts
-            // gives each lane its positions, so a wavefront's stores are
-            // consecutive.
-            constexpr int kMaxSteps = kWords / (kWaves * 64);
-            const int WPW = ((W + kWaves * 64 - 1) / (kWaves * 64)) * 64;
+            // Emit S in ascending order.  Wavefront v owns the bitmap words
+            // [v WPW, (v+1) WPW): it counts them, takes its base from the counts
+            // of the wavefronts before it (block scan), then walks them 256 at a
+            // time, four consecutive words per lane (16-byte LDS reads); a
+            // wavefront scan of the lanes' bit counts gives each lane its first
+            // position, so a wavefront's stores are nearly consecutive.
+            constexpr int kMaxSteps = kWords / (kWaves * 256);
+            const int WPW = ((W + kWaves * 256 - 1) / (kWaves * 256)) * 256;
             const int wb = wave * WPW, we = min(W, wb + WPW);
+            const uint4* b4 = reinterpret_cast<const uint4*>(u.se.bits);
             uint32_t cnt = 0;
 #pragma unroll
             for (int st = 0; st < kMaxSteps; ++st) {
-                const int i = wb + st * 64 + lane;
-                if (st * 64 < WPW) cnt += __popc(i < we ? u.se.bits[bit_slot(i)] : 0u);
+                const int i = wb + st * 256 + lane * 4;
+                if (st * 256 < WPW && i < we) {
+                    const uint4 v = b4[i >> 2];
+                    cnt += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+                }
             }
             uint32_t total;
             uint32_t pos = block_exclusive_scan(cnt, s_wave, &total);   // this lane's words come first...
             pos = __builtin_amdgcn_readfirstlane(pos);                   // ...lane 0's base is the wavefront's
-            for (int i0 = wb; i0 < we; i0 += 64) {
-                const int i = i0 + lane;
-                uint32_t bw = i < we ? u.se.bits[bit_slot(i)] : 0u;
-                const uint32_t c = __popc(bw);
+            const uint32_t last = (uint32_t)p.k - 1u;
+            for (int i0 = wb; i0 < we; i0 += 256) {
+                const int i = i0 + lane * 4;
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (i < we) v = b4[i >> 2];
+                const uint32_t c = __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
                 const uint32_t incl = wave_inclusive_scan(c);
                 uint32_t at = pos + incl - c;
                 pos += __builtin_amdgcn_readlane(incl, 63);
-                while (bw) {
-                    const int bit = __ffs(bw) - 1;
-                    bw &= bw - 1u;
-                    if (at < ke) srow[at] = i * 32 + bit;
-                    ++at;
+                uint32_t wq[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t bw = wq[q];
+                    while (bw) {
+                        const int bit = __ffs(bw) - 1;
+                        bw &= bw - 1u;
+                        srow[min(at, last)] = (i + q) * 32 + bit;   // at < ke unless the counts disagree (flagged below)
+                        ++at;
+                    }
                 }
             }
             for (int i = (int)ke + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
             if (tid == 0 && total != ke) atomicOr(p.ws.err, 2u);
         }
-        // restore the zero invariant of the head's histogram and candidate count
+        // restore the zero invariant of the head's histogram and counters
         for (int i = tid; i < kHistBins; i += kAttendThreads) gh[i] = 0u;
-        if (tid == 0) counter_reset(&p.ws.candcnt[hb]);
+        if (tid == 0) {
+            counter_reset64(&p.ws.selctr[hb]);
+            counter_reset(&p.ws.bmax[hb]);
+        }
+        __syncthreads();
+    };
+
+    // Crossing of this workgroup's first-digit histogram of the current pass
+    // (u.st.hist) at `need`: the largest digit D with at least `need` keys of
+    // the pass at or above it (0 if the pass has fewer).
+    auto local_bound = [&](uint32_t need) -> uint32_t {
+        uint32_t hc[kHistPerThread];
+        const uint4* hv = reinterpret_cast<const uint4*>(u.st.hist + kHistBins - kHistPerThread * (tid + 1));
+#pragma unroll
+        for (int c = 0; c < kHistPerThread / 4; ++c) {
+            const uint4 v4 = hv[c];
+            hc[kHistPerThread - 1 - 4 * c] = v4.x;
+            hc[kHistPerThread - 2 - 4 * c] = v4.y;
+            hc[kHistPerThread - 3 - 4 * c] = v4.z;
+            hc[kHistPerThread - 4 - 4 * c] = v4.w;
+        }
+        block_crossing<kHistPerThread>(hc, kHistBins, need, s_wave, s_res);
+        return s_res[0];
+    };
+
+    // Append the keys of positions [c_lo, c_hi) held in u.st.keys whose first
+    // digit is >= Tb to head hb's candidate list (one block scan orders them,
+    // one atomic reserves the range; device-coherent stores).
+    auto append_keys = [&](int hb, uint32_t c_lo, uint32_t c_hi, uint32_t Tb) {
+        unsigned long long* cand = p.ws.cand + (size_t)hb * p.max_ctx;
+        const uint32_t len = c_hi - c_lo;
+        uint32_t mine = 0;
+        for (uint32_t i = tid; i < len; i += kAttendThreads) mine += (u.st.keys[i] >> kLowBits) >= Tb;
+        uint32_t total;
+        uint32_t at = block_exclusive_scan(mine, s_wave, &total);
+        if (tid == 0) s_ctr = total ? (uint32_t)counter_add64(&p.ws.selctr[hb], total) : 0u;
+        __syncthreads();
+        at += s_ctr;
+        for (uint32_t i = tid; i < len; i += kAttendThreads) {
+            const uint32_t key = u.st.keys[i];
+            if ((key >> kLowBits) >= Tb) {
+                if (at < (uint32_t)p.max_ctx) coherent_store(&cand[at], pack_cand(key, c_lo + i));
+                ++at;
+            }
+        }
         __syncthreads();
     };
 
@@ -996,67 +1089,31 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         if (!HYBRID) {
             stream_range(seg_lo, seg_hi, nullptr);
         } else if (retr) {
+            uint32_t* sc = p.ws.score + (size_t)bg * p.max_ctx;
             uint32_t* gh = p.ws.hist + (size_t)bg * kHistBins;
-            unsigned long long* cand = p.ws.cand + (size_t)bg * p.max_ctx;
             for (int i = tid; i < kHistBins; i += kAttendThreads) u.st.hist[i] = 0u;
             for (uint32_t c_lo = seg_lo; c_lo < seg_hi; c_lo += kKeyCap) {
                 const uint32_t c_hi = min(seg_hi, c_lo + (uint32_t)kKeyCap);
+                const uint32_t len = c_hi - c_lo;
                 key_base = c_lo;
                 __syncthreads();
                 stream_range(c_lo, c_hi, nullptr);
                 __syncthreads();
-                // Add this pass's digit counts to the head's histogram, wait for
-                // them to land, and read the histogram back (device-coherent,
-                // coalesced, staged through LDS).  It holds this workgroup's keys
-                // and whatever the others have added so far; counts only grow,
-                // so its crossing T' is a lower bound of the final threshold digit.
+                // every key to the score buffer (read only if the bound below fails)
+                for (uint32_t i = tid; i < len; i += kAttendThreads) coherent_store(&sc[c_lo + i], u.st.keys[i]);
+                // this pass's bound: its own crossing at kSelMargin times its share of k_eff
+                const uint32_t need = (uint32_t)min((unsigned long long)len,
+                                                    ((unsigned long long)kSelMargin * ke * len + (uint32_t)n - 1u) / (uint32_t)n);
+                const uint32_t Tw = local_bound(need);
+                // the pass's counts from its bound up to the head's histogram
+                // (few bins, so few atomics on any one of them)
                 for (int i = tid; i < kHistBins; i += kAttendThreads) {
-                    const uint32_t c = u.st.hist[i];
-                    if (c) {
-                        atomicAdd(&gh[i], c);
-                        u.st.hist[i] = 0u;
-                    }
+                    const uint32_t cnt = u.st.hist[i];
+                    if (cnt && (uint32_t)i >= Tw) atomicAdd(&gh[i], cnt);
                 }
-                wait_stores_complete();
-                __syncthreads();
-                {
-                    uint32_t gv[kHistPerThread];
-#pragma unroll
-                    for (int j = 0; j < kHistPerThread; ++j) gv[j] = coherent_load(&gh[tid + kAttendThreads * j]);
-#pragma unroll
-                    for (int j = 0; j < kHistPerThread; ++j) u.st.gbuf[tid + kAttendThreads * j] = gv[j];
-                }
-                __syncthreads();
-                uint32_t hc[kHistPerThread];
-                {
-                    const uint4* hv = reinterpret_cast<const uint4*>(u.st.gbuf + kHistBins - kHistPerThread * (tid + 1));
-#pragma unroll
-                    for (int c = 0; c < kHistPerThread / 4; ++c) {
-                        const uint4 v4 = hv[c];
-                        hc[kHistPerThread - 1 - 4 * c] = v4.x;
-                        hc[kHistPerThread - 2 - 4 * c] = v4.y;
-                        hc[kHistPerThread - 3 - 4 * c] = v4.z;
-                        hc[kHistPerThread - 4 - 4 * c] = v4.w;
-                    }
-                }
-                block_crossing<kHistPerThread>(hc, kHistBins, ke, s_wave, s_res);
-                const uint32_t Tp = s_res[0];
-                // append this pass's keys with digit >= T'
-                const uint32_t len = c_hi - c_lo;
-                uint32_t mine = 0;
-                for (uint32_t i = tid; i < len; i += kAttendThreads) mine += (u.st.keys[i] >> kLowBits) >= Tp;
-                uint32_t total;
-                uint32_t at = block_exclusive_scan(mine, s_wave, &total);
-                if (tid == 0) s_ctr = total ? counter_add(&p.ws.candcnt[bg], total) : 0u;
-                __syncthreads();
-                at += s_ctr;
-                for (uint32_t i = tid; i < len; i += kAttendThreads) {
-                    const uint32_t key = u.st.keys[i];
-                    if ((key >> kLowBits) >= Tp) {
-                        if (at < (uint32_t)p.max_ctx) coherent_store(&cand[at], pack_cand(key, c_lo + i));
-                        ++at;
-                    }
-                }
+                append_keys(bg, c_lo, c_hi, Tw);
+                if (tid == 0) __hip_atomic_fetch_max(&p.ws.bmax[bg], Tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int i = tid; i < kHistBins; i += kAttendThreads) u.st.hist[i] = 0u;
             }
         } else {
             // sparse head: stage the S entries of the range in LDS (one batched
@@ -1142,7 +1199,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
         }
 
-        // ---- arrival: records to the group merger, candidates to the selector ----
+        // ---- arrival: the record to its group's merger and, for a retrieval
+        // head, this workgroup's candidates to the head's selector; one wait
+        // covers the record, the candidates and the histogram atomics ----
         const int wf = wg_of(h0), wl = wg_of(h1 - 1);
         const int nw = wl - wf + 1;
         const int c = (w - wf) / kCombineFanIn;
@@ -1156,8 +1215,16 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             const int last = (int)(old + 1u == (uint32_t)csize);
             if (last) counter_reset(ctr);
             s_flag[0] = last;
+            s_flag[1] = 0;
+            if (HYBRID && retr) {
+                const unsigned long long o64 = counter_add64(&p.ws.selctr[bg], 1ull << 32);
+                s_flag[1] = (uint32_t)(o64 >> 32) + 1u == (uint32_t)nw;
+                s_res[2] = (uint32_t)o64;                // candidates of the whole head when last
+            }
         }
         __syncthreads();
+        const bool select_last = HYBRID && retr && s_flag[1];
+        const uint32_t C_head = s_res[2];
         if (s_flag[0]) {
             const float* grp = p.ws.rec1 + (size_t)(wf + c * kCombineFanIn + bg) * RS;
             float* out_bg = p.out + ((size_t)b * Hq + (size_t)g * G) * D;
@@ -1179,20 +1246,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 if (s_flag[0]) merge_records<D, G>(p.ws.rec2 + (size_t)bg * kLevel2Max * RS, nc, nullptr, out_bg, u.st.ml);
             }
         }
-
-        // ---- selection arrival (after the record, which the head's output
-        // waits for): the last workgroup of a retrieval head resolves its top-k ----
-        if (HYBRID && retr) {
-            if (tid == 0) {
-                const int nw_h = wl - wf + 1;
-                const uint32_t old_t = counter_add(&p.ws.topkcnt[bg], 1u);
-                const int last_t = (old_t + 1u == (uint32_t)nw_h);
-                if (last_t) counter_reset(&p.ws.topkcnt[bg]);
-                s_flag[1] = last_t;
-            }
-            __syncthreads();
-            if (s_flag[1]) resolve_topk(bg, n, ke);
-        }
+        // the last workgroup of a retrieval head resolves its top-k
+        if (select_last) resolve_topk(bg, n, ke, C_head);
 
         __syncthreads();
     }

@@ -33,6 +33,12 @@ constexpr int kKeyCap = 4096;         // retrieval selection keys kept in LDS pe
 constexpr int kHistBits = 12;                 // first radix digit, histogrammed while streaming
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kCandLds = 4096;                // threshold-digit candidates resolved in LDS
+// A workgroup appends the keys of a pass whose first digit reaches its own
+// crossing at kSelMargin times its proportional share of the budget,
+// need = kSelMargin * k_eff * rows / n.  That is a lower bound of the head's
+// threshold digit unless the pass holds more than that many of the head's
+// top-k_eff keys; the selector checks it and otherwise reads every key.
+constexpr uint32_t kSelMargin = 2;
 
 // Cross-workgroup hand-off without cache-wide maintenance.  Data one
 // workgroup leaves for another inside the same launch is written with
@@ -58,6 +64,12 @@ __device__ __forceinline__ uint32_t counter_add(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void counter_reset(uint32_t* p) {
     __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ unsigned long long counter_add64(unsigned long long* p, unsigned long long v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void counter_reset64(unsigned long long* p) {
+    __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 maps as +0.
 __host__ __device__ inline uint32_t float_key(float f) {
@@ -71,12 +83,15 @@ struct Workspace {
     float* rec1;                 // [(kMaxWG + BH) * RS]      level-1 partial records
     float* rec2;                 // [BH * kLevel2Max * RS]    level-2 partial records
     unsigned long long* cand;    // [BH * max_ctx]            selection candidates (key | index << 32)
+    uint32_t* score;             // [BH * max_ctx]            every selection key of a retrieval head
+                                 //                           (read only when a head's bounds fail)
     // ---- zero-initialised region (restored to zero by every call) ----
     uint32_t* cnt1;              // [BH * kLevel2Max]         level-1 arrival counters
     uint32_t* cnt2;              // [BH]                      level-2 arrival counters
-    uint32_t* candcnt;           // [BH]                      candidates appended
-    uint32_t* topkcnt;           // [BH]                      workgroups done appending
-    uint32_t* hist;              // [BH * kHistBins]          first-digit histogram of selection keys
+    unsigned long long* selctr;  // [BH]                      candidates appended (low 32 bits) |
+                                 //                           workgroups done appending (high 32 bits)
+    uint32_t* bmax;              // [BH]                      largest candidate bound used for the head
+    uint32_t* hist;              // [BH * kHistBins]          first-digit counts from each pass's bound up
     uint32_t* err;               // [4]
     void* zero_begin;
     size_t zero_bytes;
@@ -102,11 +117,12 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_rec1 = take(sizeof(float) * (size_t)(kMaxWG + BH) * RS);
     size_t o_rec2 = take(sizeof(float) * (size_t)BH * kLevel2Max * RS);
     size_t o_cand = take(sizeof(unsigned long long) * (size_t)BH * max_ctx);
+    size_t o_score = take(sizeof(uint32_t) * (size_t)BH * max_ctx);
     size_t z0 = off;
     size_t o_cnt1 = take(sizeof(uint32_t) * (size_t)BH * kLevel2Max);
     size_t o_cnt2 = take(sizeof(uint32_t) * (size_t)BH);
-    size_t o_cc = take(sizeof(uint32_t) * (size_t)BH);
-    size_t o_tc = take(sizeof(uint32_t) * (size_t)BH);
+    size_t o_sc = take(sizeof(unsigned long long) * (size_t)BH);
+    size_t o_bmax = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_hist = take(sizeof(uint32_t) * (size_t)BH * kHistBins);
     size_t o_err = take(sizeof(uint32_t) * 4);
     Workspace w{};
@@ -117,10 +133,11 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.rec1 = (float*)(p + o_rec1);
         w.rec2 = (float*)(p + o_rec2);
         w.cand = (unsigned long long*)(p + o_cand);
+        w.score = (uint32_t*)(p + o_score);
         w.cnt1 = (uint32_t*)(p + o_cnt1);
         w.cnt2 = (uint32_t*)(p + o_cnt2);
-        w.candcnt = (uint32_t*)(p + o_cc);
-        w.topkcnt = (uint32_t*)(p + o_tc);
+        w.selctr = (unsigned long long*)(p + o_sc);
+        w.bmax = (uint32_t*)(p + o_bmax);
         w.hist = (uint32_t*)(p + o_hist);
         w.err = (uint32_t*)(p + o_err);
         w.zero_begin = p + z0;

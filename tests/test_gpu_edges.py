@@ -155,3 +155,28 @@ def test_maximum_context():
 def test_many_sequences():
     w = _w("many_seq", 99, 64, 3, 32, 8, 128, 2000, 32, "bf16", 8, ctx_range=(1, 2000), hh_frac=0.01)
     _chain(w)
+
+
+def test_clustered_top_keys_take_the_full_scan_path():
+    """300 keys far above the rest, packed into the first rows of KV head 0.
+    The workgroup streaming those rows holds ~300 of the head's top 1024 but
+    bounds its candidates at twice its proportional share (tens of keys), so
+    its bound lies above the head's threshold digit and the selector must
+    detect that and re-read every key of the head.  Both heads must still
+    match the oracle."""
+    import torch
+    w = _w("clustered", 90, 1, 1, 8, 2, 64, 65536, 1024, "f32", 0, ctx_list=(65536,))
+    x = synth.layer_inputs(w, 0)
+    qbar = x["q"][0, 0:4, :].astype(np.float64).mean(axis=0)
+    direction = (qbar / np.linalg.norm(qbar)).astype(np.float32)
+    rng = np.random.default_rng(91)
+    x["k"][0, 0, :300, :] = 8.0 * direction + 0.1 * rng.standard_normal((300, 64), dtype=np.float32)
+    role = np.ones(2, np.uint8)
+    handle = make_handle(w)
+    lens = synth.n_ctx(w)
+    n_ctx_dev = torch.from_numpy(lens).cuda()
+    log("[clustered] 300 planted keys in rows 0..299 of head 0, n=65536, k=1024")
+    out, S, _ = run_layer(handle, x, role, None, n_ctx_dev, w.k)
+    compare_layer(out, S, x, role, None, lens, w.k, w.dtype)
+    assert set(range(300)) <= set(S[0, 0].tolist())
+    handle.check_device_errors()
