@@ -462,7 +462,6 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     if (w >= P) return;
 
     auto is_retr = [&](int hb) -> bool { return !HYBRID || ((p.role_bits >> (hb % p.Hkv)) & 1ull); };
-    auto cost_of = [&](int hb) -> uint32_t { return is_retr(hb) ? kCostRetrieval : kCostSparse; };
     auto head_of = [&](uint32_t c) -> int {     // last (b, g) whose cost range starts at or before c
         int cnt = 0;                              // (wave-parallel: the starts are increasing)
         for (int base = 0; base < BH; base += 64) {
@@ -488,19 +487,28 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 const int mid = (a + z + 1) >> 1;
                 if (s_pref[mid] <= raw) a = mid; else z = mid - 1;
             }
-            const uint32_t h0 = s_pref[a], h1 = s_pref[a + 1], c = cost_of(a);
-            bnd = min(h0 + c * ((raw - h0 + c - 1) / c), h1);
+            static_assert(kCostRetrieval == 4 && kCostSparse == 7, "row snapping below uses the costs 4 and 7");
+            const uint32_t h0 = s_pref[a], h1 = s_pref[a + 1], off = raw - h0;
+            const uint32_t up = is_retr(a) ? ((off + 3u) & ~3u) : 7u * ((off + 6u) / 7u);   // next row start
+            bnd = min(h0 + up, h1);
         }
         s_bound[ww] = bnd;
     }
     __syncthreads();
-    auto wg_of = [&](uint32_t cpos) -> int {    // workgroup whose range holds cost position cpos
-        int a = 0, z = P - 1;
-        while (a < z) {
-            const int mid = (a + z + 1) >> 1;
-            if (s_bound[mid] <= cpos) a = mid; else z = mid - 1;
+    // Workgroups whose ranges hold cost positions c0 and c1: the number of
+    // range starts s_bound[1..P-1] at or before each (the starts are
+    // non-decreasing; an empty range shares its start with the next one, so
+    // the count lands on the non-empty range).  Wavefront-parallel.
+    auto wg_pair = [&](uint32_t c0, uint32_t c1, int& w0, int& w1) {
+        int n0 = 0, n1 = 0;
+        for (int base = 1; base < P; base += 64) {
+            const int i = base + lane;
+            const uint32_t v = i < P ? s_bound[i] : 0xFFFFFFFFu;
+            n0 += __popcll(__ballot(v <= c0));
+            n1 += __popcll(__ballot(v <= c1));
         }
-        return a;
+        w0 = n0;
+        w1 = n1;
     };
     const uint32_t lo = s_bound[w], hi = s_bound[w + 1];
 
@@ -1202,7 +1210,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         // ---- arrival: the record to its group's merger and, for a retrieval
         // head, this workgroup's candidates to the head's selector; one wait
         // covers the record, the candidates and the histogram atomics ----
-        const int wf = wg_of(h0), wl = wg_of(h1 - 1);
+        int wf, wl;
+        wg_pair(h0, h1 - 1, wf, wl);
         const int nw = wl - wf + 1;
         const int c = (w - wf) / kCombineFanIn;
         const int nc = (nw + kCombineFanIn - 1) / kCombineFanIn;
