@@ -64,6 +64,43 @@ __device__ __forceinline__ float dpp(float v) {
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+// Lane h of each row of 16, broadcast to the whole row (DPP row_newbcast).
+template <int H>
+__device__ __forceinline__ float row_bcast(float v) {
+    static_assert(H >= 0 && H < 16, "lane within a row");
+    return dpp<0x150 + H>(v);
+}
+
+// row_bcast with the lane given at run time (a constant once the caller's
+// loop over h < G is unrolled, so the switch folds away).
+__device__ __forceinline__ float row_bcast_dyn(float v, int h) {
+    switch (h) {
+        case 0: return row_bcast<0>(v);
+        case 1: return row_bcast<1>(v);
+        case 2: return row_bcast<2>(v);
+        case 3: return row_bcast<3>(v);
+        case 4: return row_bcast<4>(v);
+        case 5: return row_bcast<5>(v);
+        case 6: return row_bcast<6>(v);
+        default: return row_bcast<7>(v);
+    }
+}
+
+// Value of lane ^ 16 / lane ^ 32 through the VALU lane swaps.  With both
+// operands equal to v, permlane16_swap returns (v of lane - 16, v of lane + 16)
+// in (first, second) for the lanes of odd / even rows, and permlane32_swap the
+// same for the upper / lower 32 lanes.
+__device__ __forceinline__ float lane_xor16(float v) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor32(float v) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -193,15 +230,23 @@ __device__ __forceinline__ float safe_scale(float m, float M) {
     return (m == -INFINITY) ? 0.0f : fast_exp2(m - M);
 }
 
+// Reductions over the 64 lanes: rotations by 8, 4, 2, 1 inside each row,
+// then across rows by the lane swaps.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
+    v = fmaxf(v, dpp<kDppRowRor8>(v));
+    v = fmaxf(v, dpp<kDppRowRor4>(v));
+    v = fmaxf(v, dpp<kDppRowRor2>(v));
+    v = fmaxf(v, dpp<kDppRowRor1>(v));
+    v = fmaxf(v, lane_xor16(v));
+    return fmaxf(v, lane_xor32(v));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+    v += dpp<kDppRowRor8>(v);
+    v += dpp<kDppRowRor4>(v);
+    v += dpp<kDppRowRor2>(v);
+    v += dpp<kDppRowRor1>(v);
+    v += lane_xor16(v);
+    return v + lane_xor32(v);
 }
 
 // Records merged by one call: one or two per lane of a wavefront.
@@ -1063,7 +1108,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 l_run *= alpha;
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    const float ah = __shfl(alpha, (lane & 48) | h);
+                    const float ah = row_bcast_dyn(alpha, h);
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) o[h][e] *= ah;
                 }
@@ -1180,20 +1225,20 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         // ---- merge the 4 rows of each wavefront, then the 4 wavefronts ----
         const float lrow = row_sum_same_head<G>(l_run);           // head xl, this row
         float M = m_run;
-        M = fmaxf(M, __shfl_xor(M, 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
+        M = fmaxf(M, lane_xor16(M));
+        M = fmaxf(M, lane_xor32(M));
         const float sc = safe_scale(m_run, M);
         float lw = lrow * sc;
-        lw += __shfl_xor(lw, 16);
-        lw += __shfl_xor(lw, 32);
+        lw += lane_xor16(lw);
+        lw += lane_xor32(lw);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float sch = __shfl(sc, (lane & 48) | h);
+            const float sch = row_bcast_dyn(sc, h);
 #pragma unroll
             for (int e = 0; e < EPL; ++e) {
                 float v = o[h][e] * sch;
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
+                v += lane_xor16(v);
+                v += lane_xor32(v);
                 o[h][e] = v;
             }
         }
