@@ -1177,9 +1177,12 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 __syncthreads();
                 // every key to the score buffer (read only if the bound below fails)
                 for (uint32_t i = tid; i < len; i += kAttendThreads) coherent_store(&sc[c_lo + i], u.st.keys[i]);
-                // this pass's bound: its own crossing at kSelMargin times its share of k_eff
-                const uint32_t need = (uint32_t)min((unsigned long long)len,
-                                                    ((unsigned long long)kSelMargin * ke * len + (uint32_t)n - 1u) / (uint32_t)n);
+                // this pass's bound: its own crossing at its share of k_eff plus a
+                // margin, the smaller of kSelMargin - 1 shares and 5 standard
+                // deviations of a Poisson count with that mean
+                const float share = (float)ke * (float)len / (float)n;
+                const float margin = fminf((float)(kSelMargin - 1u) * share, 5.0f * sqrtf(share) + 2.0f);
+                const uint32_t need = (uint32_t)fminf((float)len, ceilf(share + margin));
                 const uint32_t Tw = local_bound(need);
                 // the pass's counts from its bound up to the head's histogram
                 // (few bins, so few atomics on any one of them)
