@@ -346,9 +346,40 @@ __device__ void merge_records(const float* recs, int count, float* dst, float* o
 
 // ---------------------------------------------------------------- selection helpers
 
-constexpr int kLowBits = 32 - kHistBits;                 // key bits below the first digit
+// First digit of a key: a monotone map of the 32-bit key onto the histogram
+// bins.  Positive logits of magnitude in [2^-12, 2^12), where attention logits
+// live, get one bin per step of their top 7 mantissa bits (128 bins per
+// octave); every other key (negative, zero, tiny or huge logits) falls in a
+// bin of 64 such steps (2 per octave).  The keys of one bin always agree on
+// their top 10 bits, so the low 22 bits and the token index order a bin's
+// keys exactly (the composite below).
+constexpr uint32_t kFineLo = 0x8000u + (127u - 12u) * 128u;      // key >> 16 of +2^-12
+constexpr uint32_t kFineBins = 24u * 128u;                        // up to +2^12
+constexpr int kCoarseShift = 6;
+constexpr uint32_t kFineBase = kFineLo >> kCoarseShift;           // digits below the fine range
+constexpr uint32_t kFineEnd = kFineLo + kFineBins;
+constexpr uint32_t kTopDigit = kFineBase + kFineBins + ((0xFFFFu - kFineEnd) >> kCoarseShift);
+static_assert(kFineLo % (1u << kCoarseShift) == 0 && kFineEnd % (1u << kCoarseShift) == 0,
+              "coarse bins line up with the fine range");
+static_assert(kTopDigit < (uint32_t)kHistBins, "every digit has a bin");
+constexpr int kLowBits = 22;                             // key bits a bin's keys may differ in
 constexpr uint32_t kIdxMask = (1u << kIdxBits) - 1u;
 constexpr int kCompBits = kLowBits + kIdxBits;           // composite: low key bits, then inverted index
+
+__device__ __forceinline__ uint32_t key_digit(uint32_t key) {
+    const uint32_t k16 = key >> 16;
+    const uint32_t lo = k16 >> kCoarseShift;
+    const uint32_t mid = kFineBase + (k16 - kFineLo);
+    const uint32_t hi = kFineBase + kFineBins + ((k16 - kFineEnd) >> kCoarseShift);
+    return k16 < kFineLo ? lo : (k16 < kFineEnd ? mid : hi);
+}
+// Smallest key of digit d (d <= kTopDigit + 1; kTopDigit + 1 maps past every key).
+__device__ __forceinline__ unsigned long long digit_first_key(uint32_t d) {
+    const uint32_t k16 = d < kFineBase ? (d << kCoarseShift)
+                         : d < kFineBase + kFineBins ? kFineLo + (d - kFineBase)
+                                                     : kFineEnd + ((d - kFineBase - kFineBins) << kCoarseShift);
+    return (unsigned long long)k16 << 16;
+}
 constexpr int kWords = kMaxCtx / 32;                     // context bitmap words
 constexpr int kHistPerThread = kHistBins / kAttendThreads;
 constexpr int kCandPerThread = kCandLds / kAttendThreads;
@@ -601,7 +632,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     const uint32_t j = (uint32_t)(vals[e] >> 32) & kIdxMask;
                     const bool valid = tid + (uint32_t)(kAttendThreads * e) < lim;
                     const bool above = valid && key > khi;
-                    const bool eq = valid && ((key - klo) >> kLowBits) == 0u;
+                    const bool eq = valid && key - klo <= khi - klo;
                     atomicOr(&u.se.bits[j >> 5], above ? (1u << (j & 31)) : 0u);
                     eqm |= (unsigned long long)eq << e;
                 }
@@ -680,7 +711,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #pragma unroll
                     for (int e = 0; e < kB; ++e) {
                         const bool valid = base + tid + (uint32_t)(kAttendThreads * e) < cnt;
-                        atomicAdd(&u.se.h12[valid ? ((uint32_t)bv[e] >> kLowBits) : 0u], valid ? 1u : 0u);
+                        atomicAdd(&u.se.h12[valid ? key_digit((uint32_t)bv[e]) : 0u], valid ? 1u : 0u);
                     }
                 }
             };
@@ -720,8 +751,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 T_ = s_res[0];
                 c_above = s_res[1];
             }
-            const uint32_t klo = T_ << kLowBits;
-            const uint32_t khi = klo | ((1u << kLowBits) - 1u);
+            const uint32_t klo = (uint32_t)digit_first_key(T_);              // key range of digit T
+            const uint32_t khi = (uint32_t)(digit_first_key(T_ + 1u) - 1ull);
             uint32_t c_eq = 0;
             if (!fb) classify_batch(cv, nslots, 0u, C, klo, khi, c_eq);
             for (uint32_t base = fb ? 0u : kAttendThreads * RC; base < Cs; base += kAttendThreads * kB) {
@@ -753,7 +784,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                         for (int e = 0; e < kB; ++e) {
                             if (base + tid + (uint32_t)(kAttendThreads * e) >= Cs) continue;
                             const uint32_t key = (uint32_t)bv[e], j = (uint32_t)(bv[e] >> 32);
-                            if ((key >> kLowBits) != T_) continue;
+                            if (key - klo > khi - klo) continue;
                             const unsigned long long cp = composite(key, j);
                             if (shift < kCompBits && (cp >> shift) != prefix) continue;
                             atomicAdd(&u.se.h[comp_digit(cp, nshift, bits)], 1u);
@@ -772,7 +803,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                         for (int e = 0; e < kB; ++e) {
                             if (base + tid + (uint32_t)(kAttendThreads * e) >= Cs) continue;
                             const uint32_t key = (uint32_t)bv[e], j = (uint32_t)(bv[e] >> 32);
-                            if ((key >> kLowBits) != T_) continue;
+                            if (key - klo > khi - klo) continue;
                             const unsigned long long cp = composite(key, j);
                             if (shift < kCompBits && (cp >> shift) != prefix) continue;
                             const uint32_t dg = comp_digit(cp, nshift, bits);
@@ -800,7 +831,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                         for (int e = 0; e < kB; ++e) {
                             const uint32_t key = (uint32_t)bv[e], j = (uint32_t)(bv[e] >> 32);
                             cpv[e] = composite(key, j);
-                            if (base + tid + (uint32_t)(kAttendThreads * e) < Cs && (key >> kLowBits) == T_ &&
+                            if (base + tid + (uint32_t)(kAttendThreads * e) < Cs && key - klo <= khi - klo &&
                                 (cpv[e] >> shift) == prefix)
                                 m |= 1ull << e;
                         }
@@ -827,19 +858,14 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 done = true;
             }
             // radix select in LDS over the remaining composite bits; a group of
-            // at most 64 is finished by direct rank in one wavefront
+            // at most 256 is finished by direct rank, one composite per thread
+            // counted against all of them (wavefront-uniform LDS reads)
             while (!done) {
-                if (c_left <= 64u) {
-                    if (wave == 0) {
-                        const unsigned long long mine = lane < (int)c_left ? u.se.comp[lane] : 0ull;
-                        uint32_t above = 0;
-                        for (uint32_t r = 0; r < c_left; ++r) {
-                            const uint32_t olo = __builtin_amdgcn_readlane((uint32_t)mine, r);
-                            const uint32_t ohi = __builtin_amdgcn_readlane((uint32_t)(mine >> 32), r);
-                            above += ((((unsigned long long)ohi << 32) | olo) > mine);
-                        }
-                        if (lane < (int)c_left && above < r_left) mark(comp_index(mine));
-                    }
+                if (c_left <= (uint32_t)kAttendThreads) {
+                    const unsigned long long mine = u.se.comp[min((uint32_t)tid, c_left - 1u)];
+                    uint32_t above = 0;
+                    for (uint32_t r = 0; r < c_left; ++r) above += u.se.comp[r] > mine;
+                    if ((uint32_t)tid < c_left && above < r_left) mark(comp_index(mine));
                     done = true;
                     break;
                 }
@@ -985,8 +1011,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     auto append_keys = [&](int hb, uint32_t c_lo, uint32_t c_hi, uint32_t Tb) {
         unsigned long long* cand = p.ws.cand + (size_t)hb * p.max_ctx;
         const uint32_t len = c_hi - c_lo;
+        const uint32_t kb = (uint32_t)digit_first_key(Tb);      // Tb <= kTopDigit: a real key
         uint32_t mine = 0;
-        for (uint32_t i = tid; i < len; i += kAttendThreads) mine += (u.st.keys[i] >> kLowBits) >= Tb;
+        for (uint32_t i = tid; i < len; i += kAttendThreads) mine += u.st.keys[i] >= kb;
         uint32_t total;
         uint32_t at = block_exclusive_scan(mine, s_wave, &total);
         if (tid == 0) s_ctr = total ? (uint32_t)counter_add64(&p.ws.selctr[hb], total) : 0u;
@@ -994,12 +1021,28 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         at += s_ctr;
         for (uint32_t i = tid; i < len; i += kAttendThreads) {
             const uint32_t key = u.st.keys[i];
-            if ((key >> kLowBits) >= Tb) {
+            if (key >= kb) {
                 if (at < (uint32_t)p.max_ctx) coherent_store(&cand[at], pack_cand(key, c_lo + i));
                 ++at;
             }
         }
         __syncthreads();
+    };
+
+    // A retrieval head's top-k is resolved by one of its last two arrivals:
+    // the second to last waits (after the rest of its range) for the last
+    // arrival, which still has its record and merges to do, and takes the
+    // resolve if it gets there first.  Each of the two adds its vote to the
+    // head's rclaim word once: 1 = second to last, ready; 2 = second to last,
+    // gave up waiting; 4 = last.  The first ready vote resolves; the second
+    // vote restores the word to zero.
+    int pend_bg = -1;              // head this workgroup is second to last of, voted after the loop
+    uint32_t pend_nw = 0, pend_ke = 0;
+    int pend_n = 0;
+    auto vote = [&](int hb, uint32_t v) -> uint32_t {   // thread 0 only; returns the earlier votes
+        const uint32_t old = counter_add(&p.ws.rclaim[hb], v);
+        if (old != 0u) counter_reset(&p.ws.rclaim[hb]);
+        return old;
     };
 
     for (int bg = head_of(lo); bg < BH && s_pref[bg] < hi; ++bg) {
@@ -1094,7 +1137,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     if (xl == 0 && vmine) {
                         const uint32_t key = float_key(pooled);
                         u.st.keys[(uint32_t)tok_mine - key_base] = key;
-                        atomicAdd(&u.st.hist[key >> kLowBits], 1u);
+                        atomicAdd(&u.st.hist[key_digit(key)], 1u);
                     }
                 }
             }
@@ -1298,12 +1341,13 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             s_flag[1] = 0;
             if (HYBRID && retr) {
                 const unsigned long long o64 = counter_add64(&p.ws.selctr[bg], 1ull << 32);
-                s_flag[1] = (uint32_t)(o64 >> 32) + 1u == (uint32_t)nw;
+                const uint32_t before = (uint32_t)(o64 >> 32);   // arrivals before this one
+                s_flag[1] = before + 1u == (uint32_t)nw ? 1 : (before + 2u == (uint32_t)nw ? 2 : 0);
                 s_res[2] = (uint32_t)o64;                // candidates of the whole head when last
             }
         }
         __syncthreads();
-        const bool select_last = HYBRID && retr && s_flag[1];
+        const int sel_role = (HYBRID && retr) ? s_flag[1] : 0;   // 1 last arrival, 2 second to last
         const uint32_t C_head = s_res[2];
         if (s_flag[0]) {
             const float* grp = p.ws.rec1 + (size_t)(wf + c * kCombineFanIn + bg) * RS;
@@ -1326,10 +1370,48 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 if (s_flag[0]) merge_records<D, G>(p.ws.rec2 + (size_t)bg * kLevel2Max * RS, nc, nullptr, out_bg, u.st.ml);
             }
         }
-        // the last workgroup of a retrieval head resolves its top-k
-        if (select_last) resolve_topk(bg, n, ke, C_head);
+        if (sel_role == 1) {
+            if (tid == 0) {
+                const uint32_t old = nw > 1 ? vote(bg, 4u) : 0u;    // alone: nobody else votes
+                s_flag[0] = old == 0u || old == 2u;
+            }
+            __syncthreads();
+            if (s_flag[0]) resolve_topk(bg, n, ke, C_head);
+        } else if (sel_role == 2) {
+            if (h1 >= hi) {            // the range ends in this head: wait after the loop
+                pend_bg = bg;
+                pend_nw = (uint32_t)nw;
+                pend_n = n;
+                pend_ke = ke;
+            } else if (tid == 0) {
+                vote(bg, 2u);          // more heads to do: leave it to the last arrival
+            }
+        }
 
         __syncthreads();
+    }
+
+    if (HYBRID && pend_bg >= 0) {
+        if (tid == 0) {
+            // wait (bounded) for the last arrival, or for its vote
+            uint32_t ready = 0, C = 0;
+            for (int it = 0; it < kResolveWaitPolls; ++it) {
+                const unsigned long long s = coherent_load(&p.ws.selctr[pend_bg]);
+                const uint32_t votes = coherent_load(&p.ws.rclaim[pend_bg]);
+                if ((uint32_t)(s >> 32) == pend_nw) {
+                    ready = 1;
+                    C = (uint32_t)s;
+                    break;
+                }
+                if (votes != 0u) break;     // the last arrival voted first
+                __builtin_amdgcn_s_sleep(4);
+            }
+            const uint32_t old = vote(pend_bg, ready ? 1u : 2u);
+            s_flag[0] = ready && old == 0u;
+            s_res[2] = C;
+        }
+        __syncthreads();
+        if (s_flag[0]) resolve_topk(pend_bg, pend_n, pend_ke, s_res[2]);
     }
 }
 

@@ -40,6 +40,9 @@ constexpr int kCandLds = 4096;                // threshold-digit candidates reso
 // threshold digit unless the pass holds more than that many of the head's
 // top-k_eff keys; the selector checks it and otherwise reads every key.
 constexpr uint32_t kSelMargin = 2;
+// Polls (about 1 us each) a head's second-to-last arrival spends waiting for
+// the last one before leaving the top-k to it.
+constexpr int kResolveWaitPolls = 64;
 
 // Cross-workgroup hand-off without cache-wide maintenance.  Data one
 // workgroup leaves for another inside the same launch is written with
@@ -92,6 +95,8 @@ struct Workspace {
     unsigned long long* selctr;  // [BH]                      candidates appended (low 32 bits) |
                                  //                           workgroups done appending (high 32 bits)
     uint32_t* bmax;              // [BH]                      largest candidate bound used for the head
+    uint32_t* rclaim;            // [BH]                      votes of a head's last two arrivals on who
+                                 //                           resolves its top-k
     uint32_t* hist;              // [BH * kHistBins]          first-digit counts from each pass's bound up
     uint32_t* err;               // [4]
     void* zero_begin;
@@ -124,6 +129,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_cnt2 = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_sc = take(sizeof(unsigned long long) * (size_t)BH);
     size_t o_bmax = take(sizeof(uint32_t) * (size_t)BH);
+    size_t o_rclaim = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_hist = take(sizeof(uint32_t) * (size_t)BH * kHistBins);
     size_t o_err = take(sizeof(uint32_t) * 4);
     Workspace w{};
@@ -139,6 +145,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.cnt2 = (uint32_t*)(p + o_cnt2);
         w.selctr = (unsigned long long*)(p + o_sc);
         w.bmax = (uint32_t*)(p + o_bmax);
+        w.rclaim = (uint32_t*)(p + o_rclaim);
         w.hist = (uint32_t*)(p + o_hist);
         w.err = (uint32_t*)(p + o_err);
         w.zero_begin = p + z0;
