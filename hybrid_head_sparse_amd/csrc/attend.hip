@@ -506,6 +506,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     __shared__ uint32_t s_res[4];
     __shared__ uint32_t s_ctr;
     __shared__ int s_flag[2];
+    __shared__ uint32_t s_sel[2];     // selection arrival: role, candidates of the head
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -1029,14 +1030,15 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         __syncthreads();
     };
 
-    // A retrieval head's top-k is resolved by one of its last two arrivals:
-    // the second to last waits (after the rest of its range) for the last
-    // arrival, which still has its record and merges to do, and takes the
-    // resolve if it gets there first.  Each of the two adds its vote to the
-    // head's rclaim word once: 1 = second to last, ready; 2 = second to last,
-    // gave up waiting; 4 = last.  The first ready vote resolves; the second
-    // vote restores the word to zero.
-    int pend_bg = -1;              // head this workgroup is second to last of, voted after the loop
+    // A retrieval head's top-k is resolved by its first free selection
+    // arrival (one whose range ends in the head) or by its last arrival: the
+    // waiter polls, once its own work is done, for the last arrival, which
+    // still has its record and merges to do, and takes the resolve if it gets
+    // there first.  Each of the two adds its vote to the head's rclaim word
+    // once: 1 = waiter, ready; 2 = waiter, gave up waiting; 4 = last.  The
+    // first ready vote resolves; the second vote restores the word to zero.
+    // A last arrival with no free arrival before it resolves without a vote.
+    int pend_bg = -1;              // head this workgroup waits for after its range
     uint32_t pend_nw = 0, pend_ke = 0;
     int pend_n = 0;
     auto vote = [&](int hb, uint32_t v) -> uint32_t {   // thread 0 only; returns the earlier votes
@@ -1205,6 +1207,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
         };
 
+        int wf, wl;                    // the head's first and last workgroups
+        wg_pair(h0, h1 - 1, wf, wl);
+        const int nw = wl - wf + 1;
         if (!HYBRID) {
             stream_range(seg_lo, seg_hi, nullptr);
         } else if (retr) {
@@ -1236,6 +1241,25 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 append_keys(bg, c_lo, c_hi, Tw);
                 if (tid == 0) __hip_atomic_fetch_max(&p.ws.bmax[bg], Tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 for (int i = tid; i < kHistBins; i += kAttendThreads) u.st.hist[i] = 0u;
+            }
+            // Selection arrival, before the record: once its stores (candidates,
+            // scores, histogram and bound atomics) complete, this workgroup's
+            // part of the head's selection is in place.  Arrivals whose range
+            // ends in this head also count as free ones.  Roles in resolving
+            // the top-k (below): 1 the last arrival, with a waiter; 3 the last
+            // arrival, with none; 2 the first free arrival that is not last
+            // (the waiter).
+            wait_stores_complete();
+            __syncthreads();
+            if (tid == 0) {
+                const bool ends_here = h1 >= hi;
+                const unsigned long long o64 =
+                    counter_add64(&p.ws.selctr[bg], kSelArrival | (ends_here ? kSelFreeArrival : 0ull));
+                const uint32_t before = (uint32_t)(o64 >> 32) & 0xFFFFu;   // arrivals before this one
+                const uint32_t free_before = (uint32_t)(o64 >> 48);
+                s_sel[0] = before + 1u == (uint32_t)nw ? (free_before ? 1u : 3u)
+                                                       : (ends_here && free_before == 0u ? 2u : 0u);
+                s_sel[1] = (uint32_t)o64;                // candidates of the whole head when last
             }
         } else {
             // sparse head: stage the S entries of the range in LDS (one batched
@@ -1321,12 +1345,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
         }
 
-        // ---- arrival: the record to its group's merger and, for a retrieval
-        // head, this workgroup's candidates to the head's selector; one wait
-        // covers the record, the candidates and the histogram atomics ----
-        int wf, wl;
-        wg_pair(h0, h1 - 1, wf, wl);
-        const int nw = wl - wf + 1;
+        // ---- arrival of the record at its group's merger ----
         const int c = (w - wf) / kCombineFanIn;
         const int nc = (nw + kCombineFanIn - 1) / kCombineFanIn;
         const int csize = min(kCombineFanIn, nw - c * kCombineFanIn);
@@ -1338,17 +1357,10 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             const int last = (int)(old + 1u == (uint32_t)csize);
             if (last) counter_reset(ctr);
             s_flag[0] = last;
-            s_flag[1] = 0;
-            if (HYBRID && retr) {
-                const unsigned long long o64 = counter_add64(&p.ws.selctr[bg], 1ull << 32);
-                const uint32_t before = (uint32_t)(o64 >> 32);   // arrivals before this one
-                s_flag[1] = before + 1u == (uint32_t)nw ? 1 : (before + 2u == (uint32_t)nw ? 2 : 0);
-                s_res[2] = (uint32_t)o64;                // candidates of the whole head when last
-            }
         }
         __syncthreads();
-        const int sel_role = (HYBRID && retr) ? s_flag[1] : 0;   // 1 last arrival, 2 second to last
-        const uint32_t C_head = s_res[2];
+        const uint32_t sel_role = (HYBRID && retr) ? s_sel[0] : 0u;
+        const uint32_t C_head = s_sel[1];
         if (s_flag[0]) {
             const float* grp = p.ws.rec1 + (size_t)(wf + c * kCombineFanIn + bg) * RS;
             float* out_bg = p.out + ((size_t)b * Hq + (size_t)g * G) * D;
@@ -1370,22 +1382,18 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 if (s_flag[0]) merge_records<D, G>(p.ws.rec2 + (size_t)bg * kLevel2Max * RS, nc, nullptr, out_bg, u.st.ml);
             }
         }
-        if (sel_role == 1) {
+        if (sel_role == 1u || sel_role == 3u) {
             if (tid == 0) {
-                const uint32_t old = nw > 1 ? vote(bg, 4u) : 0u;    // alone: nobody else votes
+                const uint32_t old = sel_role == 1u ? vote(bg, 4u) : 0u;
                 s_flag[0] = old == 0u || old == 2u;
             }
             __syncthreads();
             if (s_flag[0]) resolve_topk(bg, n, ke, C_head);
-        } else if (sel_role == 2) {
-            if (h1 >= hi) {            // the range ends in this head: wait after the loop
-                pend_bg = bg;
-                pend_nw = (uint32_t)nw;
-                pend_n = n;
-                pend_ke = ke;
-            } else if (tid == 0) {
-                vote(bg, 2u);          // more heads to do: leave it to the last arrival
-            }
+        } else if (sel_role == 2u) {   // the range ends in this head: wait and vote after the loop
+            pend_bg = bg;
+            pend_nw = (uint32_t)nw;
+            pend_n = n;
+            pend_ke = ke;
         }
 
         __syncthreads();
@@ -1398,7 +1406,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             for (int it = 0; it < kResolveWaitPolls; ++it) {
                 const unsigned long long s = coherent_load(&p.ws.selctr[pend_bg]);
                 const uint32_t votes = coherent_load(&p.ws.rclaim[pend_bg]);
-                if ((uint32_t)(s >> 32) == pend_nw) {
+                if (((uint32_t)(s >> 32) & 0xFFFFu) == pend_nw) {
                     ready = 1;
                     C = (uint32_t)s;
                     break;

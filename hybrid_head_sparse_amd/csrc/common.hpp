@@ -40,9 +40,14 @@ constexpr int kCandLds = 4096;                // threshold-digit candidates reso
 // threshold digit unless the pass holds more than that many of the head's
 // top-k_eff keys; the selector checks it and otherwise reads every key.
 constexpr uint32_t kSelMargin = 2;
-// Polls (about 1 us each) a head's second-to-last arrival spends waiting for
-// the last one before leaving the top-k to it.
+// Polls (about 1 us each) a head's waiting arrival spends on the last one
+// before leaving the top-k to it.
 constexpr int kResolveWaitPolls = 64;
+// Increments of a head's selection counter: candidates in bits 0..31,
+// arrivals in bits 32..47, arrivals whose range ends in the head in 48..63.
+constexpr unsigned long long kSelArrival = 1ull << 32;
+constexpr unsigned long long kSelFreeArrival = 1ull << 48;
+static_assert(kMaxWG < (1 << 16) && kMaxCtx <= (1ll << 32), "selection counter fields");
 
 // Cross-workgroup hand-off without cache-wide maintenance.  Data one
 // workgroup leaves for another inside the same launch is written with
@@ -92,8 +97,9 @@ struct Workspace {
     // ---- zero-initialised region (restored to zero by every call) ----
     uint32_t* cnt1;              // [BH * kLevel2Max]         level-1 arrival counters
     uint32_t* cnt2;              // [BH]                      level-2 arrival counters
-    unsigned long long* selctr;  // [BH]                      candidates appended (low 32 bits) |
-                                 //                           workgroups done appending (high 32 bits)
+    unsigned long long* selctr;  // [BH]                      candidates appended (bits 0..31) |
+                                 //                           workgroups done appending (32..47) |
+                                 //                           those whose range ends in the head (48..63)
     uint32_t* bmax;              // [BH]                      largest candidate bound used for the head
     uint32_t* rclaim;            // [BH]                      votes of a head's last two arrivals on who
                                  //                           resolves its top-k
