@@ -616,8 +616,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     // base + tid + 256 e; slots from nslots on, or past C, hold none): key above
     // the threshold digit's range -> bitmap; inside it -> the composite is
     // appended to u.se.comp after the c_eq already there, ordered by one block
-    // scan.  Branch-free per slot: the bitmap OR and the append always
-    // execute, with a zero operand or this thread's spare slot past kCandLds.
+    // scan.  LDS atomics cost per active lane, so only the lanes whose key is
+    // above issue the bitmap OR.
     auto classify_batch = [&](auto& vals, uint32_t nslots, uint32_t base, uint32_t C, uint32_t klo, uint32_t khi,
                               uint32_t& c_eq) {
         constexpr int NB = (int)(sizeof(vals) / sizeof(vals[0]));
@@ -634,23 +634,24 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     const bool valid = tid + (uint32_t)(kAttendThreads * e) < lim;
                     const bool above = valid && key > khi;
                     const bool eq = valid && key - klo <= khi - klo;
-                    atomicOr(&u.se.bits[j >> 5], above ? (1u << (j & 31)) : 0u);
+                    if (above) atomicOr(&u.se.bits[j >> 5], 1u << (j & 31));
                     eqm |= (unsigned long long)eq << e;
                 }
             }
         }
         uint32_t tot;
         uint32_t pos = c_eq + block_exclusive_scan((uint32_t)__popcll(eqm), s_wave, &tot);
-        if (tot) {
+        if (tot) {      // few keys share the threshold digit: store only theirs
 #pragma unroll
             for (int g8 = 0; g8 < NB; g8 += 8) {
-                if ((uint32_t)g8 < nslots) {
+                if ((uint32_t)g8 < nslots && ((eqm >> g8) & 0xFFull)) {
 #pragma unroll
                     for (int e = g8; e < g8 + 8; ++e) {
-                        const bool is = (eqm >> e) & 1ull;
-                        const uint32_t at = (is && pos < (uint32_t)kCandLds) ? pos : (uint32_t)(kCandLds + tid);
-                        u.se.comp[at] = composite((uint32_t)vals[e], (uint32_t)(vals[e] >> 32) & kIdxMask);
-                        pos += is;
+                        if ((eqm >> e) & 1ull) {
+                            if (pos < (uint32_t)kCandLds)
+                                u.se.comp[pos] = composite((uint32_t)vals[e], (uint32_t)(vals[e] >> 32) & kIdxMask);
+                            ++pos;
+                        }
                     }
                 }
             }
@@ -740,6 +741,14 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // is the head's threshold digit.  Otherwise a pass held more than its
             // margin of the head's top keys: count and use every key instead.
             fb = bmaxv > T_;
+            // the head's histogram and counters are read: restore their zeros
+            // now (the stores complete while the rest runs)
+#pragma unroll
+            for (int j = 0; j < kHistPerThread; ++j) coherent_store(&gh[tid + kAttendThreads * j], 0u);
+            if (tid == 0) {
+                counter_reset64(&p.ws.selctr[hb]);
+                counter_reset(&p.ws.bmax[hb]);
+            }
             uint32_t Cs = C;
             if (fb) {
                 Cs = (uint32_t)n;
@@ -979,11 +988,12 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             for (int i = (int)ke + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
             if (tid == 0 && total != ke) atomicOr(p.ws.err, 2u);
         }
-        // restore the zero invariant of the head's histogram and counters
-        for (int i = tid; i < kHistBins; i += kAttendThreads) gh[i] = 0u;
-        if (tid == 0) {
-            counter_reset64(&p.ws.selctr[hb]);
-            counter_reset(&p.ws.bmax[hb]);
+        if (ke == (uint32_t)n) {       // (the selection path restores these as soon as it has read them)
+            for (int i = tid; i < kHistBins; i += kAttendThreads) gh[i] = 0u;
+            if (tid == 0) {
+                counter_reset64(&p.ws.selctr[hb]);
+                counter_reset(&p.ws.bmax[hb]);
+            }
         }
         __syncthreads();
     };
