@@ -18,7 +18,6 @@ once by the copy and counted as the 4 k_eff read).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -35,7 +34,6 @@ import synth
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attend_llama3_128k_counters.json")
-ATTEND_SRC = os.path.join(ROOT, "hybrid_head_sparse_amd", "csrc", "attend.hip")
 
 
 def algorithmic_bytes(w: synth.Workload, roles: np.ndarray, lens: np.ndarray):
@@ -107,8 +105,8 @@ def counters_traffic():
         return None
     with open(COUNTERS_FILE) as f:
         c = json.load(f)
-    sha = hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()
-    if c.get("attend_source_sha256") != sha:
+    from hybrid_head_sparse_amd.profiling import kernel_code_digest
+    if c.get("kernel_code_sha256") != kernel_code_digest():
         return None
     return c.get("traffic_bytes_per_launch")
 

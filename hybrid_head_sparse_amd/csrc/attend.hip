@@ -20,17 +20,20 @@
 //
 // Selection without a second pass over the scores.  While streaming, every
 // retrieval workgroup keeps the order-preserving 32-bit keys of its pooled
-// logits in LDS and counts their first 12-bit digit.  When its range is done
-// it adds its counts to the head's global histogram, reads the histogram
-// back, and takes the digit T' that holds the k-th largest key among the keys
-// counted so far.  Counts only grow, so T' is a lower bound of the final
-// threshold digit T; the workgroup appends only its keys with digit >= T' to
-// the head's candidate list.  The last workgroup of the head reads the final
-// histogram (T and the count above it), keeps candidates above T, resolves
-// the ones in digit T by radix select on the rest of the key and then the
-// token index (larger key first, lower index first: a strict total order, so
-// the result is exact and unique), marks the winners in an LDS bitmap of the
-// context and writes them in ascending order.
+// logits in LDS and counts their first digit (4096 bins, fine where logits
+// live).  When a pass is done it takes its own bound: the digit where its
+// histogram reaches its share of k plus a margin.  It adds its counts from
+// that bound up to the head's global histogram and appends its keys from the
+// bound up to the head's candidate list.  The resolver reads the final
+// histogram: if no pass's bound exceeds the head's threshold digit T, the
+// histogram is exact from T up and the candidates hold every key from T up
+// (otherwise it re-reads every key).  It keeps the candidates above T,
+// resolves the ones in digit T by the rest of the key and then the token
+// index (larger key first, lower index first: a strict total order, so the
+// result is exact and unique), marks the winners in an LDS bitmap of the
+// context and writes them in ascending order.  The resolve runs on the head's
+// first arrival whose range ends in the head (it waits, bounded, for the last
+// one) or on the last arrival, whichever votes first.
 //
 // CDNA4 mapping of the streaming loop: a key row is spread over 16 lanes (one
 // DPP row), each lane issuing one 8-32 byte load per row; the G query heads of

@@ -21,6 +21,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 
@@ -28,8 +29,24 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 ATTEND_SRC = os.path.join(HERE, "csrc", "attend.hip")
+KERNEL_SOURCES = (ATTEND_SRC, os.path.join(HERE, "csrc", "common.hpp"))
 HYBRID_KERNEL = "attend_kernel<lychee::(anonymous namespace)::BF16, 128, 4, true>"
 DENSE_KERNEL = "attend_kernel<lychee::(anonymous namespace)::BF16, 128, 4, false>"
+
+
+def kernel_code_digest(texts=None) -> str:
+    """sha256 of the kernel's sources (attend.hip, common.hpp) with comments
+    and runs of blank space removed: editing a comment leaves it unchanged,
+    editing code changes it."""
+    if texts is None:
+        texts = [open(f).read() for f in KERNEL_SOURCES]
+    h = hashlib.sha256()
+    for src in texts:
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(re.sub(r"\s+", " ", src).strip().encode())
+        h.update(b"\0")
+    return h.hexdigest()
 
 
 def run_copy(mib: int) -> None:
@@ -85,7 +102,7 @@ def summarize(a) -> None:
     write_b = statistics.mean(write) * 1024.0 * w_scale
     stats = _kernel_stats(a.trace)
     cmds = open(a.commands).read().strip()
-    sha = hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()
+    sha = kernel_code_digest()
     wl = a.workload
 
     rows = []
@@ -108,7 +125,7 @@ def summarize(a) -> None:
     res = {
         "workload": wl,
         "kernel": HYBRID_KERNEL,
-        "attend_source_sha256": sha,
+        "kernel_code_sha256": sha,
         "dispatches": {"fetch": len(fetch), "write": len(write)},
         "fetch_kib_per_dispatch_raw": statistics.mean(fetch),
         "write_kib_per_dispatch_raw": statistics.mean(write),
@@ -129,7 +146,7 @@ def summarize(a) -> None:
                 f"{sum(big(cw)):.0f} KiB written -> scale {f_scale:.4f} (fetch), {w_scale:.4f} (write)\n")
         f.write(f"- traffic per launch: {fetch_b / 1e6:.2f} MB fetched + {write_b / 1e6:.2f} MB written = "
                 f"{(fetch_b + write_b) / 1e6:.2f} MB\n")
-        f.write(f"- attend.hip sha256 at measurement: `{sha}`\n")
+        f.write(f"- kernel code digest at measurement (attend.hip + common.hpp, comments removed): `{sha}`\n")
     print(json.dumps(res, indent=1))
 
 
