@@ -509,7 +509,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     __shared__ uint32_t s_res[4];
     __shared__ uint32_t s_ctr;
     __shared__ int s_flag[2];
-    __shared__ uint32_t s_sel[2];     // selection arrival: role, candidates of the head
+    __shared__ uint32_t s_sel[4];     // selection arrival: role, candidates of the head, slice or helpers, slices taken
+    __shared__ int s_rel;
+    __shared__ uint32_t s_ceq;        // resolver: threshold-digit composites appended so far
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -617,16 +619,17 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 
     // Classify the candidates this thread holds (slot e is candidate
     // base + tid + 256 e; slots from nslots on, or past C, hold none): key above
-    // the threshold digit's range -> bitmap; inside it -> the composite is
-    // appended to u.se.comp after the c_eq already there, ordered by one block
-    // scan.  LDS atomics cost per active lane, so only the lanes whose key is
-    // above issue the bitmap OR.
+    // the threshold digit's range -> the bitmap bit if its index lies in the
+    // slice [rlo, rlo + rlen), else counted in `below` if it lies under the
+    // slice; inside the digit's range -> the composite is appended to u.se.comp
+    // at the position an LDS counter (s_ceq) hands out (the group is ranked by
+    // value, so its order does not matter).  LDS operations cost per active
+    // lane, so only the lanes with something to write issue them.
     auto classify_batch = [&](auto& vals, uint32_t nslots, uint32_t base, uint32_t C, uint32_t klo, uint32_t khi,
-                              uint32_t& c_eq) {
+                              uint32_t rlo, uint32_t rlen, uint32_t& below) {
         constexpr int NB = (int)(sizeof(vals) / sizeof(vals[0]));
         static_assert(NB % 8 == 0 && NB <= 64, "slots come in groups of 8, at most 64");
         const uint32_t lim = C - base;
-        unsigned long long eqm = 0;
 #pragma unroll
         for (int g8 = 0; g8 < NB; g8 += 8) {
             if ((uint32_t)g8 < nslots) {
@@ -637,39 +640,28 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     const bool valid = tid + (uint32_t)(kAttendThreads * e) < lim;
                     const bool above = valid && key > khi;
                     const bool eq = valid && key - klo <= khi - klo;
-                    if (above) atomicOr(&u.se.bits[j >> 5], 1u << (j & 31));
-                    eqm |= (unsigned long long)eq << e;
-                }
-            }
-        }
-        uint32_t tot;
-        uint32_t pos = c_eq + block_exclusive_scan((uint32_t)__popcll(eqm), s_wave, &tot);
-        if (tot) {      // few keys share the threshold digit: store only theirs
-#pragma unroll
-            for (int g8 = 0; g8 < NB; g8 += 8) {
-                if ((uint32_t)g8 < nslots && ((eqm >> g8) & 0xFFull)) {
-#pragma unroll
-                    for (int e = g8; e < g8 + 8; ++e) {
-                        if ((eqm >> e) & 1ull) {
-                            if (pos < (uint32_t)kCandLds)
-                                u.se.comp[pos] = composite((uint32_t)vals[e], (uint32_t)(vals[e] >> 32) & kIdxMask);
-                            ++pos;
-                        }
+                    if (above && j - rlo < rlen) atomicOr(&u.se.bits[(j - rlo) >> 5], 1u << (j & 31));
+                    below += (above && j < rlo) ? 1u : 0u;
+                    if (eq) {
+                        const uint32_t at = atomicAdd(&s_ceq, 1u);
+                        if (at < (uint32_t)kCandLds) u.se.comp[at] = composite(key, j);
                     }
                 }
             }
         }
-        c_eq += tot;
     };
 
-    // Set the bitmap bit of index j.
-    auto mark = [&](uint32_t j) { atomicOr(&u.se.bits[j >> 5], 1u << (j & 31)); };
-
-    // Exact top-k of one retrieval head: the final first-digit histogram gives
-    // the threshold digit T and the count above it; every key with digit >= T
-    // is in the candidate list.  Writes S_out's row and restores the head's
-    // zeroed histogram and candidate count.
-    auto resolve_topk = [&](int hb, int n, uint32_t ke, uint32_t C) {
+    // Exact top-k of one retrieval head, for the slices [j0, j1) of its
+    // context (slice j starts at bitmap word j W / kResolveSlices, rounded
+    // down to 4 words): the final first-digit histogram gives the threshold
+    // digit T and the count above it; every key with digit >= T is in the
+    // candidate list.  Every slice's resolver reads all of them and reaches the
+    // same T and the same winners among the keys of digit T; it marks only the
+    // winners inside its slice in the LDS bitmap, counts those below it (its
+    // first position in S) and writes its part of S_out.  The resolver that
+    // finishes reading the head's histogram and counters last, over all
+    // slices, restores them to zero.
+    auto resolve_topk = [&](int hb, int n, uint32_t ke, uint32_t C, uint32_t j0, uint32_t j1) {
         int32_t* srow = p.S_out + (size_t)hb * p.k;
         const unsigned long long* cand = p.ws.cand + (size_t)hb * p.max_ctx;
         const uint32_t* sc = p.ws.score + (size_t)hb * p.max_ctx;
@@ -679,10 +671,40 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         auto fetch = [&](uint32_t i) -> unsigned long long {
             return fb ? pack_cand(coherent_load(&sc[i]), i) : coherent_load(&cand[i]);
         };
-        const int W = (n + 31) >> 5;
+        const uint32_t Wn = ((uint32_t)n + 31u) >> 5;       // bitmap words of the whole context
+        auto slice_word = [&](uint32_t j) -> uint32_t {
+            return j >= (uint32_t)kResolveSlices ? Wn : ((j * Wn) / (uint32_t)kResolveSlices) & ~3u;
+        };
+        const uint32_t wlo = slice_word(j0), whi = slice_word(j1);
+        const uint32_t rlo = wlo * 32u, rlen = (whi - wlo) * 32u;
+        const int W = (int)(whi - wlo);                      // bitmap words of the slices
+        uint32_t below = 0;                                  // this thread's winners under the slices
+        auto mark = [&](uint32_t j) {                        // winner j
+            if (j - rlo < rlen) atomicOr(&u.se.bits[(j - rlo) >> 5], 1u << (j & 31));
+            below += j < rlo ? 1u : 0u;
+        };
+        // this resolver is done reading the head's histogram and counters
+        auto release_head = [&]() {
+            if (tid == 0) {
+                const uint32_t cnt = j1 - j0;
+                const uint32_t old = counter_add(&p.ws.rdone[hb], cnt);
+                s_rel = old + cnt == (uint32_t)kResolveSlices;
+                if (s_rel) {
+                    counter_reset(&p.ws.rdone[hb]);
+                    counter_reset64(&p.ws.selctr[hb]);
+                    counter_reset(&p.ws.bmax[hb]);
+                }
+            }
+            __syncthreads();
+            if (s_rel)
+                for (int i = tid; i < kHistBins; i += kAttendThreads) coherent_store(&gh[i], 0u);
+        };
         __syncthreads();
         if (ke == (uint32_t)n) {
-            for (int i = tid; i < p.k; i += kAttendThreads) srow[i] = (i < n) ? i : -1;
+            release_head();
+            for (uint32_t i = rlo + tid; i < min(rlo + rlen, (uint32_t)n); i += kAttendThreads) srow[i] = (int32_t)i;
+            if (whi == Wn)
+                for (int i = n + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
         } else {
             constexpr int RC = 64;     // candidate slots per thread in the first load (16384 per head)
             constexpr int kB = 16;     // batch of later candidates
@@ -690,6 +712,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // with the arrival that made this workgroup the last one) and the
             // largest bound used
             C = max(1u, min(C, (uint32_t)p.max_ctx));
+            if (tid == 0) s_ceq = 0u;        // (ordered before the classification by the crossing's barriers)
             const uint32_t nslots = min((C + kAttendThreads - 1) / kAttendThreads, (uint32_t)RC);
             const uint32_t bmaxv = coherent_load(&p.ws.bmax[hb]);
             uint32_t gv[kHistPerThread];
@@ -744,14 +767,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // is the head's threshold digit.  Otherwise a pass held more than its
             // margin of the head's top keys: count and use every key instead.
             fb = bmaxv > T_;
-            // the head's histogram and counters are read: restore their zeros
-            // now (the stores complete while the rest runs)
-#pragma unroll
-            for (int j = 0; j < kHistPerThread; ++j) coherent_store(&gh[tid + kAttendThreads * j], 0u);
-            if (tid == 0) {
-                counter_reset64(&p.ws.selctr[hb]);
-                counter_reset(&p.ws.bmax[hb]);
-            }
+            release_head();
             uint32_t Cs = C;
             if (fb) {
                 Cs = (uint32_t)n;
@@ -766,16 +782,15 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
             const uint32_t klo = (uint32_t)digit_first_key(T_);              // key range of digit T
             const uint32_t khi = (uint32_t)(digit_first_key(T_ + 1u) - 1ull);
-            uint32_t c_eq = 0;
-            if (!fb) classify_batch(cv, nslots, 0u, C, klo, khi, c_eq);
+            if (!fb) classify_batch(cv, nslots, 0u, C, klo, khi, rlo, rlen, below);
             for (uint32_t base = fb ? 0u : kAttendThreads * RC; base < Cs; base += kAttendThreads * kB) {
                 unsigned long long bv[kB];
 #pragma unroll
                 for (int e = 0; e < kB; ++e) bv[e] = fetch(min(base + tid + (uint32_t)(kAttendThreads * e), Cs - 1u));
-                classify_batch(bv, (uint32_t)kB, base, Cs, klo, khi, c_eq);
+                classify_batch(bv, (uint32_t)kB, base, Cs, klo, khi, rlo, rlen, below);
             }
             __syncthreads();
-            uint32_t c_left = c_eq;
+            uint32_t c_left = s_ceq;          // keys of digit T appended
             uint32_t r_left = ke - c_above;
             int shift = kCompBits;
             bool done = (r_left == 0u);
@@ -820,8 +835,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                             const unsigned long long cp = composite(key, j);
                             if (shift < kCompBits && (cp >> shift) != prefix) continue;
                             const uint32_t dg = comp_digit(cp, nshift, bits);
-                            if (dg > Dg || (r_left - gt == keep && dg == Dg))
-                                atomicOr(&u.se.bits[j >> 5], 1u << (j & 31));
+                            if (dg > Dg || (r_left - gt == keep && dg == Dg)) mark(j);
                         }
                     }
                     __syncthreads();
@@ -865,8 +879,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
             if (!done && r_left == c_left) {   // the whole threshold group is selected
                 for (uint32_t i = tid; i < c_left; i += kAttendThreads) {
-                    const uint32_t j = comp_index(u.se.comp[i]);
-                    atomicOr(&u.se.bits[j >> 5], 1u << (j & 31));
+                    mark(comp_index(u.se.comp[i]));
                 }
                 done = true;
             }
@@ -915,8 +928,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 for (int e = 0; e < kCandPerThread; ++e) {
                     if ((uint32_t)e < nsl) {
                         const bool sel = dg[e] != 0xFFFFFFFFu && dg[e] > Dg;
-                        const uint32_t j = comp_index(mine[e]) & kIdxMask;
-                        atomicOr(&u.se.bits[j >> 5], sel ? (1u << (j & 31)) : 0u);
+                        if (sel) mark(comp_index(mine[e]) & kIdxMask);
                         m |= (uint32_t)(dg[e] == Dg) << e;
                     }
                 }
@@ -937,8 +949,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     done = true;
                 } else if (r_left == c_left) {
                     for (uint32_t i = tid; i < c_left; i += kAttendThreads) {
-                        const uint32_t j = comp_index(u.se.comp[i]);
-                        atomicOr(&u.se.bits[j >> 5], 1u << (j & 31));
+                        mark(comp_index(u.se.comp[i]));
                     }
                     done = true;
                 }
@@ -964,9 +975,11 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     cnt += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
                 }
             }
+            uint32_t below_total;
+            (void)block_exclusive_scan(below, s_wave, &below_total);   // winners under the slices
             uint32_t total;
             uint32_t pos = block_exclusive_scan(cnt, s_wave, &total);   // this lane's words come first...
-            pos = __builtin_amdgcn_readfirstlane(pos);                   // ...lane 0's base is the wavefront's
+            pos = below_total + __builtin_amdgcn_readfirstlane(pos);    // ...lane 0's base is the wavefront's
             const uint32_t last = (uint32_t)p.k - 1u;
             for (int i0 = wb; i0 < we; i0 += 256) {
                 const int i = i0 + lane * 4;
@@ -983,19 +996,14 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     while (bw) {
                         const int bit = __ffs(bw) - 1;
                         bw &= bw - 1u;
-                        srow[min(at, last)] = (i + q) * 32 + bit;   // at < ke unless the counts disagree (flagged below)
+                        srow[min(at, last)] = (int32_t)(rlo + (uint32_t)((i + q) * 32 + bit));   // at < ke unless the counts disagree (flagged below)
                         ++at;
                     }
                 }
             }
-            for (int i = (int)ke + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
-            if (tid == 0 && total != ke) atomicOr(p.ws.err, 2u);
-        }
-        if (ke == (uint32_t)n) {       // (the selection path restores these as soon as it has read them)
-            for (int i = tid; i < kHistBins; i += kAttendThreads) gh[i] = 0u;
-            if (tid == 0) {
-                counter_reset64(&p.ws.selctr[hb]);
-                counter_reset(&p.ws.bmax[hb]);
+            if (whi == Wn) {           // the slice holding the end of the context
+                for (int i = (int)ke + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
+                if (tid == 0 && below_total + total != ke) atomicOr(p.ws.err, 2u);
             }
         }
         __syncthreads();
@@ -1043,20 +1051,21 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         __syncthreads();
     };
 
-    // A retrieval head's top-k is resolved by its first free selection
-    // arrival (one whose range ends in the head) or by its last arrival: the
-    // waiter polls, once its own work is done, for the last arrival, which
-    // still has its record and merges to do, and takes the resolve if it gets
-    // there first.  Each of the two adds its vote to the head's rclaim word
-    // once: 1 = waiter, ready; 2 = waiter, gave up waiting; 4 = last.  The
+    // A retrieval head's top-k is resolved in kResolveSlices slices of its
+    // context.  Slice j goes to the head's free selection arrival number j (one
+    // whose range ends in the head), a helper, or to the last arrival: the
+    // helper polls, once its own work is done, for the last arrival, which
+    // still has its record and merges to do, and takes the slice if it gets
+    // there first.  Each of the two adds its vote to the slice's rclaim word
+    // once: 1 = helper, ready; 2 = helper, gave up waiting; 4 = last.  The
     // first ready vote resolves; the second vote restores the word to zero.
-    // A last arrival with no free arrival before it resolves without a vote.
+    // The last arrival takes the slices that have no helper without a vote.
     int pend_bg = -1;              // head this workgroup waits for after its range
-    uint32_t pend_nw = 0, pend_ke = 0;
+    uint32_t pend_nw = 0, pend_ke = 0, pend_slice = 0;
     int pend_n = 0;
-    auto vote = [&](int hb, uint32_t v) -> uint32_t {   // thread 0 only; returns the earlier votes
-        const uint32_t old = counter_add(&p.ws.rclaim[hb], v);
-        if (old != 0u) counter_reset(&p.ws.rclaim[hb]);
+    auto vote = [&](int word, uint32_t v) -> uint32_t {   // one lane; returns the earlier votes
+        const uint32_t old = counter_add(&p.ws.rclaim[word], v);
+        if (old != 0u) counter_reset(&p.ws.rclaim[word]);
         return old;
     };
 
@@ -1259,9 +1268,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // scores, histogram and bound atomics) complete, this workgroup's
             // part of the head's selection is in place.  Arrivals whose range
             // ends in this head also count as free ones.  Roles in resolving
-            // the top-k (below): 1 the last arrival, with a waiter; 3 the last
-            // arrival, with none; 2 the first free arrival that is not last
-            // (the waiter).
+            // the top-k (below): 1 the last arrival (with the number of helpers
+            // before it); 2 one of the first kResolveSlices free arrivals that
+            // is not last, a helper for slice number = free arrivals before it.
             wait_stores_complete();
             __syncthreads();
             if (tid == 0) {
@@ -1270,9 +1279,10 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     counter_add64(&p.ws.selctr[bg], kSelArrival | (ends_here ? kSelFreeArrival : 0ull));
                 const uint32_t before = (uint32_t)(o64 >> 32) & 0xFFFFu;   // arrivals before this one
                 const uint32_t free_before = (uint32_t)(o64 >> 48);
-                s_sel[0] = before + 1u == (uint32_t)nw ? (free_before ? 1u : 3u)
-                                                       : (ends_here && free_before == 0u ? 2u : 0u);
+                const bool last = before + 1u == (uint32_t)nw;
+                s_sel[0] = last ? 1u : (ends_here && free_before < (uint32_t)kResolveSlices ? 2u : 0u);
                 s_sel[1] = (uint32_t)o64;                // candidates of the whole head when last
+                s_sel[2] = last ? min(free_before, (uint32_t)kResolveSlices) : free_before;
             }
         } else {
             // sparse head: stage the S entries of the range in LDS (one batched
@@ -1374,6 +1384,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         __syncthreads();
         const uint32_t sel_role = (HYBRID && retr) ? s_sel[0] : 0u;
         const uint32_t C_head = s_sel[1];
+        const uint32_t sel_aux = s_sel[2];           // helpers before the last arrival, or a helper's slice
         if (s_flag[0]) {
             const float* grp = p.ws.rec1 + (size_t)(wf + c * kCombineFanIn + bg) * RS;
             float* out_bg = p.out + ((size_t)b * Hq + (size_t)g * G) * D;
@@ -1395,18 +1406,34 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 if (s_flag[0]) merge_records<D, G>(p.ws.rec2 + (size_t)bg * kLevel2Max * RS, nc, nullptr, out_bg, u.st.ml);
             }
         }
-        if (sel_role == 1u || sel_role == 3u) {
-            if (tid == 0) {
-                const uint32_t old = sel_role == 1u ? vote(bg, 4u) : 0u;
-                s_flag[0] = old == 0u || old == 2u;
+        if (sel_role == 1u) {
+            // the last arrival votes on each slice that has a helper and takes
+            // the slices with none, or whose helper gave up or is still waiting
+            if (wave == 0) {
+                uint32_t old = 0;
+                if (lane < kResolveSlices && (uint32_t)lane < sel_aux)
+                    old = vote(bg * kResolveSlices + lane, 4u);
+                const unsigned long long take = __ballot(lane < kResolveSlices && (old == 0u || old == 2u));
+                if (lane == 0) s_sel[3] = (uint32_t)take;
             }
             __syncthreads();
-            if (s_flag[0]) resolve_topk(bg, n, ke, C_head);
+            const uint32_t take = s_sel[3];
+            for (uint32_t j0 = 0; j0 < (uint32_t)kResolveSlices;) {     // each run of taken slices at once
+                if (!((take >> j0) & 1u)) {
+                    ++j0;
+                    continue;
+                }
+                uint32_t j1 = j0 + 1u;
+                while (j1 < (uint32_t)kResolveSlices && ((take >> j1) & 1u)) ++j1;
+                resolve_topk(bg, n, ke, C_head, j0, j1);
+                j0 = j1;
+            }
         } else if (sel_role == 2u) {   // the range ends in this head: wait and vote after the loop
             pend_bg = bg;
             pend_nw = (uint32_t)nw;
             pend_n = n;
             pend_ke = ke;
+            pend_slice = sel_aux;
         }
 
         __syncthreads();
@@ -1418,7 +1445,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             uint32_t ready = 0, C = 0;
             for (int it = 0; it < kResolveWaitPolls; ++it) {
                 const unsigned long long s = coherent_load(&p.ws.selctr[pend_bg]);
-                const uint32_t votes = coherent_load(&p.ws.rclaim[pend_bg]);
+                const uint32_t votes = coherent_load(&p.ws.rclaim[pend_bg * kResolveSlices + pend_slice]);
                 if (((uint32_t)(s >> 32) & 0xFFFFu) == pend_nw) {
                     ready = 1;
                     C = (uint32_t)s;
@@ -1427,12 +1454,12 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 if (votes != 0u) break;     // the last arrival voted first
                 __builtin_amdgcn_s_sleep(4);
             }
-            const uint32_t old = vote(pend_bg, ready ? 1u : 2u);
+            const uint32_t old = vote(pend_bg * kResolveSlices + pend_slice, ready ? 1u : 2u);
             s_flag[0] = ready && old == 0u;
             s_res[2] = C;
         }
         __syncthreads();
-        if (s_flag[0]) resolve_topk(pend_bg, pend_n, pend_ke, s_res[2]);
+        if (s_flag[0]) resolve_topk(pend_bg, pend_n, pend_ke, s_res[2], pend_slice, pend_slice + 1u);
     }
 }
 

@@ -40,9 +40,12 @@ constexpr int kCandLds = 4096;                // threshold-digit candidates reso
 // threshold digit unless the pass holds more than that many of the head's
 // top-k_eff keys; the selector checks it and otherwise reads every key.
 constexpr uint32_t kSelMargin = 2;
-// Polls (about 1 us each) a head's waiting arrival spends on the last one
-// before leaving the top-k to it.
+// Polls (about 1 us each) a helper spends waiting for the head's last arrival
+// before leaving its slice of the top-k to it.
 constexpr int kResolveWaitPolls = 64;
+// Slices of a retrieval head's context whose top-k winners are resolved by
+// separate workgroups (each reads every candidate, marks and writes its slice).
+constexpr int kResolveSlices = 8;
 // Increments of a head's selection counter: candidates in bits 0..31,
 // arrivals in bits 32..47, arrivals whose range ends in the head in 48..63.
 constexpr unsigned long long kSelArrival = 1ull << 32;
@@ -101,8 +104,10 @@ struct Workspace {
                                  //                           workgroups done appending (32..47) |
                                  //                           those whose range ends in the head (48..63)
     uint32_t* bmax;              // [BH]                      largest candidate bound used for the head
-    uint32_t* rclaim;            // [BH]                      votes of a head's last two arrivals on who
-                                 //                           resolves its top-k
+    uint32_t* rclaim;            // [BH * kResolveSlices]     votes of a helper and the last arrival on
+                                 //                           who resolves a slice of a head's top-k
+    uint32_t* rdone;             // [BH]                      slices whose resolver has read the head's
+                                 //                           histogram and counters
     uint32_t* hist;              // [BH * kHistBins]          first-digit counts from each pass's bound up
     uint32_t* err;               // [4]
     void* zero_begin;
@@ -135,7 +140,8 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_cnt2 = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_sc = take(sizeof(unsigned long long) * (size_t)BH);
     size_t o_bmax = take(sizeof(uint32_t) * (size_t)BH);
-    size_t o_rclaim = take(sizeof(uint32_t) * (size_t)BH);
+    size_t o_rclaim = take(sizeof(uint32_t) * (size_t)BH * kResolveSlices);
+    size_t o_rdone = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_hist = take(sizeof(uint32_t) * (size_t)BH * kHistBins);
     size_t o_err = take(sizeof(uint32_t) * 4);
     Workspace w{};
@@ -152,6 +158,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.selctr = (unsigned long long*)(p + o_sc);
         w.bmax = (uint32_t*)(p + o_bmax);
         w.rclaim = (uint32_t*)(p + o_rclaim);
+        w.rdone = (uint32_t*)(p + o_rdone);
         w.hist = (uint32_t*)(p + o_hist);
         w.err = (uint32_t*)(p + o_err);
         w.zero_begin = p + z0;
