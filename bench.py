@@ -234,6 +234,7 @@ def main():
     l0_achieved = hyb_bytes[0] / (l0_ms * 1e-3) / 1e9
 
     dense_res = None
+    dense_l0 = None
     if not args.no_dense:
         dense_step()
         torch.cuda.synchronize()
@@ -243,6 +244,24 @@ def main():
                      "p90_us": dense_per[(9 * len(dense_per)) // 10] * 1e3,
                      "algorithmic_bytes": sum(dense_bytes),
                      "achieved_GBps": sum(dense_bytes) / (dense_ms * 1e-3) / 1e9}
+        # the same kernel without selection on layer 0's inputs (HIP events on the handle's stream)
+        d0_ms = []
+        d0_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a_, b_ in d0_ev:
+            a_.record()
+            b_.record()
+        torch.cuda.synchronize()
+        for a_, b_ in d0_ev:
+            h.set_profile_events(a_, b_)
+            x = dev[0]
+            h.dense_decode_layer(x["q"], x["k"], x["v"], dense_outs[0], n_ctx)
+        h.set_profile_events(None, None)
+        torch.cuda.synchronize()
+        d0_ms = statistics.mean(a_.elapsed_time(b_) for a_, b_ in d0_ev)
+        dense_l0 = {"kernel": "attend_kernel (dense: the retrieval path without selection), layer 0 inputs",
+                    "achieved": dense_bytes[0] / (d0_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": dense_bytes[0] / (d0_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "bytes_per_launch": dense_bytes[0],
+                    "avg_launch_us": d0_ms * 1e3}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -283,6 +302,7 @@ def main():
                                          "achieved": l0_achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                          "frac": l0_achieved / HBM_PEAK_GBPS, "bytes_per_launch": hyb_bytes[0],
                                          "avg_launch_us": l0_ms * 1e3},
+        "roofline_all_retrieval_layer_without_selection": dense_l0,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

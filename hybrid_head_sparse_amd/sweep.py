@@ -1,0 +1,178 @@
+"""Kernel sweep in the shape of the pages' kernel-latency figure (one GPU).
+
+The LycheeDecode paper's kernel figure (Section 4.4 and Fig. 5 of the paper
+page) times the hybrid-head kernel against the sparse-head ratio (4/8, 6/8,
+7/8, 8/8 of the heads sparse), the batch (1-8) and the context (16K-128K) at
+90% sparsity.  This sweep times the built kernel over the same grid on the
+Llama3-8B attention shape (32 query heads over 8 KV heads, d = 128, bf16 KV
+cache) with a budget of k = n / 10 tokens (the 90% sparsity, at token rather
+than 64-token-block granularity):
+
+  * every point builds two layers of seeded normal inputs on the device
+    (q, K ~ N(0,1)/sqrt(d), V ~ N(0,1); torch's generator, seed per point);
+  * layer 0 is all retrieval and produces S; the measured layer has its first
+    round(ratio * 8) KV heads sparse (they attend to layer 0's S) and the
+    rest retrieval;
+  * the measured layer and the dense all-heads kernel on the same inputs are
+    each captured --reps times back to back in a HIP graph, whose replay is
+    timed with events (so a launch's time includes the gap to the next one,
+    as in a model's step, and no host time);
+  * the pages' qualitative claims are checked between the ends of each axis:
+    the layer's time grows from the smallest to the largest batch and
+    context, and falls from the fewest to the most sparse heads.
+
+    python3 -m hybrid_head_sparse_amd.sweep [--batches 1 2 4 8] [--ctx 16384 ...]
+        [--ratios 4 6 7 8] [--reps 10] [--out profiles/sweep_fig5_shape.md]
+"""
+from __future__ import annotations
+
+import argparse
+import math
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+HQ, HKV, D = 32, 8, 128
+HBM_PEAK_GBPS = 8000.0
+
+
+def budget(n: int) -> int:
+    """k at 90% sparsity."""
+    return max(1, int(round(n / 10)))
+
+
+def layer_bytes(B: int, n: int, k: int, n_sparse: int) -> tuple[int, int]:
+    """Algorithmic HBM bytes of the measured hybrid layer and of the dense layer."""
+    s = 2
+    qo = B * HQ * D * (s + 4)
+    ke = min(k, n)
+    hyb = qo + B * ((HKV - n_sparse) * (2 * n * D * s + 4 * ke) + n_sparse * (2 * ke * D * s + 4 * ke))
+    dense = qo + B * HKV * 2 * n * D * s
+    return hyb, dense
+
+
+def run_point(hhs, torch, B: int, n: int, n_sparse: int, reps: int, seed: int) -> dict:
+    k = budget(n)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    inv = 1.0 / math.sqrt(D)
+
+    def layer():
+        q = (torch.randn(B, HQ, D, generator=gen, device="cuda") * inv).to(torch.bfloat16)
+        kc = (torch.randn(B, HKV, n, D, generator=gen, device="cuda") * inv).to(torch.bfloat16)
+        vc = torch.randn(B, HKV, n, D, generator=gen, device="cuda").to(torch.bfloat16)
+        return q, kc, vc
+
+    x0, x1 = layer(), layer()
+    h = hhs.Handle(B, HQ, HKV, D, n, k, "bf16")
+    n_ctx = torch.full((B,), n, dtype=torch.int32, device="cuda")
+    S0 = torch.empty((B, HKV, k), dtype=torch.int32, device="cuda")
+    S1 = torch.empty_like(S0)
+    out = torch.empty((B, HQ, D), dtype=torch.float32, device="cuda")
+    role0 = [1] * HKV
+    role1 = [0] * n_sparse + [1] * (HKV - n_sparse)
+    h.decode_layer(*x0, role0, None, S0, out, n_ctx, k)
+
+    def timed(fn):
+        fn()                                       # warm
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            h.set_stream(torch.cuda.current_stream())
+            for _ in range(reps):
+                fn()
+        h.set_stream(torch.cuda.current_stream())
+        g.replay()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b) / reps * 1e3)
+        return statistics.median(t)
+
+    def hybrid():
+        h.decode_layer(*x1, role1, S0, S1, out, n_ctx, k)
+
+    def dense():
+        h.dense_decode_layer(*x1, out, n_ctx)
+
+    us = timed(hybrid)
+    dus = timed(dense)
+    h.check_device_errors()
+    hb, db = layer_bytes(B, n, k, n_sparse)
+    del x0, x1, h
+    torch.cuda.empty_cache()
+    return {"batch": B, "n": n, "k": k, "sparse": n_sparse, "us": us, "dense_us": dus,
+            "gbps": hb / (us * 1e-6) / 1e9, "dense_gbps": db / (dus * 1e-6) / 1e9, "speedup": dus / us}
+
+
+def checks(rows: list[dict]) -> list[tuple[str, bool]]:
+    """The pages' qualitative claims over the measured grid."""
+    by = {(r["sparse"], r["batch"], r["n"]): r["us"] for r in rows}
+    sparse = sorted({r["sparse"] for r in rows})
+    batches = sorted({r["batch"] for r in rows})
+    ctxs = sorted({r["n"] for r in rows})
+    res = []
+    lo, hi = ctxs[0], ctxs[-1]
+    res.append((f"time grows from n = {lo} to n = {hi} at every ratio and batch",
+                all(by[(s, b, lo)] < by[(s, b, hi)] for s in sparse for b in batches)))
+    lo, hi = batches[0], batches[-1]
+    res.append((f"time grows from batch {lo} to batch {hi} at every ratio and context",
+                all(by[(s, lo, n)] < by[(s, hi, n)] for s in sparse for n in ctxs)))
+    lo, hi = sparse[0], sparse[-1]
+    res.append((f"time falls from {lo}/8 to {hi}/8 sparse heads at every batch and context",
+                all(by[(lo, b, n)] > by[(hi, b, n)] for b in batches for n in ctxs)))
+    return res
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--batches", type=int, nargs="+", default=[1, 2, 4, 8])
+    ap.add_argument("--ctx", type=int, nargs="+", default=[16384, 32768, 65536, 131072])
+    ap.add_argument("--ratios", type=int, nargs="+", default=[4, 6, 7, 8], help="sparse KV heads out of 8")
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=7)
+    ap.add_argument("--out", default=os.path.join(ROOT, "profiles", "sweep_fig5_shape.md"))
+    a = ap.parse_args(argv)
+    sys.path.insert(0, ROOT)
+    import torch
+    import hybrid_head_sparse_amd as hhs
+    rows = []
+    for si, s in enumerate(a.ratios):
+        for bi, B in enumerate(a.batches):
+            for ni, n in enumerate(a.ctx):
+                r = run_point(hhs, torch, B, n, s, a.reps, a.seed * 1000 + si * 100 + bi * 10 + ni)
+                rows.append(r)
+                print(f"[sweep] sparse {s}/8 batch {B} n {n} k {r['k']}: {r['us']:.1f} us "
+                      f"({r['gbps']:.0f} GB/s), dense {r['dense_us']:.1f} us, {r['speedup']:.2f}x", flush=True)
+    res = checks(rows)
+    cmd = "python3 -m hybrid_head_sparse_amd.sweep " + " ".join(argv if argv is not None else sys.argv[1:])
+    with open(a.out, "w") as f:
+        f.write("# Hybrid-layer kernel sweep, the shape of the pages' kernel-latency figure\n\n")
+        f.write(f"Command (repository root, one MI355X): `{cmd.strip()}`\n\n")
+        f.write("Llama3-8B attention shape (32 query / 8 KV heads, d = 128, bf16 KV), k = n/10 (90% sparsity, "
+                "token granularity), one measured layer after an all-retrieval layer 0; a HIP graph of "
+                f"{a.reps} back-to-back launches, replay timed with events (median of 3 replays), so each "
+                "launch's time includes the gap to the next.  GB/s are algorithmic bytes per launch over "
+                "that time.\n\n")
+        f.write("| sparse heads | batch | n | k | hybrid us | GB/s | dense us | dense GB/s | speedup |\n")
+        f.write("|---|---|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| {r['sparse']}/8 | {r['batch']} | {r['n']} | {r['k']} | {r['us']:.1f} | {r['gbps']:.0f} | "
+                    f"{r['dense_us']:.1f} | {r['dense_gbps']:.0f} | {r['speedup']:.2f}x |\n")
+        f.write("\nChecks (the pages' qualitative claims):\n\n")
+        for name, ok in res:
+            f.write(f"- {'PASS' if ok else 'FAIL'}: {name}\n")
+    for name, ok in res:
+        print(f"[sweep] {'PASS' if ok else 'FAIL'}: {name}", flush=True)
+    return 0 if all(ok for _, ok in res) else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
