@@ -1238,8 +1238,11 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             uint32_t* sc = p.ws.score + (size_t)bg * p.max_ctx;
             uint32_t* gh = p.ws.hist + (size_t)bg * kHistBins;
             for (int i = tid; i < kHistBins; i += kAttendThreads) u.st.hist[i] = 0u;
-            for (uint32_t c_lo = seg_lo; c_lo < seg_hi; c_lo += kKeyCap) {
-                const uint32_t c_hi = min(seg_hi, c_lo + (uint32_t)kKeyCap);
+            // equal passes of at most kKeyCap rows (no short tail pass)
+            const uint32_t npass = (seg_hi - seg_lo + kKeyCap - 1) / kKeyCap;
+            const uint32_t plen = npass ? (seg_hi - seg_lo + npass - 1) / npass : 1u;
+            for (uint32_t c_lo = seg_lo; c_lo < seg_hi; c_lo += plen) {
+                const uint32_t c_hi = min(seg_hi, c_lo + plen);
                 const uint32_t len = c_hi - c_lo;
                 key_base = c_lo;
                 __syncthreads();
@@ -1247,12 +1250,15 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 __syncthreads();
                 // every key to the score buffer (read only if the bound below fails)
                 for (uint32_t i = tid; i < len; i += kAttendThreads) coherent_store(&sc[c_lo + i], u.st.keys[i]);
-                // this pass's bound: its own crossing at its share of k_eff plus a
-                // margin, the smaller of kSelMargin - 1 shares and 5 standard
-                // deviations of a Poisson count with that mean
+                // this pass's bound: its own crossing at its share s of k_eff plus
+                // a margin, the smaller of kSelMargin - 1 shares and 5 standard
+                // deviations of a Poisson count with mean s (plus 2), but never
+                // under 4 deviations plus 4 (a pass of a few rows keeps them all)
                 const float share = (float)ke * (float)len / (float)n;
-                const float margin = fminf((float)(kSelMargin - 1u) * share, 5.0f * sqrtf(share) + 2.0f);
-                const uint32_t need = (uint32_t)fminf((float)len, ceilf(share + margin));
+                const float rs = sqrtf(share);
+                const float margin = fmaxf(fminf((float)(kSelMargin - 1u) * share, 5.0f * rs + 2.0f), 4.0f * rs + 4.0f);
+                // (a need beyond the pass's rows gives bound 0: every key kept)
+                const uint32_t need = (uint32_t)fminf((float)len + 1.0f, ceilf(share + margin));
                 const uint32_t Tw = local_bound(need);
                 // the pass's counts from its bound up to the head's histogram
                 // (few bins, so few atomics on any one of them)

@@ -34,9 +34,10 @@ constexpr int kHistBits = 12;                 // first radix digit, histogrammed
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kCandLds = 4096;                // threshold-digit candidates resolved in LDS
 // A workgroup appends the keys of a pass whose first digit reaches its own
-// crossing at its proportional share of the budget, k_eff * rows / n, plus
-// a margin (at most kSelMargin - 1 shares, at most 5 Poisson standard
-// deviations of the share plus 2).  That is a lower bound of the head's
+// crossing at its proportional share s of the budget, k_eff * rows / n, plus
+// a margin: the smaller of kSelMargin - 1 shares and 5 Poisson standard
+// deviations of s plus 2, raised to at least 4 deviations plus 4 (for passes
+// of a few rows, whose share is tiny).  That is a lower bound of the head's
 // threshold digit unless the pass holds more than that many of the head's
 // top-k_eff keys; the selector checks it and otherwise reads every key.
 constexpr uint32_t kSelMargin = 2;

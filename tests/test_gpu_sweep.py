@@ -47,6 +47,14 @@ def test_large_budget_all_retrieval():
     _two_layers(w, None)
 
 
+def test_multi_pass_ranges_at_ninety_percent_sparsity():
+    # 2 x 8 heads of 128K rows over the grid: every workgroup streams its part
+    # of a retrieval head in several passes, and the ranges split heads at
+    # arbitrary rows (short boundary passes)
+    w = synth.Workload("sweep_b2_128k", 23, 2, 2, 32, 8, 128, 131072, 13107, "bf16", 4, hh_frac=0.01)
+    _two_layers(w, np.array([0, 0, 0, 0, 1, 1, 1, 1], np.uint8))
+
+
 def test_sweep_trends_on_a_reduced_grid():
     import torch
     import hybrid_head_sparse_amd as hhs
