@@ -433,8 +433,9 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t*
 // Crossing of a histogram spread over the block, PER bins per thread held in
 // `cnt` (thread t holds the bins of descending rank t*PER .. t*PER+PER-1, i.e.
 // bin nbins-1-rank): finds D with (count above D) < need <= (count >= D).
-// Result in s_res[0] (digit), s_res[1] (count above D); if the whole
-// histogram holds fewer than `need`, D = 0 and the count above it is returned.
+// Result in s_res[0] (digit), s_res[1] (count above D), s_res[3] (count at
+// or above D); if the whole histogram holds fewer than `need`, D = 0 and the
+// counts above it and in all are returned.
 template <int PER>
 __device__ void block_crossing(const uint32_t (&cnt)[PER], int nbins, uint32_t need, uint32_t* s_wave,
                                uint32_t* s_res) {
@@ -452,6 +453,7 @@ __device__ void block_crossing(const uint32_t (&cnt)[PER], int nbins, uint32_t n
             if (r0 + i == nbins - 1) {
                 s_res[0] = 0u;
                 s_res[1] = tot - cnt[i];
+                s_res[3] = tot;
             }
         }
     } else if (before < need && need <= before + sum) {
@@ -462,6 +464,7 @@ __device__ void block_crossing(const uint32_t (&cnt)[PER], int nbins, uint32_t n
             if (!found && acc + cnt[i] >= need) {
                 s_res[0] = (uint32_t)(nbins - 1 - (r0 + i));
                 s_res[1] = acc;
+                s_res[3] = acc + cnt[i];
                 found = true;
             }
             acc += cnt[i];
@@ -479,7 +482,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 
     struct StreamLds {
         uint32_t hist[HYBRID ? kHistBins : 1];
-        uint32_t gbuf[HYBRID ? kHistBins : 1];      // the head's global histogram as read back
+        uint32_t gbuf[HYBRID ? kKeyCap : 1];        // a pass's kept positions, staged for the append
         uint32_t keys[HYBRID ? kKeyCap : 1];
         int32_t idx[HYBRID ? kIdxChunk : 1];
         float pw[kWaves][4][16];
@@ -508,6 +511,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     __shared__ uint32_t s_wave[kWaves];
     __shared__ uint32_t s_res[4];
     __shared__ uint32_t s_ctr;
+    __shared__ uint32_t s_lcnt;       // a pass's kept keys staged so far
     __shared__ int s_flag[2];
     __shared__ uint32_t s_sel[4];     // selection arrival: role, candidates of the head, slice or helpers, slices taken
     __shared__ int s_rel;
@@ -1009,48 +1013,6 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         __syncthreads();
     };
 
-    // Crossing of this workgroup's first-digit histogram of the current pass
-    // (u.st.hist) at `need`: the largest digit D with at least `need` keys of
-    // the pass at or above it (0 if the pass has fewer).
-    auto local_bound = [&](uint32_t need) -> uint32_t {
-        uint32_t hc[kHistPerThread];
-        const uint4* hv = reinterpret_cast<const uint4*>(u.st.hist + kHistBins - kHistPerThread * (tid + 1));
-#pragma unroll
-        for (int c = 0; c < kHistPerThread / 4; ++c) {
-            const uint4 v4 = hv[c];
-            hc[kHistPerThread - 1 - 4 * c] = v4.x;
-            hc[kHistPerThread - 2 - 4 * c] = v4.y;
-            hc[kHistPerThread - 3 - 4 * c] = v4.z;
-            hc[kHistPerThread - 4 - 4 * c] = v4.w;
-        }
-        block_crossing<kHistPerThread>(hc, kHistBins, need, s_wave, s_res);
-        return s_res[0];
-    };
-
-    // Append the keys of positions [c_lo, c_hi) held in u.st.keys whose first
-    // digit is >= Tb to head hb's candidate list (one block scan orders them,
-    // one atomic reserves the range; device-coherent stores).
-    auto append_keys = [&](int hb, uint32_t c_lo, uint32_t c_hi, uint32_t Tb) {
-        unsigned long long* cand = p.ws.cand + (size_t)hb * p.max_ctx;
-        const uint32_t len = c_hi - c_lo;
-        const uint32_t kb = (uint32_t)digit_first_key(Tb);      // Tb <= kTopDigit: a real key
-        uint32_t mine = 0;
-        for (uint32_t i = tid; i < len; i += kAttendThreads) mine += u.st.keys[i] >= kb;
-        uint32_t total;
-        uint32_t at = block_exclusive_scan(mine, s_wave, &total);
-        if (tid == 0) s_ctr = total ? (uint32_t)counter_add64(&p.ws.selctr[hb], total) : 0u;
-        __syncthreads();
-        at += s_ctr;
-        for (uint32_t i = tid; i < len; i += kAttendThreads) {
-            const uint32_t key = u.st.keys[i];
-            if (key >= kb) {
-                if (at < (uint32_t)p.max_ctx) coherent_store(&cand[at], pack_cand(key, c_lo + i));
-                ++at;
-            }
-        }
-        __syncthreads();
-    };
-
     // A retrieval head's top-k is resolved in kResolveSlices slices of its
     // context.  Slice j goes to the head's free selection arrival number j (one
     // whose range ends in the head), a helper, or to the last arrival: the
@@ -1259,16 +1221,64 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 const float margin = fmaxf(fminf((float)(kSelMargin - 1u) * share, 5.0f * rs + 2.0f), 4.0f * rs + 4.0f);
                 // (a need beyond the pass's rows gives bound 0: every key kept)
                 const uint32_t need = (uint32_t)fminf((float)len + 1.0f, ceilf(share + margin));
-                const uint32_t Tw = local_bound(need);
-                // the pass's counts from its bound up to the head's histogram
-                // (few bins, so few atomics on any one of them)
-                for (int i = tid; i < kHistBins; i += kAttendThreads) {
-                    const uint32_t cnt = u.st.hist[i];
-                    if (cnt && (uint32_t)i >= Tw) atomicAdd(&gh[i], cnt);
+                // the pass's bound Tw: the crossing of its histogram at `need`
+                // (thread t holds bins 4095 - 16t down to 4080 - 16t)
+                uint32_t hc[kHistPerThread];
+                {
+                    uint4* hv = reinterpret_cast<uint4*>(u.st.hist + kHistBins - kHistPerThread * (tid + 1));
+#pragma unroll
+                    for (int c = 0; c < kHistPerThread / 4; ++c) {
+                        const uint4 v4 = hv[c];
+                        hc[kHistPerThread - 1 - 4 * c] = v4.x;
+                        hc[kHistPerThread - 2 - 4 * c] = v4.y;
+                        hc[kHistPerThread - 3 - 4 * c] = v4.z;
+                        hc[kHistPerThread - 4 - 4 * c] = v4.w;
+                    }
                 }
-                append_keys(bg, c_lo, c_hi, Tw);
-                if (tid == 0) __hip_atomic_fetch_max(&p.ws.bmax[bg], Tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                for (int i = tid; i < kHistBins; i += kAttendThreads) u.st.hist[i] = 0u;
+                if (tid == 0) s_lcnt = 0u;
+                block_crossing<kHistPerThread>(hc, kHistBins, need, s_wave, s_res);
+                const uint32_t Tw = s_res[0];
+                const uint32_t nkeep = s_res[3];                      // keys with digit >= Tw
+                // wavefront 0: the pass's bound to the head's bound word and a
+                // range of the candidate list for its keys from Tw up (it waits
+                // for that reply alone); wavefronts 1-3: the pass's counts from Tw
+                // up to the head's histogram (few bins, so few atomics on any one
+                // of them; other workgroups add to the same bins), then zeros
+                if (wave == 0) {
+                    if (tid == 0) {
+                        __hip_atomic_fetch_max(&p.ws.bmax[bg], Tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        s_ctr = nkeep ? (uint32_t)counter_add64(&p.ws.selctr[bg], nkeep) : 0u;
+                    }
+                } else {
+                    for (int i = tid - 64; i < kHistBins; i += kAttendThreads - 64) {
+                        const uint32_t cnt = u.st.hist[i];
+                        if (cnt && (uint32_t)i >= Tw) atomicAdd(&gh[i], cnt);
+                        u.st.hist[i] = 0u;                           // the next pass starts from zero
+                    }
+                }
+                // while the reservation travels: the kept positions to LDS (any
+                // order: the selector's result does not depend on it) ...
+                {
+                    const uint32_t kb = (uint32_t)digit_first_key(Tw);  // Tw <= kTopDigit: a real key
+                    for (uint32_t i = tid; i < len; i += kAttendThreads) {
+                        if (u.st.keys[i] >= kb) {
+                            const uint32_t at = atomicAdd(&s_lcnt, 1u);
+                            if (at < (uint32_t)kKeyCap) u.st.gbuf[at] = i;
+                        }
+                    }
+                }
+                __syncthreads();
+                // ... then out with consecutive device-coherent stores
+                {
+                    unsigned long long* cand = p.ws.cand + (size_t)bg * p.max_ctx;
+                    const uint32_t base = s_ctr, cnt = min(nkeep, (uint32_t)kKeyCap);
+                    for (uint32_t j = tid; j < cnt; j += kAttendThreads) {
+                        const uint32_t off = u.st.gbuf[j];
+                        if (base + j < (uint32_t)p.max_ctx)
+                            coherent_store(&cand[base + j], pack_cand(u.st.keys[off], c_lo + off));
+                    }
+                }
+                __syncthreads();
             }
             // Selection arrival, before the record: once its stores (candidates,
             // scores, histogram and bound atomics) complete, this workgroup's
