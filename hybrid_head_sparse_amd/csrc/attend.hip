@@ -710,7 +710,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             if (whi == Wn)
                 for (int i = n + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
         } else {
-            constexpr int RC = 64;     // candidate slots per thread in the first load (16384 per head)
+            constexpr int RC = 32;     // candidate slots per thread in the first load (8192 per head; fewer registers)
             constexpr int kB = 16;     // batch of later candidates
             // one round of loads: the head's histogram, the candidates (C came
             // with the arrival that made this workgroup the last one) and the
