@@ -73,6 +73,8 @@ def _load():
         i = ctypes.c_int
         lib.oracle_layer.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p, i, p, i]
         lib.oracle_layer.restype = i
+        lib.oracle_layer_select.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p, i, i, ctypes.c_double, p, i]
+        lib.oracle_layer_select.restype = i
         _lib = lib
     return _lib
 
@@ -89,9 +91,18 @@ def _dtype_code(a: np.ndarray) -> int:
     raise TypeError(f"oracle takes float32 or bf16-as-uint16 arrays, got {a.dtype}")
 
 
+RULES = {"topk": 0, "ratio": 1, "threshold": 2}
+
+
 def layer(q, k_cache, v_cache, role, S_in, n_ctx, k, *, want_scores=False,
-          threads=0):
+          threads=0, rule="topk", param=0.0):
     """One layer.  Returns (out[B,Hq,d] float64, S_out[B,Hkv,k] int32, scores).
+
+    ``rule`` selects S (reading R7 of oracle.c): "topk" (the top min(k, n)),
+    "ratio" (the top min(k, ceil(param * n)), param in (0, 1]) or
+    "threshold" (the tokens with pooled score >= param, the k highest if
+    more); S rows are ascending and padded with -1, and a sparse head skips
+    -1 entries.
 
     q: [B,Hq,d]; k_cache, v_cache: [B,Hkv,max_ctx,d] (float32, or uint16
     holding bfloat16 bits); role: [Hkv] (1 retrieval / 0 sparse); S_in:
@@ -118,9 +129,10 @@ def layer(q, k_cache, v_cache, role, S_in, n_ctx, k, *, want_scores=False,
     out = np.zeros((B, Hq, d), dtype=np.float64)
     S_out = np.full((B, Hkv, k), -1, dtype=np.int32)
     scores = np.full((B, Hkv, max_ctx), np.nan, dtype=np.float64) if want_scores else None
-    rc = _load().oracle_layer(B, Hq, Hkv, d, max_ctx, dt, _ptr(q), _ptr(k_cache),
-                              _ptr(v_cache), _ptr(role), _ptr(S_in), _ptr(S_out),
-                              _ptr(out), _ptr(n_ctx), int(k), _ptr(scores), int(threads))
+    rc = _load().oracle_layer_select(B, Hq, Hkv, d, max_ctx, dt, _ptr(q), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(role), _ptr(S_in), _ptr(S_out),
+                                     _ptr(out), _ptr(n_ctx), int(k), RULES[rule], float(param),
+                                     _ptr(scores), int(threads))
     if rc != 0:
         raise ValueError(f"oracle_layer: {ERRORS.get(rc, rc)}")
     return out, S_out, scores

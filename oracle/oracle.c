@@ -32,6 +32,14 @@
  *   R5  no causal mask, no forced sink / recent tokens; rows >= n are never
  *       read; scale 1/sqrt(d) for both head kinds.
  *   R6  query head h reads KV head floor(h / G).
+ *   R7  selection rules other than top-k (the digest's ablation of
+ *       selection methods, section 4.4.1 / Figure 6, names them without a
+ *       formula): Ratio(theta) keeps the top min(k, ceil(theta * n)) tokens
+ *       (at least 1), theta * n evaluated in double; Threshold(tau) keeps the
+ *       tokens whose pooled score (R2) is >= tau, the k highest of them if
+ *       more.  S then holds fewer than min(k, n) valid entries, padded with
+ *       -1; a sparse head skips -1 entries (an empty set gives output 0).
+ *       Top-p is not provided.
  *
  * Parity status: pinned (see the header of oracle/__init__.py for the list
  * of pins and the tests that hold them).
@@ -102,9 +110,13 @@ static void softmax_weighted_sum(const double* z, const int32_t* rows, int cnt,
     }
 }
 
+#define ORACLE_RULE_TOPK 0
+#define ORACLE_RULE_RATIO 1
+#define ORACLE_RULE_THRESHOLD 2
+
 /*
  * One layer of the step (the per-layer body of Algorithm 1 in [Digest 3.4],
- * attention part only).
+ * attention part only), with the selection rule of reading R7 (rule, param).
  *
  *   q        [B, Hq, d]           dtype
  *   kc, vc   [B, Hkv, max_ctx, d] dtype
@@ -118,12 +130,14 @@ static void softmax_weighted_sum(const double* z, const int32_t* rows, int cnt,
  *   nthreads OpenMP threads (<= 0: library default)
  * Returns ORACLE_OK or a negative error code.
  */
-int oracle_layer(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
-                 const void* q, const void* kc, const void* vc,
-                 const uint8_t* role, const int32_t* S_in, int32_t* S_out,
-                 double* out, const int32_t* n_ctx, int k, double* scores,
-                 int nthreads) {
+int oracle_layer_select(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
+                        const void* q, const void* kc, const void* vc,
+                        const uint8_t* role, const int32_t* S_in, int32_t* S_out,
+                        double* out, const int32_t* n_ctx, int k, int rule, double param,
+                        double* scores, int nthreads) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_ctx <= 0 || k <= 0) return ORACLE_ERR_ARG;
+    if (rule != ORACLE_RULE_TOPK && rule != ORACLE_RULE_RATIO && rule != ORACLE_RULE_THRESHOLD) return ORACLE_ERR_ARG;
+    if (rule == ORACLE_RULE_RATIO && !(param > 0.0 && param <= 1.0)) return ORACLE_ERR_ARG;
     if (Hq % Hkv != 0 || (dtype != 0 && dtype != 1)) return ORACLE_ERR_ARG;
     if (!q || !kc || !vc || !role || !S_out || !out || !n_ctx) return ORACLE_ERR_ARG;
     for (int g = 0; g < Hkv; ++g)
@@ -179,24 +193,39 @@ int oracle_layer(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
                 memcpy(dst, pooled, sizeof(double) * (size_t)n);
             }
             qsort(order, (size_t)n, sizeof(scored), cmp_desc_score_asc_index);
-            for (int r = 0; r < ke; ++r) s_out[r] = order[r].j;
-            qsort(s_out, (size_t)ke, sizeof(int32_t), cmp_int_asc);
-            for (int r = ke; r < k; ++r) s_out[r] = -1;
+            int cnt = ke;                                   /* reading R7 */
+            if (rule == ORACLE_RULE_RATIO) {
+                const double t = ceil(param * (double)n);
+                const int kr = t < 1.0 ? 1 : (t > (double)n ? n : (int)t);
+                cnt = kr < ke ? kr : ke;
+            } else if (rule == ORACLE_RULE_THRESHOLD) {
+                cnt = 0;
+                while (cnt < ke && order[cnt].s >= param) ++cnt;
+            }
+            for (int r = 0; r < cnt; ++r) s_out[r] = order[r].j;
+            qsort(s_out, (size_t)cnt, sizeof(int32_t), cmp_int_asc);
+            for (int r = cnt; r < k; ++r) s_out[r] = -1;
             free(z); free(pooled); free(order);
         } else {
             /* Sparse head: attention over the inherited rows only (Eq. 3), and
              * S^(l+1) = S^(l) unchanged. */
             const int32_t* s_in = S_in + ((size_t)b * Hkv + g) * k;
-            int bad = 0;
-            for (int r = 0; r < ke; ++r)
+            int bad = 0, cnt = 0;
+            int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * (size_t)(ke > 0 ? ke : 1));
+            for (int r = 0; r < ke && rows; ++r) {
+                if (s_in[r] == -1) continue;                /* padding (reading R7) */
                 if (s_in[r] < 0 || s_in[r] >= n) bad = 1;
-            if (bad) {
+                else rows[cnt++] = s_in[r];
+            }
+            if (bad || !rows) {
+                free(rows);
 #pragma omp atomic write
-                status = ORACLE_ERR_S_RANGE;
+                status = bad ? ORACLE_ERR_S_RANGE : ORACLE_ERR_MEM;
                 continue;
             }
-            double* z = (double*)malloc(sizeof(double) * (size_t)ke);
+            double* z = (double*)malloc(sizeof(double) * (size_t)(ke > 0 ? ke : 1));
             if (!z) {
+                free(rows);
 #pragma omp atomic write
                 status = ORACLE_ERR_MEM;
                 continue;
@@ -204,13 +233,28 @@ int oracle_layer(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
             for (int i = 0; i < G; ++i) {
                 const int h = g * G + i;
                 const size_t q_off = ((size_t)b * Hq + h) * d;
-                for (int r = 0; r < ke; ++r)
-                    z[r] = c * dot_row(q, q_off, kc, kv_base + (size_t)s_in[r] * d, d, dtype);
-                softmax_weighted_sum(z, s_in, ke, vc, kv_base, d, dtype, out + q_off);
+                if (cnt == 0) {                             /* empty set: output 0 */
+                    for (int t = 0; t < d; ++t) out[q_off + t] = 0.0;
+                    continue;
+                }
+                for (int r = 0; r < cnt; ++r)
+                    z[r] = c * dot_row(q, q_off, kc, kv_base + (size_t)rows[r] * d, d, dtype);
+                softmax_weighted_sum(z, rows, cnt, vc, kv_base, d, dtype, out + q_off);
             }
             if (s_out != s_in) memmove(s_out, s_in, sizeof(int32_t) * (size_t)k);
             free(z);
+            free(rows);
         }
     }
     return status;
+}
+
+/* The top-k rule (the product's default): oracle_layer_select with rule 0. */
+int oracle_layer(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
+                 const void* q, const void* kc, const void* vc,
+                 const uint8_t* role, const int32_t* S_in, int32_t* S_out,
+                 double* out, const int32_t* n_ctx, int k, double* scores,
+                 int nthreads) {
+    return oracle_layer_select(B, Hq, Hkv, d, max_ctx, dtype, q, kc, vc, role, S_in, S_out, out, n_ctx, k,
+                               ORACLE_RULE_TOPK, 0.0, scores, nthreads);
 }

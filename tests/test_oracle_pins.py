@@ -308,3 +308,90 @@ def test_oracle_rejects_bad_arguments():
         oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, np.array([33], np.int32), 4)
     with pytest.raises(ValueError):
         oracle.step([(q, kc, vc, np.zeros(1, np.uint8))], n_ctx, 4)
+
+
+# ---------------------------------------------------------------- selection rules (reading R7)
+
+def _pooled_scores_by_hand(q, kc, b, g, n, G):
+    """Mean over the group's G heads of q_h . k_j / sqrt(d), in float64 loops."""
+    d = q.shape[2]
+    s = np.zeros(n)
+    for j in range(n):
+        acc = 0.0
+        for i in range(G):
+            acc += float(np.dot(q[b, g * G + i].astype(np.float64), kc[b, g, j].astype(np.float64))) / math.sqrt(d)
+        s[j] = acc / G
+    return s
+
+
+def test_ratio_rule_is_topk_of_ceil_theta_n():
+    """Ratio(theta) keeps min(k, ceil(theta * n)) tokens; theta with
+    ceil(theta * n) = k' reduces to top-k', theta = 1 with k >= n keeps all."""
+    rng = np.random.default_rng(31)
+    G, Hkv, d, n = 4, 2, 32, 200
+    q, kc, vc, n_ctx = _f32_case(rng, 1, Hkv * G, Hkv, d, n)
+    ones = np.ones(Hkv, np.uint8)
+    for theta, kprime in ((0.1, 20), (0.2525, 51), (0.005, 1), (0.0001, 1)):
+        _, S_r, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, 64, rule="ratio", param=theta)
+        _, S_k, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, kprime)
+        np.testing.assert_array_equal(S_r[:, :, :kprime], S_k, err_msg=f"theta={theta}")
+        assert np.all(S_r[:, :, kprime:] == -1)
+    _, S_all, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, 256, rule="ratio", param=1.0)
+    np.testing.assert_array_equal(S_all[0, 0, :n], np.arange(n))
+    assert np.all(S_all[:, :, n:] == -1)
+    # the budget cap k still applies
+    _, S_cap, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, 16, rule="ratio", param=0.5)
+    _, S_16, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, 16)
+    np.testing.assert_array_equal(S_cap, S_16)
+
+
+def test_threshold_rule_matches_scores_computed_by_hand():
+    """Threshold(tau) keeps the tokens with pooled score >= tau (the k highest
+    if more): checked against scores computed in plain loops, plus the closed
+    forms tau = -inf (top-k) and tau = +inf (empty)."""
+    rng = np.random.default_rng(32)
+    G, Hkv, d, n, k = 2, 2, 16, 60, 40
+    q, kc, vc, n_ctx = _f32_case(rng, 1, Hkv * G, Hkv, d, n)
+    ones = np.ones(Hkv, np.uint8)
+    for g in range(Hkv):
+        s = _pooled_scores_by_hand(q, kc, 0, g, n, G)
+        for tau in (np.sort(s)[-5], np.sort(s)[-25], np.median(s), np.sort(s)[-50]):
+            _, S, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, k, rule="threshold", param=float(tau))
+            keep = [j for j in sorted(range(n), key=lambda j: (-s[j], j)) if s[j] >= tau][:k]
+            got = S[0, g]
+            np.testing.assert_array_equal(got[:len(keep)], np.sort(keep), err_msg=f"g={g} tau={tau}")
+            assert np.all(got[len(keep):] == -1)
+    _, S_lo, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, k, rule="threshold", param=-math.inf)
+    _, S_k, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, k)
+    np.testing.assert_array_equal(S_lo, S_k)
+    _, S_hi, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, k, rule="threshold", param=math.inf)
+    assert np.all(S_hi == -1)
+
+
+def test_sparse_head_skips_padding_and_empty_set_gives_zero():
+    """-1 entries of S_in are padding: a sparse head over S with padding equals
+    the sparse head over the valid entries alone; an all-padding S gives 0."""
+    rng = np.random.default_rng(33)
+    G, Hkv, d, n, k = 4, 2, 32, 100, 10
+    q, kc, vc, n_ctx = _f32_case(rng, 1, Hkv * G, Hkv, d, n)
+    sparse = np.zeros(Hkv, np.uint8)
+    S_pad = np.full((1, Hkv, k), -1, np.int32)
+    S_pad[0, 0, :4] = [3, 17, 50, 99]
+    S_pad[0, 1, :1] = [42]
+    out_pad, S_fwd, _ = oracle.layer(q, kc, vc, sparse, S_pad, n_ctx, k)
+    np.testing.assert_array_equal(S_fwd, S_pad)
+    # head 0 over rows {3, 17, 50, 99} equals dense attention restricted to them by hand
+    for i in range(G):
+        h = i
+        z = np.array([float(np.dot(q[0, h].astype(np.float64), kc[0, 0, j].astype(np.float64))) / math.sqrt(d)
+                      for j in (3, 17, 50, 99)])
+        w = np.exp(z - z.max())
+        w /= w.sum()
+        ref = sum(w[r] * vc[0, 0, j].astype(np.float64) for r, j in enumerate((3, 17, 50, 99)))
+        np.testing.assert_allclose(out_pad[0, h], ref, rtol=0, atol=1e-12)
+    # head 1 over a single row returns that V row
+    for i in range(G):
+        np.testing.assert_allclose(out_pad[0, G + i], vc[0, 1, 42].astype(np.float64), rtol=0, atol=1e-12)
+    S_empty = np.full((1, Hkv, k), -1, np.int32)
+    out_e, _, _ = oracle.layer(q, kc, vc, sparse, S_empty, n_ctx, k)
+    assert np.all(out_e == 0.0)
