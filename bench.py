@@ -6,6 +6,7 @@ resident in HBM, captured once into a HIP graph and replayed.  Reported next
 to the dense all-heads decode step on the same GPU and the CPU oracle.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama3_128k]
+                    [--rule topk|ratio|threshold --param P]
 
 Prints one JSON line.  Algorithmic bytes per step (what the method must move;
 workspace traffic excluded):
@@ -13,7 +14,9 @@ workspace traffic excluded):
             + R_l sum_b 4 k_eff + B Hq d (s + 4) ]
 with R_l retrieval KV heads in layer l, s bytes per cache element, k_eff =
 min(k, n_b) (S_out aliases nothing extra: sparse rows are read once, written
-once by the copy and counted as the 4 k_eff read).
+once by the copy and counted as the 4 k_eff read).  Under the ratio and
+threshold rules a sparse head gathers only the valid (not -1) entries of its
+row, so its 2 k_eff d s term counts those instead.
 """
 from __future__ import annotations
 
@@ -36,8 +39,10 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attend_llama3_128k_counters.json")
 
 
-def algorithmic_bytes(w: synth.Workload, roles: np.ndarray, lens: np.ndarray):
-    """Per-layer algorithmic bytes of the hybrid step and of the dense step."""
+def algorithmic_bytes(w: synth.Workload, roles: np.ndarray, lens: np.ndarray, valid=None):
+    """Per-layer algorithmic bytes of the hybrid step and of the dense step.
+    ``valid[l][b][g]``: valid entries of the S row a sparse head of layer l
+    attends to (default k_eff)."""
     s = 2 if w.dtype == "bf16" else 4
     d = w.head_dim
     hyb, dense = [], []
@@ -49,7 +54,10 @@ def algorithmic_bytes(w: synth.Workload, roles: np.ndarray, lens: np.ndarray):
             n = int(lens[b])
             ke = min(w.k, n)
             tot += R * (2 * n * d * s + 4 * ke)
-            tot += (w.n_kv_heads - R) * (2 * ke * d * s + 4 * ke)
+            for g in range(w.n_kv_heads):
+                if not roles[l][g]:
+                    nv = ke if valid is None else int(valid[l][b][g])
+                    tot += 2 * nv * d * s + 4 * ke
         hyb.append(tot)
         dense.append(qo + w.n_kv_heads * sum(2 * int(n) * d * s for n in lens))
     return hyb, dense
@@ -73,7 +81,7 @@ def load_inputs(w, roles, lens, keep_host_layers: int, threads: int):
     return dev, host
 
 
-def cpu_baseline(w, roles, lens, host_layers, budget_s: float, threads: int):
+def cpu_baseline(w, roles, lens, host_layers, budget_s: float, threads: int, rule="topk", param=0.0):
     """Time the oracle (as it stands) on the first layers of the step, chained
     through S, repeating that chain until `budget_s` of CPU work; scale to the
     whole step by pooled work units (n per retrieval head, k_eff per sparse head)."""
@@ -88,7 +96,8 @@ def cpu_baseline(w, roles, lens, host_layers, budget_s: float, threads: int):
         S = None
         for l, x in enumerate(host_layers):
             t0 = time.perf_counter()
-            _, S, _ = oracle.layer(x["q"], x["k"], x["v"], roles[l], S, lens, w.k, threads=threads)
+            _, S, _ = oracle.layer(x["q"], x["k"], x["v"], roles[l], S, lens, w.k, threads=threads, rule=rule,
+                                   param=param)
             t_total += time.perf_counter() - t0
         passes += 1
     frac = passes * sum(units[:nl]) / sum(units)
@@ -120,6 +129,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--rule", default="topk", choices=["topk", "ratio", "threshold"],
+                    help="selection rule of the retrieval heads (default: top-k, the headline)")
+    ap.add_argument("--param", type=float, default=0.0, help="theta of the ratio rule, tau of the threshold rule")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -147,7 +159,8 @@ def main():
     def step():
         for l in range(w.layers):
             x = dev[l]
-            h.decode_layer(x["q"], x["k"], x["v"], roles[l], S[l - 1] if l else None, S[l], outs[l], n_ctx, k)
+            h.decode_layer(x["q"], x["k"], x["v"], roles[l], S[l - 1] if l else None, S[l], outs[l], n_ctx, k,
+                           rule=args.rule, param=args.param)
 
     def dense_step():
         for l in range(w.layers):
@@ -216,7 +229,8 @@ def main():
             a, b = rep[l]
             h.set_profile_events(a, b)
             x = dev[l]
-            h.decode_layer(x["q"], x["k"], x["v"], roles[l], S[l - 1] if l else None, S[l], outs[l], n_ctx, k)
+            h.decode_layer(x["q"], x["k"], x["v"], roles[l], S[l - 1] if l else None, S[l], outs[l], n_ctx, k,
+                           rule=args.rule, param=args.param)
     h.set_profile_events(None, None)
     torch.cuda.synchronize()
     for rep in ev_pairs:
@@ -224,7 +238,12 @@ def main():
             a, b = rep[l]
             att_ms[l].append(a.elapsed_time(b))
 
-    hyb_bytes, dense_bytes = algorithmic_bytes(w, roles, lens)
+    valid = None
+    kept = [int((ref_S[l][:, g] != -1).sum()) for l in range(w.layers) for g in range(Hkv) if roles[l][g]]
+    if args.rule != "topk":
+        valid = [np.zeros((B, Hkv), np.int64)] + [(ref_S[l - 1] != -1).sum(dim=2).cpu().numpy()
+                                                  for l in range(1, w.layers)]
+    hyb_bytes, dense_bytes = algorithmic_bytes(w, roles, lens, valid)
     step_bytes = sum(hyb_bytes)
     att_mean = [statistics.mean(v) for v in att_ms]
     att_all_bytes = sum(hyb_bytes)                    # per step, over all attention launches
@@ -265,7 +284,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, roles, lens, host, args.cpu_budget, threads)
+        cpu = cpu_baseline(w, roles, lens, host, args.cpu_budget, threads, args.rule, args.param)
 
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     n_retr = int(roles.sum())
@@ -285,7 +304,9 @@ def main():
         "config": {"workload": w.name, "batch": B, "layers": w.layers, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": d, "n_ctx": [int(v) for v in lens] if B > 1 else int(lens[0]), "k": k,
                    "kv_cache": w.dtype, "retrieval_kv_head_instances": n_retr,
-                   "sparse_kv_head_instances": w.layers * Hkv - n_retr},
+                   "sparse_kv_head_instances": w.layers * Hkv - n_retr,
+                   "selection_rule": args.rule if args.rule == "topk" else f"{args.rule}({args.param:g})"},
+        "mean_selected_per_retrieval_head": statistics.mean(kept) / B,
         "achieved_GBps": step_gbps,
         "frac_of_hbm_peak": step_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
@@ -296,7 +317,7 @@ def main():
         "speedup_vs_dense": (dense_res["us_per_step"] / (ms_per_step * 1e3)) if dense_res else None,
         "roofline": {"kernel": "attend_kernel (hybrid, all launches of the step)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": counters_traffic(),
+                     "traffic": counters_traffic() if args.rule == "topk" else None,
                      "bytes_per_launch": att_all_bytes / w.layers, "avg_launch_us": att_all_ms / w.layers * 1e3},
         "roofline_all_retrieval_layer": {"kernel": "attend_kernel (hybrid), layer 0: every KV head retrieval",
                                          "achieved": l0_achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -31,9 +31,11 @@ LYCHEE_ERR_WORKSPACE = -4
 LYCHEE_ERR_DEVICE_CHECK = -5
 LYCHEE_F32 = 0
 LYCHEE_BF16 = 1
+SELECT_RULES = {"topk": 0, "ratio": 1, "threshold": 2}   # LYCHEE_SELECT_*
 
 EXPORTED = (
-    "lychee_workspace_bytes", "lychee_create", "lychee_decode_layer", "lychee_dense_decode_layer",
+    "lychee_workspace_bytes", "lychee_create", "lychee_decode_layer", "lychee_decode_layer_select",
+    "lychee_dense_decode_layer",
     "lychee_validate_layer", "lychee_set_stream", "lychee_set_profile_events",
     "lychee_check_device_errors", "lychee_destroy", "lychee_status_str", "lychee_last_error",
 )
@@ -69,6 +71,7 @@ def load() -> ctypes.CDLL:
         "lychee_workspace_bytes": (u64, [pd]),
         "lychee_create": (i32, [pd, vp, u64, vp, ctypes.POINTER(vp)]),
         "lychee_decode_layer": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]),
+        "lychee_decode_layer_select": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_double]),
         "lychee_dense_decode_layer": (i32, [vp, vp, vp, vp, vp, vp]),
         "lychee_validate_layer": (i32, [pd, vp, vp, vp, vp, vp, vp, vp, vp, i32]),
         "lychee_set_stream": (i32, [vp, vp]),
@@ -169,8 +172,14 @@ class Handle:
     def set_stream(self, stream=None):
         _check(load().lychee_set_stream(self._h, self._stream_ptr(stream)), "lychee_set_stream")
 
-    def decode_layer(self, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k):
-        """One hybrid layer; enqueues on the handle's stream and returns at once."""
+    def decode_layer(self, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k, rule="topk", param=0.0):
+        """One hybrid layer; enqueues on the handle's stream and returns at once.
+
+        ``rule`` picks the retrieval heads' selection ("topk", "ratio" with
+        theta = ``param``, "threshold" with tau = ``param``); anything but
+        "topk" goes through lychee_decode_layer_select."""
+        if rule not in SELECT_RULES:
+            raise ValueError(f"unknown selection rule {rule!r}; expected one of {sorted(SELECT_RULES)}")
         d = self.dims
         torch = self._torch
         self._check_common(q, k_cache, v_cache, out, n_ctx)
@@ -180,9 +189,13 @@ class Handle:
         role = np.ascontiguousarray(np.asarray(role_mask, dtype=np.uint8).reshape(-1))
         if role.size != d.n_kv_heads:
             raise ValueError(f"role_mask has {role.size} entries, expected {d.n_kv_heads}")
-        _check(load().lychee_decode_layer(self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                          role.ctypes.data_as(ctypes.c_void_p), _ptr(S_in), _ptr(S_out),
-                                          _ptr(out), _ptr(n_ctx), int(k)), "lychee_decode_layer")
+        args = (self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache), role.ctypes.data_as(ctypes.c_void_p), _ptr(S_in),
+                _ptr(S_out), _ptr(out), _ptr(n_ctx), int(k))
+        if rule == "topk":
+            _check(load().lychee_decode_layer(*args), "lychee_decode_layer")
+        else:
+            _check(load().lychee_decode_layer_select(*args, SELECT_RULES[rule], float(param)),
+                   "lychee_decode_layer_select")
 
     def dense_decode_layer(self, q, k_cache, v_cache, out, n_ctx):
         """Dense all-heads decode attention (the baseline)."""

@@ -222,7 +222,8 @@ lychee_status lychee_set_profile_events(lychee_handle* h, void* start, void* sto
 
 static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, const void* vc,
                                const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out, float* out,
-                               const int32_t* n_ctx, int32_t k, bool hybrid) {
+                               const int32_t* n_ctx, int32_t k, bool hybrid, int32_t rule = LYCHEE_SELECT_TOPK,
+                               double param = 0.0) {
     const lychee_dims& d = h->dims;
     uint64_t bits = 0;
     for (int g = 0; g < d.n_kv_heads; ++g)
@@ -243,6 +244,12 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
     ap.k = hybrid ? k : 1;
     ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
     const int G = d.n_q_heads / d.n_kv_heads;
+    ap.sel_ratio = rule == LYCHEE_SELECT_RATIO ? param : 1.0;
+    // The kernel's selection key is the fp32 sum of the G query heads' raw
+    // dot products, i.e. G sqrt(d) times the pooled score: tau maps there.
+    ap.sel_tkey = rule == LYCHEE_SELECT_THRESHOLD
+                      ? float_key((float)(param * (double)G * std::sqrt((double)d.head_dim)))
+                      : 0u;
     if (h->ev_start && hipEventRecord(h->ev_start, h->stream) != hipSuccess)
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
     hipError_t e = launch_attend(ap, d.dtype, d.head_dim, G, hybrid, h->cus, h->per_cu, h->stream);
@@ -259,6 +266,23 @@ lychee_status lychee_decode_layer(lychee_handle* h, const void* q, const void* k
     lychee_status s = lychee_validate_layer(&h->dims, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k);
     if (s != LYCHEE_OK) return s;
     return run_layer(h, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k, true);
+}
+
+lychee_status lychee_decode_layer_select(lychee_handle* h, const void* q, const void* k_cache,
+                                         const void* v_cache, const uint8_t* role_mask, const int32_t* S_in,
+                                         int32_t* S_out, float* out, const int32_t* n_ctx, int32_t k, int32_t rule,
+                                         double param) {
+    // the rule is checked first (host-only, so it can be checked without a device)
+    if (rule != LYCHEE_SELECT_TOPK && rule != LYCHEE_SELECT_RATIO && rule != LYCHEE_SELECT_THRESHOLD)
+        return fail(LYCHEE_ERR_INVALID_ARG, "rule must be LYCHEE_SELECT_TOPK, _RATIO or _THRESHOLD (got %d)", rule);
+    if (rule == LYCHEE_SELECT_RATIO && !(param > 0.0 && param <= 1.0))
+        return fail(LYCHEE_ERR_INVALID_ARG, "the ratio rule's theta must be in (0, 1] (got %g)", param);
+    if (rule == LYCHEE_SELECT_THRESHOLD && std::isnan(param))
+        return fail(LYCHEE_ERR_INVALID_ARG, "the threshold rule's tau is NaN");
+    if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");
+    lychee_status s = lychee_validate_layer(&h->dims, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k);
+    if (s != LYCHEE_OK) return s;
+    return run_layer(h, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k, true, rule, param);
 }
 
 lychee_status lychee_dense_decode_layer(lychee_handle* h, const void* q, const void* k_cache, const void* v_cache,
@@ -278,7 +302,7 @@ lychee_status lychee_check_device_errors(lychee_handle* h) {
     if (flag) {
         if (hipMemset(h->ws.err, 0, sizeof flag) != hipSuccess)
             return fail(LYCHEE_ERR_HIP, "clearing the device error flag failed");
-        return fail(LYCHEE_ERR_DEVICE_CHECK, "device error flag 0x%x (1: S_in entry outside [0, n_ctx); 2: select count mismatch)",
+        return fail(LYCHEE_ERR_DEVICE_CHECK, "device error flag 0x%x (1: S_in entry outside [0, n_ctx) and not -1; 2: select count mismatch)",
                     flag);
     }
     return ok();

@@ -508,6 +508,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     __shared__ uint32_t s_pref[kMaxBH + 1];
     __shared__ uint32_t s_bound[kMaxWG + 1];   // cost position where each workgroup's range starts
     __shared__ int32_t s_nctx[kMaxBH];
+    __shared__ uint32_t s_ke[kMaxBH];          // tokens a retrieval head of sequence b selects
     __shared__ uint32_t s_wave[kWaves];
     __shared__ uint32_t s_res[4];
     __shared__ uint32_t s_ctr;
@@ -531,8 +532,16 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #pragma unroll
         for (int i = 0; i < PER; ++i) nb[i] = p.n_ctx[min(tid * PER + i, p.B - 1)];
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (tid * PER + i < p.B) s_nctx[tid * PER + i] = nb[i];
+        for (int i = 0; i < PER; ++i) {
+            if (tid * PER + i < p.B) {
+                const int n = nb[i];
+                // min(k, n), or under the ratio rule min(k, ceil(theta n)) (at least one)
+                const double t = ceil(p.sel_ratio * (double)n);
+                const uint32_t kr = t < 1.0 ? 1u : (t > (double)n ? (uint32_t)n : (uint32_t)t);
+                s_nctx[tid * PER + i] = n;
+                s_ke[tid * PER + i] = min((uint32_t)min(p.k, n), kr);
+            }
+        }
         __syncthreads();
         uint32_t u_[PER];
         uint32_t tot = 0;
@@ -623,14 +632,14 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 
     // Classify the candidates this thread holds (slot e is candidate
     // base + tid + 256 e; slots from nslots on, or past C, hold none): key above
-    // the threshold digit's range -> the bitmap bit if its index lies in the
-    // slice [rlo, rlo + rlen), else counted in `below` if it lies under the
-    // slice; inside the digit's range -> the composite is appended to u.se.comp
+    // kab (the top of the threshold digit's range, raised to just under the
+    // threshold rule's key floor) -> the bitmap bit if its index lies in the
+    // slice [rlo, rlo + rlen), else counted in `below` if it lies under the slice; inside the digit's range -> the composite is appended to u.se.comp
     // at the position an LDS counter (s_ceq) hands out (the group is ranked by
     // value, so its order does not matter).  LDS operations cost per active
     // lane, so only the lanes with something to write issue them.
     auto classify_batch = [&](auto& vals, uint32_t nslots, uint32_t base, uint32_t C, uint32_t klo, uint32_t khi,
-                              uint32_t rlo, uint32_t rlen, uint32_t& below) {
+                              uint32_t kab, uint32_t rlo, uint32_t rlen, uint32_t& below) {
         constexpr int NB = (int)(sizeof(vals) / sizeof(vals[0]));
         static_assert(NB % 8 == 0 && NB <= 64, "slots come in groups of 8, at most 64");
         const uint32_t lim = C - base;
@@ -642,7 +651,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     const uint32_t key = (uint32_t)vals[e];
                     const uint32_t j = (uint32_t)(vals[e] >> 32) & kIdxMask;
                     const bool valid = tid + (uint32_t)(kAttendThreads * e) < lim;
-                    const bool above = valid && key > khi;
+                    const bool above = valid && key > kab;
                     const bool eq = valid && key - klo <= khi - klo;
                     if (above && j - rlo < rlen) atomicOr(&u.se.bits[(j - rlo) >> 5], 1u << (j & 31));
                     below += (above && j < rlo) ? 1u : 0u;
@@ -683,7 +692,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         const uint32_t rlo = wlo * 32u, rlen = (whi - wlo) * 32u;
         const int W = (int)(whi - wlo);                      // bitmap words of the slices
         uint32_t below = 0;                                  // this thread's winners under the slices
-        auto mark = [&](uint32_t j) {                        // winner j
+        auto mark = [&](uint32_t j, uint32_t key) {          // winner j with selection key `key`
+            if (key < p.sel_tkey) return;                    // under the threshold rule's floor
             if (j - rlo < rlen) atomicOr(&u.se.bits[(j - rlo) >> 5], 1u << (j & 31));
             below += j < rlo ? 1u : 0u;
         };
@@ -704,7 +714,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 for (int i = tid; i < kHistBins; i += kAttendThreads) coherent_store(&gh[i], 0u);
         };
         __syncthreads();
-        if (ke == (uint32_t)n) {
+        if (ke == (uint32_t)n && p.sel_tkey == 0u) {      // every token (the threshold rule still filters)
             release_head();
             for (uint32_t i = rlo + tid; i < min(rlo + rlen, (uint32_t)n); i += kAttendThreads) srow[i] = (int32_t)i;
             if (whi == Wn)
@@ -786,12 +796,17 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
             const uint32_t klo = (uint32_t)digit_first_key(T_);              // key range of digit T
             const uint32_t khi = (uint32_t)(digit_first_key(T_ + 1u) - 1ull);
-            if (!fb) classify_batch(cv, nslots, 0u, C, klo, khi, rlo, rlen, below);
+            // key of a composite of digit T (the digit's keys share their bits above kLowBits)
+            auto comp_key = [&](unsigned long long cp) -> uint32_t {
+                return (klo & ~((1u << kLowBits) - 1u)) | (uint32_t)(cp >> kIdxBits);
+            };
+            const uint32_t kab = p.sel_tkey ? max(khi, p.sel_tkey - 1u) : khi;   // winners above the digit
+            if (!fb) classify_batch(cv, nslots, 0u, C, klo, khi, kab, rlo, rlen, below);
             for (uint32_t base = fb ? 0u : kAttendThreads * RC; base < Cs; base += kAttendThreads * kB) {
                 unsigned long long bv[kB];
 #pragma unroll
                 for (int e = 0; e < kB; ++e) bv[e] = fetch(min(base + tid + (uint32_t)(kAttendThreads * e), Cs - 1u));
-                classify_batch(bv, (uint32_t)kB, base, Cs, klo, khi, rlo, rlen, below);
+                classify_batch(bv, (uint32_t)kB, base, Cs, klo, khi, kab, rlo, rlen, below);
             }
             __syncthreads();
             uint32_t c_left = s_ceq;          // keys of digit T appended
@@ -839,7 +854,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                             const unsigned long long cp = composite(key, j);
                             if (shift < kCompBits && (cp >> shift) != prefix) continue;
                             const uint32_t dg = comp_digit(cp, nshift, bits);
-                            if (dg > Dg || (r_left - gt == keep && dg == Dg)) mark(j);
+                            if (dg > Dg || (r_left - gt == keep && dg == Dg)) mark(j, key);
                         }
                     }
                     __syncthreads();
@@ -883,7 +898,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
             if (!done && r_left == c_left) {   // the whole threshold group is selected
                 for (uint32_t i = tid; i < c_left; i += kAttendThreads) {
-                    mark(comp_index(u.se.comp[i]));
+                    const unsigned long long cp = u.se.comp[i];
+                    mark(comp_index(cp), comp_key(cp));
                 }
                 done = true;
             }
@@ -895,7 +911,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     const unsigned long long mine = u.se.comp[min((uint32_t)tid, c_left - 1u)];
                     uint32_t above = 0;
                     for (uint32_t r = 0; r < c_left; ++r) above += u.se.comp[r] > mine;
-                    if ((uint32_t)tid < c_left && above < r_left) mark(comp_index(mine));
+                    if ((uint32_t)tid < c_left && above < r_left) mark(comp_index(mine), comp_key(mine));
                     done = true;
                     break;
                 }
@@ -932,7 +948,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 for (int e = 0; e < kCandPerThread; ++e) {
                     if ((uint32_t)e < nsl) {
                         const bool sel = dg[e] != 0xFFFFFFFFu && dg[e] > Dg;
-                        if (sel) mark(comp_index(mine[e]) & kIdxMask);
+                        if (sel) mark(comp_index(mine[e]) & kIdxMask, comp_key(mine[e]));
                         m |= (uint32_t)(dg[e] == Dg) << e;
                     }
                 }
@@ -953,7 +969,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     done = true;
                 } else if (r_left == c_left) {
                     for (uint32_t i = tid; i < c_left; i += kAttendThreads) {
-                        mark(comp_index(u.se.comp[i]));
+                        const unsigned long long cp = u.se.comp[i];
+                        mark(comp_index(cp), comp_key(cp));
                     }
                     done = true;
                 }
@@ -1006,8 +1023,11 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 }
             }
             if (whi == Wn) {           // the slice holding the end of the context
-                for (int i = (int)ke + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
-                if (tid == 0 && below_total + total != ke) atomicOr(p.ws.err, 2u);
+                // (the threshold rule keeps the winners at or above its floor)
+                const uint32_t kept = p.sel_tkey ? min(below_total + total, ke) : ke;
+                for (int i = (int)kept + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
+                if (tid == 0 && (p.sel_tkey ? below_total + total > ke : below_total + total != ke))
+                    atomicOr(p.ws.err, 2u);
             }
         }
         __syncthreads();
@@ -1040,7 +1060,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         const uint32_t seg_lo = (max(lo, h0) - h0) / cw;     // first row (position) of this head
         const uint32_t seg_hi = (min(hi, h1) - h0) / cw;
         const int n = s_nctx[b];
-        const uint32_t ke = (uint32_t)min(p.k, n);
+        const uint32_t ks = (uint32_t)min(p.k, n);         // S entries of the head
+        const uint32_t ke = s_ke[b];                          // tokens a retrieval head selects
 
         // query slices: register h' holds query head g*G + (h' ^ xl), elements x*EPL..
         Frag<NDW> qf[G];
@@ -1082,7 +1103,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     tk = sidx[pk - r_lo];
                     tv = sidx[pv - r_lo];
                     const bool okk = (unsigned)tk < (unsigned)n;
-                    if (!okk) bad_index = true;
+                    if ((unsigned)(tk + 1) > (unsigned)n) bad_index = true;   // -1 (padding of a shorter set) is fine
                     if (i == 0) vmine = okk && (rb + (uint32_t)xh < r_hi);
                     tk = okk ? tk : 0;
                     tv = ((unsigned)tv < (unsigned)n) ? tv : 0;
@@ -1326,7 +1347,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // entries past min(k, n) (the -1 padding of a short context) belong
             // to the workgroup that finishes the head
             if (Sout && h1 <= hi) {
-                for (uint32_t i = ke + tid; i < (uint32_t)p.k; i += kAttendThreads) Sout[i] = Srow[i];
+                for (uint32_t i = ks + tid; i < (uint32_t)p.k; i += kAttendThreads) Sout[i] = Srow[i];
             }
         }
         if (bad_index) atomicOr(p.ws.err, 1u);

@@ -180,6 +180,12 @@ struct AttendParams {
     uint64_t role_bits;     // bit g set = KV head g is a retrieval head
     int32_t B, Hkv, max_ctx, k;
     float scale_log2;       // log2(e) / sqrt(d)
+    // Selection rule of the retrieval heads: the top min(k, ceil(sel_ratio n))
+    // tokens (at least one; sel_ratio = 1 for top-k), of which those whose
+    // selection key is >= sel_tkey (0 = no floor: every key is >= 0) are
+    // kept.  S is padded with -1.
+    double sel_ratio;
+    uint32_t sel_tkey;
 };
 
 // Host launcher (defined next to the kernel).  dtype: 0 fp32, 1 bf16.  The

@@ -92,20 +92,50 @@ lychee_status lychee_create(const lychee_dims* dims, void* workspace, size_t wor
  *   role_mask  (host) [Hkv] uint8, nonzero = retrieval head, 0 = sparse head
  *   S_in       [B, Hkv, k] int32 from the previous layer's S_out; may be NULL
  *              only when every role is retrieval (layer 0).  Entries of a
- *              sparse head's row must lie in [0, n_ctx[b]) for the first
- *              min(k, n_ctx[b]) positions; other entries are ignored.
+ *              sparse head's row must lie in [0, n_ctx[b]) or be -1 (padding
+ *              of a set shorter than min(k, n_ctx[b]), skipped) for the first
+ *              min(k, n_ctx[b]) positions; later entries are copied, not read.
+ *              A sparse head whose entries are all padding outputs zeros.
  *   S_out      [B, Hkv, k] int32; retrieval rows get the new set (ascending,
  *              -1 padded), sparse rows a copy of S_in's row.  S_out may equal
  *              S_in (in place); any other overlap is rejected.
  *   out        [B, Hq, d] fp32, fully overwritten
  *   n_ctx      [B] int32 on the device, 1 <= n_ctx[b] <= max_ctx
  *   k          1 <= k <= k_max
- * Entries of S_in outside [0, n_ctx[b]) are skipped (never read through) and
- * latch a flag reported by lychee_check_device_errors. */
+ * Entries of S_in outside [0, n_ctx[b]) other than -1 are skipped (never read
+ * through) and latch a flag reported by lychee_check_device_errors. */
 lychee_status lychee_decode_layer(lychee_handle* h,
                                   const void* q, const void* k_cache, const void* v_cache,
                                   const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out,
                                   float* out, const int32_t* n_ctx, int32_t k);
+
+/* Selection rules of lychee_decode_layer_select.  The digest's ablation of
+ * selection methods (section 4.4.1, Figure 6) compares top-k with a ratio and
+ * a threshold rule without giving their formulas; these are the plain
+ * readings, with s_j the score Eq. 2 ranks (the mean over a KV head's G
+ * query heads of q . k_j / sqrt(d)) and n = n_ctx[b]:
+ *   TOPK       the min(k, n) highest-scoring tokens (lychee_decode_layer);
+ *   RATIO      the min(k, ceil(theta n)) highest (at least one), theta =
+ *              param in (0, 1], theta n evaluated in double;
+ *   THRESHOLD  the tokens with s_j >= tau (param), the k highest of them if
+ *              there are more.  The kernel compares the fp32 sum over the G
+ *              heads of q . k_j with tau G sqrt(d) rounded to fp32, so a score
+ *              within fp32 rounding of tau may fall on either side.
+ * Ties go to the lower index under every rule. */
+enum { LYCHEE_SELECT_TOPK = 0, LYCHEE_SELECT_RATIO = 1, LYCHEE_SELECT_THRESHOLD = 2 };
+
+/* lychee_decode_layer with a selection rule for the retrieval heads (above).
+ * A retrieval row of S_out holds its selected tokens ascending, then -1 up to
+ * k; a later sparse head skips the -1 entries.  Arguments as for
+ * lychee_decode_layer, plus `rule` (a LYCHEE_SELECT_* value) and `param`
+ * (theta for RATIO, tau for THRESHOLD, unused for TOPK).  Returns
+ * LYCHEE_ERR_INVALID_ARG for an unknown rule, theta outside (0, 1] or a NaN
+ * tau, after which nothing is enqueued. */
+lychee_status lychee_decode_layer_select(lychee_handle* h,
+                                         const void* q, const void* k_cache, const void* v_cache,
+                                         const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out,
+                                         float* out, const int32_t* n_ctx, int32_t k, int32_t rule,
+                                         double param);
 
 /* Dense all-heads decode attention over the same layout (every head attends
  * to all n_ctx[b] tokens, Eq. 1 without selection): the baseline the hybrid

@@ -98,7 +98,7 @@ def layer(q, k_cache, v_cache, role, S_in, n_ctx, k, *, want_scores=False,
           threads=0, rule="topk", param=0.0):
     """One layer.  Returns (out[B,Hq,d] float64, S_out[B,Hkv,k] int32, scores).
 
-    ``rule`` selects S (reading R7 of oracle.c): "topk" (the top min(k, n)),
+    ``rule`` selects S (reading R16 of oracle.c): "topk" (the top min(k, n)),
     "ratio" (the top min(k, ceil(param * n)), param in (0, 1]) or
     "threshold" (the tokens with pooled score >= param, the k highest if
     more); S rows are ascending and padded with -1, and a sparse head skips

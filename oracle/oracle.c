@@ -32,7 +32,7 @@
  *   R5  no causal mask, no forced sink / recent tokens; rows >= n are never
  *       read; scale 1/sqrt(d) for both head kinds.
  *   R6  query head h reads KV head floor(h / G).
- *   R7  selection rules other than top-k (the digest's ablation of
+ *   R16 selection rules other than top-k (the digest's ablation of
  *       selection methods, section 4.4.1 / Figure 6, names them without a
  *       formula): Ratio(theta) keeps the top min(k, ceil(theta * n)) tokens
  *       (at least 1), theta * n evaluated in double; Threshold(tau) keeps the
@@ -116,7 +116,7 @@ static void softmax_weighted_sum(const double* z, const int32_t* rows, int cnt,
 
 /*
  * One layer of the step (the per-layer body of Algorithm 1 in [Digest 3.4],
- * attention part only), with the selection rule of reading R7 (rule, param).
+ * attention part only), with the selection rule of reading R16 (rule, param).
  *
  *   q        [B, Hq, d]           dtype
  *   kc, vc   [B, Hkv, max_ctx, d] dtype
@@ -193,7 +193,7 @@ int oracle_layer_select(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
                 memcpy(dst, pooled, sizeof(double) * (size_t)n);
             }
             qsort(order, (size_t)n, sizeof(scored), cmp_desc_score_asc_index);
-            int cnt = ke;                                   /* reading R7 */
+            int cnt = ke;                                   /* reading R16 */
             if (rule == ORACLE_RULE_RATIO) {
                 const double t = ceil(param * (double)n);
                 const int kr = t < 1.0 ? 1 : (t > (double)n ? n : (int)t);
@@ -213,7 +213,7 @@ int oracle_layer_select(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
             int bad = 0, cnt = 0;
             int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * (size_t)(ke > 0 ? ke : 1));
             for (int r = 0; r < ke && rows; ++r) {
-                if (s_in[r] == -1) continue;                /* padding (reading R7) */
+                if (s_in[r] == -1) continue;                /* padding (reading R16) */
                 if (s_in[r] < 0 || s_in[r] >= n) bad = 1;
                 else rows[cnt++] = s_in[r];
             }

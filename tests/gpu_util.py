@@ -27,7 +27,7 @@ def make_handle(w: synth.Workload):
     return hhs.Handle(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_ctx, w.k, w.dtype)
 
 
-def run_layer(handle, x, role, S_in_dev, n_ctx_dev, k, *, S_out_dev=None):
+def run_layer(handle, x, role, S_in_dev, n_ctx_dev, k, *, S_out_dev=None, rule="topk", param=0.0):
     """Returns (out_host, S_out_host, S_out_dev)."""
     import torch
     d = handle.dims
@@ -38,7 +38,7 @@ def run_layer(handle, x, role, S_in_dev, n_ctx_dev, k, *, S_out_dev=None):
     if S_out_dev is None:
         S_out_dev = torch.full((d.batch, d.n_kv_heads, k), -7, dtype=torch.int32, device="cuda")
     out = torch.full((d.batch, d.n_q_heads, d.head_dim), float("nan"), dtype=torch.float32, device="cuda")
-    handle.decode_layer(q, kc, vc, role, S_in_dev, S_out_dev, out, n_ctx_dev, k)
+    handle.decode_layer(q, kc, vc, role, S_in_dev, S_out_dev, out, n_ctx_dev, k, rule=rule, param=param)
     torch.cuda.synchronize()
     res = out.cpu().numpy(), S_out_dev.cpu().numpy().copy(), S_out_dev
     del q, kc, vc

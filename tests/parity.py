@@ -9,6 +9,10 @@ Tolerances (stated for the method's parity bar):
     same score on both sides, so where such a group straddles the boundary
     the selected members must be the lowest-indexed ones (checked exactly);
   * S rows are ascending, duplicate-free, inside [0, n), padded with -1.
+  * selection rules (the oracle's reading R16): under the ratio rule the GPU
+    keeps exactly as many tokens as the oracle; under the threshold rule the
+    count may differ only by tokens whose pooled score lies within 1e-3
+    (relative) of tau, which joins the k-th score as a second band.
 The oracle receives the same S_in as the GPU (the GPU's S_out of the previous
 layer), so a tolerated boundary swap upstream cannot move a downstream
 sparse-head output.
@@ -23,8 +27,9 @@ OUT_TOL = {"f32": 1e-4, "bf16": 2e-2}
 BAND_REL = 1e-3
 
 
-def check_S_row(S_gpu_row, n, k):
-    ke = min(k, n)
+def check_S_row(S_gpu_row, n, k, count=None):
+    """A row of S: `count` (default min(k, n)) ascending entries in [0, n), then -1."""
+    ke = min(k, n) if count is None else count
     row = np.asarray(S_gpu_row)
     assert row.shape == (k,)
     assert np.all(row[ke:] == -1), "padding"
@@ -34,7 +39,12 @@ def check_S_row(S_gpu_row, n, k):
     return sel
 
 
-def compare_S(S_gpu, S_or, scores, role, n_ctx, k, ties=None):
+def _band(s, cut):
+    tol = BAND_REL * abs(cut) if abs(cut) >= 1e-6 else 1e-9
+    return np.abs(s - cut) <= tol
+
+
+def compare_S(S_gpu, S_or, scores, role, n_ctx, k, ties=None, rule="topk", param=0.0):
     """Returns the number of band positions that differ (informational)."""
     B, Hkv, _ = S_gpu.shape
     band_diffs = 0
@@ -42,14 +52,23 @@ def compare_S(S_gpu, S_or, scores, role, n_ctx, k, ties=None):
         n = int(n_ctx[b])
         ke = min(k, n)
         for g in range(Hkv):
-            A = check_S_row(S_gpu[b, g], n, k)
             if not role[g]:
-                continue
-            O = S_or[b, g, :ke]
+                continue          # a sparse head forwards S_in (checked by the caller)
+            O = S_or[b, g]
+            O = O[O != -1]
+            if rule == "threshold":
+                # as many as the oracle, give or take tokens in the band around tau
+                cnt = int(np.count_nonzero(S_gpu[b, g] != -1))
+                assert cnt <= ke, f"threshold rule kept {cnt} > min(k, n) = {ke} at b={b} g={g}"
+                A = check_S_row(S_gpu[b, g], n, k, cnt)
+            else:
+                A = check_S_row(S_gpu[b, g], n, k, O.size)
             s = scores[b, g, :n]
-            s_k = s[O].min()
-            tol = BAND_REL * abs(s_k) if abs(s_k) >= 1e-6 else 1e-9
-            band = np.abs(s - s_k) <= tol
+            band = np.zeros(n, bool)
+            if O.size:
+                band |= _band(s, s[O].min())
+            if rule == "threshold" and np.isfinite(param):
+                band |= _band(s, param)
             a_set = set(A.tolist())
             o_set = set(O.tolist())
             a_out = {j for j in a_set if not band[j]}
@@ -68,10 +87,11 @@ def compare_S(S_gpu, S_or, scores, role, n_ctx, k, ties=None):
     return band_diffs
 
 
-def compare_layer(out_gpu, S_gpu, inputs, role, S_in, n_ctx, k, dtype, ties=None, threads=0):
+def compare_layer(out_gpu, S_gpu, inputs, role, S_in, n_ctx, k, dtype, ties=None, threads=0, rule="topk",
+                  param=0.0):
     """Run the oracle on the same inputs and S_in; assert the parity bar."""
     out_or, S_or, scores = oracle.layer(inputs["q"], inputs["k"], inputs["v"], role, S_in, n_ctx, k,
-                                        want_scores=True, threads=threads)
+                                        want_scores=True, threads=threads, rule=rule, param=param)
     err = np.abs(out_gpu.astype(np.float64) - out_or)
     assert np.all(np.isfinite(out_gpu)), "non-finite output"
     assert err.max() <= OUT_TOL[dtype], f"max |out err| {err.max():.3e} > {OUT_TOL[dtype]}"
@@ -79,5 +99,5 @@ def compare_layer(out_gpu, S_gpu, inputs, role, S_in, n_ctx, k, dtype, ties=None
         for g in range(S_gpu.shape[1]):
             if not role[g]:
                 np.testing.assert_array_equal(S_gpu[b, g], S_in[b, g], err_msg="sparse head must forward S")
-    band = compare_S(S_gpu, S_or, scores, role, n_ctx, k, ties)
+    band = compare_S(S_gpu, S_or, scores, role, n_ctx, k, ties, rule, param)
     return float(err.max()), band

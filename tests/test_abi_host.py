@@ -119,3 +119,26 @@ def test_null_handle_is_rejected(lib):
     assert lib.lychee_decode_layer(None, None, None, None, None, None, None, None, None, 1) == hhs.LYCHEE_ERR_INVALID_ARG
     assert lib.lychee_check_device_errors(None) == hhs.LYCHEE_ERR_INVALID_ARG
     lib.lychee_destroy(None)
+
+
+@pytest.mark.parametrize("rule, param, needle", [
+    (3, 0.0, "rule"),
+    (-1, 0.0, "rule"),
+    (hhs.SELECT_RULES["ratio"], 0.0, "theta"),
+    (hhs.SELECT_RULES["ratio"], 1.5, "theta"),
+    (hhs.SELECT_RULES["ratio"], float("nan"), "theta"),
+    (hhs.SELECT_RULES["threshold"], float("nan"), "tau"),
+])
+def test_bad_selection_rules_are_rejected(lib, rule, param, needle):
+    # the rule is checked before the handle, so a NULL handle still reports it
+    st = lib.lychee_decode_layer_select(None, None, None, None, None, None, None, None, None, 1, rule, param)
+    assert st == hhs.LYCHEE_ERR_INVALID_ARG
+    assert needle in lib.lychee_last_error().decode()
+
+
+@pytest.mark.parametrize("rule, param", [(0, 0.0), (1, 1.0), (1, 1e-9), (2, float("inf")), (2, -float("inf")),
+                                         (2, -3.5)])
+def test_valid_selection_rules_reach_the_handle_check(lib, rule, param):
+    st = lib.lychee_decode_layer_select(None, None, None, None, None, None, None, None, None, 1, rule, param)
+    assert st == hhs.LYCHEE_ERR_INVALID_ARG
+    assert "handle" in lib.lychee_last_error().decode()

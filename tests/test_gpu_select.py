@@ -1,0 +1,134 @@
+"""Selection rules other than top-k on the GPU, against the oracle (reading R16
+of the oracle: the ratio and threshold rules of the digest's ablation of
+selection methods, section 4.4.1 / Figure 6).
+
+Each case runs layer 0 (all retrieval) under a rule and a layer 1 with half
+of the KV heads sparse under the same rule, so the sparse heads attend to a
+set padded with -1.  Ragged contexts (one not a multiple of 32) and, at the
+end, a context shorter than k (every token is a candidate) and the 128K
+context (several passes per workgroup) are covered.  Hand-made S_in rows with
+-1 entries anywhere, and a row of padding only, check the sparse path alone."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import log, make_handle, run_layer
+from parity import compare_layer
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = synth.Workload("select_ragged", 31, 2, 2, 32, 8, 128, 16384, 1024, "bf16", 4,
+                        ctx_list=(16384, 9001), hh_frac=0.01)
+SHORT = synth.Workload("select_short", 32, 2, 2, 32, 8, 128, 4096, 4096, "bf16", 4,
+                       ctx_list=(3001, 4096), hh_frac=0.01)
+HALF = np.array([0, 1, 0, 1, 0, 1, 0, 1], np.uint8)
+
+
+def _two_layers(w: synth.Workload, rule: str, param: float, role1=HALF):
+    import torch
+    handle = make_handle(w)
+    lens = synth.n_ctx(w)
+    n_ctx_dev = torch.from_numpy(lens).cuda()
+    role0 = np.ones(w.n_kv_heads, np.uint8)
+    x0 = synth.layer_inputs(w, 0)
+    out0, S0, S0_dev = run_layer(handle, x0, role0, None, n_ctx_dev, w.k, rule=rule, param=param)
+    err0, band0 = compare_layer(out0, S0, x0, role0, None, lens, w.k, w.dtype, rule=rule, param=param)
+    kept = (S0 != -1).sum(axis=2)
+    log(f"[{w.name}] {rule}({param:g}) layer 0: kept per head {kept.min()}..{kept.max()}, "
+        f"max|err|={err0:.2e} band-diffs={band0}")
+    x1 = synth.layer_inputs(w, 1)
+    out1, S1, _ = run_layer(handle, x1, role1, S0_dev, n_ctx_dev, w.k, rule=rule, param=param)
+    err1, band1 = compare_layer(out1, S1, x1, role1, S0, lens, w.k, w.dtype, rule=rule, param=param)
+    log(f"[{w.name}] {rule}({param:g}) layer 1 roles={list(role1)}: max|err|={err1:.2e} band-diffs={band1}")
+    handle.check_device_errors()
+    return S0, out1
+
+
+def _tau_keeping(w: synth.Workload, rank: int) -> float:
+    """A tau between the rank-th and (rank+1)-th pooled scores of layer 0's
+    first head (so about `rank` tokens per head pass it)."""
+    lens = synth.n_ctx(w)
+    x0 = synth.layer_inputs(w, 0)
+    _, _, scores = oracle.layer(x0["q"], x0["k"], x0["v"], np.ones(w.n_kv_heads, np.uint8), None, lens, w.k,
+                                want_scores=True)
+    s = np.sort(scores[0, 0, :int(lens[0])])[::-1]
+    return float(0.5 * (s[rank - 1] + s[rank]))
+
+
+def test_ratio_rule_below_k():
+    # ceil(0.03 n) = 492 and 271 < k = 1024
+    S0, _ = _two_layers(RAGGED, "ratio", 0.03)
+    for b, n in enumerate(synth.n_ctx(RAGGED)):
+        assert np.all((S0[b] != -1).sum(axis=1) == math.ceil(0.03 * int(n)))
+
+
+def test_ratio_rule_above_k_equals_topk():
+    S0, _ = _two_layers(RAGGED, "ratio", 0.5)
+    assert np.all((S0 != -1).sum(axis=2) == RAGGED.k)
+
+
+def test_ratio_rule_whole_context():
+    # theta = 1 and k >= n: every token, in order
+    S0, _ = _two_layers(SHORT, "ratio", 1.0)
+    for b, n in enumerate(synth.n_ctx(SHORT)):
+        assert np.all(S0[b, :, :n] == np.arange(n)) and np.all(S0[b, :, n:] == -1)
+
+
+def test_threshold_rule_below_k():
+    _two_layers(RAGGED, "threshold", _tau_keeping(RAGGED, 300))
+
+
+def test_threshold_rule_bound_by_k():
+    _two_layers(RAGGED, "threshold", _tau_keeping(RAGGED, 6000))
+
+
+def test_threshold_rule_every_token_a_candidate():
+    # k >= n: the threshold alone cuts the set
+    _two_layers(SHORT, "threshold", _tau_keeping(SHORT, 700))
+
+
+def test_threshold_minus_infinity_is_topk_and_plus_infinity_is_empty():
+    S0, _ = _two_layers(RAGGED, "threshold", -math.inf)
+    assert np.all((S0 != -1).sum(axis=2) == RAGGED.k)
+    S0, out1 = _two_layers(RAGGED, "threshold", math.inf)
+    assert np.all(S0 == -1)
+    # the sparse heads of layer 1 attend to nothing: output 0
+    G = RAGGED.group
+    for g in np.nonzero(HALF == 0)[0]:
+        assert np.all(out1[:, g * G:(g + 1) * G, :] == 0.0)
+
+
+def test_ratio_rule_at_128k_context():
+    w = synth.Workload("select_128k", 33, 1, 2, 32, 8, 128, 131072, 4096, "bf16", 4, hh_frac=0.01)
+    _two_layers(w, "ratio", 0.02)
+
+
+def test_sparse_heads_skip_padding_anywhere():
+    import torch
+    w = RAGGED
+    handle = make_handle(w)
+    lens = synth.n_ctx(w)
+    n_ctx_dev = torch.from_numpy(lens).cuda()
+    role0 = np.ones(w.n_kv_heads, np.uint8)
+    x0 = synth.layer_inputs(w, 0)
+    _, S0, _ = run_layer(handle, x0, role0, None, n_ctx_dev, w.k)
+    rng = np.random.default_rng(77)
+    S_in = S0.copy()
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            hole = rng.random(w.k) < 0.3
+            S_in[b, g, hole] = -1
+    S_in[1, 2, :] = -1                  # a sparse head (g = 2) with nothing to attend to
+    S_in_dev = torch.from_numpy(S_in).cuda()
+    x1 = synth.layer_inputs(w, 1)
+    out1, S1, _ = run_layer(handle, x1, HALF, S_in_dev, n_ctx_dev, w.k)
+    err, _ = compare_layer(out1, S1, x1, HALF, S_in, lens, w.k, w.dtype)
+    log(f"[{w.name}] padded S_in: max|err|={err:.2e}")
+    G = w.group
+    assert np.all(out1[1, 2 * G:3 * G, :] == 0.0)
+    handle.check_device_errors()

@@ -310,7 +310,7 @@ def test_oracle_rejects_bad_arguments():
         oracle.step([(q, kc, vc, np.zeros(1, np.uint8))], n_ctx, 4)
 
 
-# ---------------------------------------------------------------- selection rules (reading R7)
+# ---------------------------------------------------------------- selection rules (reading R16)
 
 def _pooled_scores_by_hand(q, kc, b, g, n, G):
     """Mean over the group's G heads of q_h . k_j / sqrt(d), in float64 loops."""
