@@ -30,7 +30,14 @@ Pins (the tests that hold the oracle to something other than itself; all in
   * invariants: constant V rows reproduce the constant; each output lies in
     the per-coordinate hull of V; logit shift and row permutation
     (in)variance; sparse S_out == S_in bitwise; an all-sparse chain returns
-    the layer-0 S bitwise.
+    the layer-0 S bitwise;
+  * selection rules (reading R16 of oracle.c): Ratio equals top-k at
+    k' = ceil(theta n); Threshold matches pooled scores computed in plain
+    loops and reduces to top-k / the empty set at tau = -inf / +inf; Top-p
+    over identical keys keeps ceil(p n) tokens, over a two-level score
+    profile keeps the closed-form count of heavy tokens, keeps the argmax
+    alone for a tiny p and equals top-k at p = 1; a sparse head skips -1
+    padding and outputs zeros for an empty set.
 """
 from __future__ import annotations
 
@@ -91,7 +98,7 @@ def _dtype_code(a: np.ndarray) -> int:
     raise TypeError(f"oracle takes float32 or bf16-as-uint16 arrays, got {a.dtype}")
 
 
-RULES = {"topk": 0, "ratio": 1, "threshold": 2}
+RULES = {"topk": 0, "ratio": 1, "threshold": 2, "topp": 3}
 
 
 def layer(q, k_cache, v_cache, role, S_in, n_ctx, k, *, want_scores=False,
@@ -101,8 +108,10 @@ def layer(q, k_cache, v_cache, role, S_in, n_ctx, k, *, want_scores=False,
     ``rule`` selects S (reading R16 of oracle.c): "topk" (the top min(k, n)),
     "ratio" (the top min(k, ceil(param * n)), param in (0, 1]) or
     "threshold" (the tokens with pooled score >= param, the k highest if
-    more); S rows are ascending and padded with -1, and a sparse head skips
-    -1 entries.
+    more) or "topp" (the shortest prefix of the ranking whose softmax share
+    of the pooled scores reaches param in (0, 1], the k highest if longer);
+    S rows are ascending and padded with -1, and a sparse head skips -1
+    entries.
 
     q: [B,Hq,d]; k_cache, v_cache: [B,Hkv,max_ctx,d] (float32, or uint16
     holding bfloat16 bits); role: [Hkv] (1 retrieval / 0 sparse); S_in:

@@ -39,7 +39,9 @@
  *       tokens whose pooled score (R2) is >= tau, the k highest of them if
  *       more.  S then holds fewer than min(k, n) valid entries, padded with
  *       -1; a sparse head skips -1 entries (an empty set gives output 0).
- *       Top-p is not provided.
+ *       TopP(p) keeps the shortest prefix of that ranking whose share of
+ *       the softmax of the pooled scores over the whole context reaches p
+ *       (the k highest if it is longer); shares are added in rank order.
  *
  * Parity status: pinned (see the header of oracle/__init__.py for the list
  * of pins and the tests that hold them).
@@ -113,6 +115,7 @@ static void softmax_weighted_sum(const double* z, const int32_t* rows, int cnt,
 #define ORACLE_RULE_TOPK 0
 #define ORACLE_RULE_RATIO 1
 #define ORACLE_RULE_THRESHOLD 2
+#define ORACLE_RULE_TOPP 3
 
 /*
  * One layer of the step (the per-layer body of Algorithm 1 in [Digest 3.4],
@@ -136,8 +139,11 @@ int oracle_layer_select(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
                         double* out, const int32_t* n_ctx, int k, int rule, double param,
                         double* scores, int nthreads) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_ctx <= 0 || k <= 0) return ORACLE_ERR_ARG;
-    if (rule != ORACLE_RULE_TOPK && rule != ORACLE_RULE_RATIO && rule != ORACLE_RULE_THRESHOLD) return ORACLE_ERR_ARG;
-    if (rule == ORACLE_RULE_RATIO && !(param > 0.0 && param <= 1.0)) return ORACLE_ERR_ARG;
+    if (rule != ORACLE_RULE_TOPK && rule != ORACLE_RULE_RATIO && rule != ORACLE_RULE_THRESHOLD &&
+        rule != ORACLE_RULE_TOPP)
+        return ORACLE_ERR_ARG;
+    if ((rule == ORACLE_RULE_RATIO || rule == ORACLE_RULE_TOPP) && !(param > 0.0 && param <= 1.0))
+        return ORACLE_ERR_ARG;
     if (Hq % Hkv != 0 || (dtype != 0 && dtype != 1)) return ORACLE_ERR_ARG;
     if (!q || !kc || !vc || !role || !S_out || !out || !n_ctx) return ORACLE_ERR_ARG;
     for (int g = 0; g < Hkv; ++g)
@@ -201,6 +207,20 @@ int oracle_layer_select(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
             } else if (rule == ORACLE_RULE_THRESHOLD) {
                 cnt = 0;
                 while (cnt < ke && order[cnt].s >= param) ++cnt;
+            } else if (rule == ORACLE_RULE_TOPP) {
+                /* softmax of the pooled scores over all n tokens, shares added
+                 * in rank order until they reach p */
+                const double m = order[0].s;
+                double Z = 0.0;
+                for (int j = 0; j < n; ++j) Z += exp(pooled[j] - m);
+                double cum = 0.0;
+                for (int r = 0; r < ke; ++r) {
+                    cum += exp(order[r].s - m) / Z;
+                    if (cum >= param) {
+                        cnt = r + 1;
+                        break;
+                    }
+                }
             }
             for (int r = 0; r < cnt; ++r) s_out[r] = order[r].j;
             qsort(s_out, (size_t)cnt, sizeof(int32_t), cmp_int_asc);

@@ -395,3 +395,67 @@ def test_sparse_head_skips_padding_and_empty_set_gives_zero():
     S_empty = np.full((1, Hkv, k), -1, np.int32)
     out_e, _, _ = oracle.layer(q, kc, vc, sparse, S_empty, n_ctx, k)
     assert np.all(out_e == 0.0)
+
+
+def test_topp_rule_identical_keys_keeps_ceil_p_n():
+    """Identical keys: every pooled share is 1/n, so Top-p keeps ceil(p n)
+    tokens, the lowest indices (ties), for p n away from an integer."""
+    rng = np.random.default_rng(34)
+    G, Hkv, d, n = 2, 1, 16, 200
+    q, kc, vc, n_ctx = _f32_case(rng, 1, G * Hkv, Hkv, d, n)
+    kc[0, 0, :] = kc[0, 0, 7]
+    for p, r in ((0.3025, 61), (0.0001, 1), (0.9975, 200)):
+        _, S, _ = oracle.layer(q, kc, vc, np.ones(Hkv, np.uint8), None, n_ctx, 256, rule="topp", param=p)
+        np.testing.assert_array_equal(S[0, 0, :r], np.arange(r), err_msg=f"p={p}")
+        assert np.all(S[0, 0, r:] == -1), f"p={p}"
+
+
+def test_topp_rule_two_level_profile_closed_form():
+    """m heavy tokens with pooled score a, n - m light ones with score 0: each
+    heavy share is e^a / Z and each light share 1 / Z with Z = m e^a + n - m,
+    so Top-p keeps ceil(p Z / e^a) heavy tokens (lowest indices first), or all
+    m heavy plus ceil((p - m e^a / Z) Z) light ones (lowest indices)."""
+    d, n = 16, 120
+    heavy = np.array([5, 17, 40, 41, 99])
+    m = heavy.size
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 8.0
+    kc = np.zeros((1, 1, n, d), np.float32)
+    kc[0, 0, :, 1] = 1.0                      # light rows: orthogonal to q, score 0
+    kc[0, 0, heavy, 1] = 0.0
+    kc[0, 0, heavy, 0] = 1.0                  # heavy rows: score 8 / sqrt(16) = 2
+    vc = np.random.default_rng(35).standard_normal((1, 1, n, d)).astype(np.float32)
+    n_ctx = np.array([n], np.int32)
+    a = 2.0
+    Z = m * math.exp(a) + (n - m)
+    light = np.setdiff1d(np.arange(n), heavy)
+    for p in (0.1, 0.2, 0.25, 0.3):
+        x = p * Z / math.exp(a)
+        if x <= m:
+            assert abs(x - round(x)) > 1e-3
+            keep = heavy[:math.ceil(x)]
+        else:
+            y = (p - m * math.exp(a) / Z) * Z
+            assert abs(y - round(y)) > 1e-3
+            keep = np.concatenate([heavy, light[:math.ceil(y)]])
+        _, S, _ = oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, n_ctx, 64, rule="topp", param=p)
+        np.testing.assert_array_equal(S[0, 0, :keep.size], np.sort(keep), err_msg=f"p={p}")
+        assert np.all(S[0, 0, keep.size:] == -1), f"p={p}"
+
+
+def test_topp_rule_limits():
+    """A tiny p keeps the argmax alone (top-1); p = 1 with k < n is capped by
+    k (the shares of the other n - k tokens keep the sum below 1): top-k."""
+    rng = np.random.default_rng(36)
+    G, Hkv, d, n, k = 4, 2, 32, 100, 40
+    q, kc, vc, n_ctx = _f32_case(rng, 1, Hkv * G, Hkv, d, n)
+    ones = np.ones(Hkv, np.uint8)
+    _, S_p, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, k, rule="topp", param=1e-12)
+    _, S_1, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, 1)
+    np.testing.assert_array_equal(S_p[:, :, :1], S_1)
+    assert np.all(S_p[:, :, 1:] == -1)
+    _, S_p, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, k, rule="topp", param=1.0)
+    _, S_k, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, k)
+    np.testing.assert_array_equal(S_p, S_k)
+    with pytest.raises(ValueError):
+        oracle.layer(q, kc, vc, ones, None, n_ctx, k, rule="topp", param=0.0)
