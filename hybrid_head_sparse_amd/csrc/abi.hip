@@ -11,6 +11,7 @@
 
 #include "../../include/lychee.h"
 #include "common.hpp"
+#include "topp.hpp"
 
 using namespace lychee;
 
@@ -254,6 +255,26 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
     hipError_t e = launch_attend(ap, d.dtype, d.head_dim, G, hybrid, h->cus, h->per_cu, h->stream);
     if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+    if (hybrid && rule == LYCHEE_SELECT_TOPP) {
+        // the attention kernel wrote the top-min(k, n) sets; cut them to the Top-p prefix
+        TopPParams tp{};
+        tp.S = S_out;
+        tp.score = h->ws.score;
+        tp.comp = h->ws.cand;
+        tp.rec = h->ws.prec;
+        tp.ctr = h->ws.pctr;
+        tp.n_ctx = n_ctx;
+        tp.err = h->ws.err;
+        tp.role_bits = bits;
+        tp.B = d.batch;
+        tp.Hkv = d.n_kv_heads;
+        tp.max_ctx = d.max_ctx;
+        tp.k = k;
+        tp.c_log2 = (float)(1.4426950408889634 / ((double)G * std::sqrt((double)d.head_dim)));
+        tp.P = (unsigned long long)(param * 0x1p52);
+        e = launch_topp_trim(tp, h->stream);
+        if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "Top-p trim launch failed: %s", hipGetErrorString(e));
+    }
     if (h->ev_stop && hipEventRecord(h->ev_stop, h->stream) != hipSuccess)
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
     return ok();
@@ -273,10 +294,14 @@ lychee_status lychee_decode_layer_select(lychee_handle* h, const void* q, const 
                                          int32_t* S_out, float* out, const int32_t* n_ctx, int32_t k, int32_t rule,
                                          double param) {
     // the rule is checked first (host-only, so it can be checked without a device)
-    if (rule != LYCHEE_SELECT_TOPK && rule != LYCHEE_SELECT_RATIO && rule != LYCHEE_SELECT_THRESHOLD)
-        return fail(LYCHEE_ERR_INVALID_ARG, "rule must be LYCHEE_SELECT_TOPK, _RATIO or _THRESHOLD (got %d)", rule);
+    if (rule != LYCHEE_SELECT_TOPK && rule != LYCHEE_SELECT_RATIO && rule != LYCHEE_SELECT_THRESHOLD &&
+        rule != LYCHEE_SELECT_TOPP)
+        return fail(LYCHEE_ERR_INVALID_ARG, "rule must be LYCHEE_SELECT_TOPK, _RATIO, _THRESHOLD or _TOPP (got %d)",
+                    rule);
     if (rule == LYCHEE_SELECT_RATIO && !(param > 0.0 && param <= 1.0))
         return fail(LYCHEE_ERR_INVALID_ARG, "the ratio rule's theta must be in (0, 1] (got %g)", param);
+    if (rule == LYCHEE_SELECT_TOPP && !(param > 0.0 && param <= 1.0))
+        return fail(LYCHEE_ERR_INVALID_ARG, "the Top-p rule's p must be in (0, 1] (got %g)", param);
     if (rule == LYCHEE_SELECT_THRESHOLD && std::isnan(param))
         return fail(LYCHEE_ERR_INVALID_ARG, "the threshold rule's tau is NaN");
     if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");

@@ -52,6 +52,9 @@ constexpr int kResolveSlices = 8;
 constexpr unsigned long long kSelArrival = 1ull << 32;
 constexpr unsigned long long kSelFreeArrival = 1ull << 48;
 static_assert(kMaxWG < (1 << 16) && kMaxCtx <= (1ll << 32), "selection counter fields");
+// Workgroups per retrieval head of the Top-p trim kernel (each sums a slice
+// of the softmax normaliser; the last to arrive cuts the set).
+constexpr int kTopPSplit = 16;
 
 // Cross-workgroup hand-off without cache-wide maintenance.  Data one
 // workgroup leaves for another inside the same launch is written with
@@ -97,7 +100,9 @@ struct Workspace {
     float* rec2;                 // [BH * kLevel2Max * RS]    level-2 partial records
     unsigned long long* cand;    // [BH * max_ctx]            selection candidates (key | index << 32)
     uint32_t* score;             // [BH * max_ctx]            every selection key of a retrieval head
-                                 //                           (read only when a head's bounds fail)
+                                 //                           (read when a head's bounds fail, and by
+                                 //                           the Top-p trim)
+    unsigned long long* prec;    // [BH * kTopPSplit * 2]     Top-p trim: per-slice normaliser partials
     // ---- zero-initialised region (restored to zero by every call) ----
     uint32_t* cnt1;              // [BH * kLevel2Max]         level-1 arrival counters
     uint32_t* cnt2;              // [BH]                      level-2 arrival counters
@@ -110,6 +115,7 @@ struct Workspace {
     uint32_t* rdone;             // [BH]                      slices whose resolver has read the head's
                                  //                           histogram and counters
     uint32_t* hist;              // [BH * kHistBins]          first-digit counts from each pass's bound up
+    uint32_t* pctr;              // [BH]                      Top-p trim: slices done
     uint32_t* err;               // [4]
     void* zero_begin;
     size_t zero_bytes;
@@ -136,6 +142,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_rec2 = take(sizeof(float) * (size_t)BH * kLevel2Max * RS);
     size_t o_cand = take(sizeof(unsigned long long) * (size_t)BH * max_ctx);
     size_t o_score = take(sizeof(uint32_t) * (size_t)BH * max_ctx);
+    size_t o_prec = take(sizeof(unsigned long long) * (size_t)BH * kTopPSplit * 2);
     size_t z0 = off;
     size_t o_cnt1 = take(sizeof(uint32_t) * (size_t)BH * kLevel2Max);
     size_t o_cnt2 = take(sizeof(uint32_t) * (size_t)BH);
@@ -144,6 +151,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_rclaim = take(sizeof(uint32_t) * (size_t)BH * kResolveSlices);
     size_t o_rdone = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_hist = take(sizeof(uint32_t) * (size_t)BH * kHistBins);
+    size_t o_pctr = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_err = take(sizeof(uint32_t) * 4);
     Workspace w{};
     char* p = (char*)base;
@@ -154,6 +162,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.rec2 = (float*)(p + o_rec2);
         w.cand = (unsigned long long*)(p + o_cand);
         w.score = (uint32_t*)(p + o_score);
+        w.prec = (unsigned long long*)(p + o_prec);
         w.cnt1 = (uint32_t*)(p + o_cnt1);
         w.cnt2 = (uint32_t*)(p + o_cnt2);
         w.selctr = (unsigned long long*)(p + o_sc);
@@ -161,6 +170,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.rclaim = (uint32_t*)(p + o_rclaim);
         w.rdone = (uint32_t*)(p + o_rdone);
         w.hist = (uint32_t*)(p + o_hist);
+        w.pctr = (uint32_t*)(p + o_pctr);
         w.err = (uint32_t*)(p + o_err);
         w.zero_begin = p + z0;
     }

@@ -121,16 +121,23 @@ lychee_status lychee_decode_layer(lychee_handle* h,
  *              there are more.  The kernel compares the fp32 sum over the G
  *              heads of q . k_j with tau G sqrt(d) rounded to fp32, so a score
  *              within fp32 rounding of tau may fall on either side.
+ *   TOPP       the shortest prefix of the ranking whose share of softmax(s)
+ *              over all n tokens reaches p = param in (0, 1], at most
+ *              min(k, n) tokens.  Shares are fp32 exponentials over an fp64
+ *              normaliser, summed as 52-bit fixed point, so a cut within that
+ *              rounding of p may land one token either side.  Runs a second
+ *              kernel after the attention kernel.
  * Ties go to the lower index under every rule. */
-enum { LYCHEE_SELECT_TOPK = 0, LYCHEE_SELECT_RATIO = 1, LYCHEE_SELECT_THRESHOLD = 2 };
+enum { LYCHEE_SELECT_TOPK = 0, LYCHEE_SELECT_RATIO = 1, LYCHEE_SELECT_THRESHOLD = 2, LYCHEE_SELECT_TOPP = 3 };
 
 /* lychee_decode_layer with a selection rule for the retrieval heads (above).
  * A retrieval row of S_out holds its selected tokens ascending, then -1 up to
  * k; a later sparse head skips the -1 entries.  Arguments as for
  * lychee_decode_layer, plus `rule` (a LYCHEE_SELECT_* value) and `param`
- * (theta for RATIO, tau for THRESHOLD, unused for TOPK).  Returns
- * LYCHEE_ERR_INVALID_ARG for an unknown rule, theta outside (0, 1] or a NaN
- * tau, after which nothing is enqueued. */
+ * (theta for RATIO, tau for THRESHOLD, p for TOPP, unused for TOPK).
+ * Returns LYCHEE_ERR_INVALID_ARG for an unknown rule, theta or p outside
+ * (0, 1] or a NaN tau, after which nothing is enqueued.  With profile events
+ * set, `stop` follows the Top-p kernel. */
 lychee_status lychee_decode_layer_select(lychee_handle* h,
                                          const void* q, const void* k_cache, const void* v_cache,
                                          const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out,

@@ -12,7 +12,11 @@ Tolerances (stated for the method's parity bar):
   * selection rules (the oracle's reading R16): under the ratio rule the GPU
     keeps exactly as many tokens as the oracle; under the threshold rule the
     count may differ only by tokens whose pooled score lies within 1e-3
-    (relative) of tau, which joins the k-th score as a second band.
+    (relative) of tau, which joins the k-th score as a second band; under
+    the Top-p rule the GPU's count c must be a valid cut of the oracle's
+    cumulative shares to within 1e-5 (the top c - 1 shares sum to less
+    than p + 1e-5 and the top c to at least p - 1e-5, or c = min(k, n)),
+    and its set must be the oracle's top c up to the band at its own cut.
 The oracle receives the same S_in as the GPU (the GPU's S_out of the previous
 layer), so a tolerated boundary swap upstream cannot move a downstream
 sparse-head output.
@@ -25,6 +29,7 @@ import oracle
 
 OUT_TOL = {"f32": 1e-4, "bf16": 2e-2}
 BAND_REL = 1e-3
+TOPP_TOL = 1e-5
 
 
 def check_S_row(S_gpu_row, n, k, count=None):
@@ -56,10 +61,24 @@ def compare_S(S_gpu, S_or, scores, role, n_ctx, k, ties=None, rule="topk", param
                 continue          # a sparse head forwards S_in (checked by the caller)
             O = S_or[b, g]
             O = O[O != -1]
+            if rule == "topp":
+                cnt = int(np.count_nonzero(S_gpu[b, g] != -1))
+                assert 1 <= cnt <= ke, f"Top-p kept {cnt} of min(k, n) = {ke} at b={b} g={g}"
+                s = scores[b, g, :n]
+                order = np.lexsort((np.arange(n), -s))          # score desc, index asc
+                sh = np.exp(s - s.max())
+                cum = np.cumsum(sh[order] / sh.sum())
+                assert cnt == ke or cum[cnt - 1] >= param - TOPP_TOL, \
+                    f"Top-p stopped early at b={b} g={g}: {cnt} tokens hold {cum[cnt - 1]:.8f} < p = {param}"
+                assert cnt == 1 or cum[cnt - 2] < param + TOPP_TOL, \
+                    f"Top-p stopped late at b={b} g={g}: {cnt - 1} tokens already hold {cum[cnt - 2]:.8f}"
+                O = order[:cnt]                                  # the oracle's top-cnt
             if rule == "threshold":
                 # as many as the oracle, give or take tokens in the band around tau
                 cnt = int(np.count_nonzero(S_gpu[b, g] != -1))
                 assert cnt <= ke, f"threshold rule kept {cnt} > min(k, n) = {ke} at b={b} g={g}"
+                A = check_S_row(S_gpu[b, g], n, k, cnt)
+            elif rule == "topp":
                 A = check_S_row(S_gpu[b, g], n, k, cnt)
             else:
                 A = check_S_row(S_gpu[b, g], n, k, O.size)

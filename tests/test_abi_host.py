@@ -128,6 +128,9 @@ def test_null_handle_is_rejected(lib):
     (hhs.SELECT_RULES["ratio"], 1.5, "theta"),
     (hhs.SELECT_RULES["ratio"], float("nan"), "theta"),
     (hhs.SELECT_RULES["threshold"], float("nan"), "tau"),
+    (hhs.SELECT_RULES["topp"], 0.0, "p must"),
+    (hhs.SELECT_RULES["topp"], 1.0000001, "p must"),
+    (4, 0.5, "rule"),
 ])
 def test_bad_selection_rules_are_rejected(lib, rule, param, needle):
     # the rule is checked before the handle, so a NULL handle still reports it
@@ -137,7 +140,7 @@ def test_bad_selection_rules_are_rejected(lib, rule, param, needle):
 
 
 @pytest.mark.parametrize("rule, param", [(0, 0.0), (1, 1.0), (1, 1e-9), (2, float("inf")), (2, -float("inf")),
-                                         (2, -3.5)])
+                                         (2, -3.5), (3, 1.0), (3, 1e-12)])
 def test_valid_selection_rules_reach_the_handle_check(lib, rule, param):
     st = lib.lychee_decode_layer_select(None, None, None, None, None, None, None, None, None, 1, rule, param)
     assert st == hhs.LYCHEE_ERR_INVALID_ARG

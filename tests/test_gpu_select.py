@@ -1,6 +1,6 @@
 """Selection rules other than top-k on the GPU, against the oracle (reading R16
-of the oracle: the ratio and threshold rules of the digest's ablation of
-selection methods, section 4.4.1 / Figure 6).
+of the oracle: the ratio, threshold and Top-p rules of the digest's ablation
+of selection methods, section 4.4.1 / Figure 6).
 
 Each case runs layer 0 (all retrieval) under a rule and a layer 1 with half
 of the KV heads sparse under the same rule, so the sparse heads attend to a
@@ -132,3 +132,31 @@ def test_sparse_heads_skip_padding_anywhere():
     G = w.group
     assert np.all(out1[1, 2 * G:3 * G, :] == 0.0)
     handle.check_device_errors()
+
+
+# Top-p needs logits large enough for the pooled softmax to concentrate:
+# q, K ~ N(0, 1) (unscaled) with 1% heavy hitters
+LOUD = synth.Workload("select_topp", 34, 2, 2, 32, 8, 128, 16384, 4096, "bf16", 4,
+                      ctx_list=(16384, 9001), qk_scaled=False, hh_frac=0.01)
+LOUD_SHORT = synth.Workload("select_topp_short", 35, 2, 2, 32, 8, 128, 4096, 4096, "bf16", 4,
+                            ctx_list=(3001, 4096), qk_scaled=False, hh_frac=0.01)
+
+
+@pytest.mark.parametrize("p", [0.05, 0.3, 0.6])
+def test_topp_rule(p):
+    S0, _ = _two_layers(LOUD, "topp", p)
+    kept = (S0 != -1).sum(axis=2)
+    assert kept.min() >= 1 and kept.max() <= LOUD.k
+
+
+def test_topp_rule_limits():
+    # a tiny p keeps the argmax alone; p = 1 keeps min(k, n)
+    S0, _ = _two_layers(LOUD, "topp", 1e-12)
+    assert np.all((S0 != -1).sum(axis=2) == 1)
+    S0, _ = _two_layers(LOUD, "topp", 1.0)
+    assert np.all((S0 != -1).sum(axis=2) == LOUD.k)
+
+
+def test_topp_rule_every_token_a_candidate():
+    # k >= n: the shares of the whole context decide alone
+    _two_layers(LOUD_SHORT, "topp", 0.4)
