@@ -37,7 +37,11 @@ Pins (the tests that hold the oracle to something other than itself; all in
     over identical keys keeps ceil(p n) tokens, over a two-level score
     profile keeps the closed-form count of heavy tokens, keeps the argmax
     alone for a tiny p and equals top-k at p = 1; a sparse head skips -1
-    padding and outputs zeros for an empty set.
+    padding and outputs zeros for an empty set;
+  * block selection (reading R17): blocks of one token are top-k; planted
+    heavy tokens pick their blocks in closed form, ties between blocks go
+    to the lower block; a short last block and k covering every block list
+    all tokens.
 """
 from __future__ import annotations
 
@@ -98,7 +102,7 @@ def _dtype_code(a: np.ndarray) -> int:
     raise TypeError(f"oracle takes float32 or bf16-as-uint16 arrays, got {a.dtype}")
 
 
-RULES = {"topk": 0, "ratio": 1, "threshold": 2, "topp": 3}
+RULES = {"topk": 0, "ratio": 1, "threshold": 2, "topp": 3, "block": 4}
 
 
 def layer(q, k_cache, v_cache, role, S_in, n_ctx, k, *, want_scores=False,
@@ -108,10 +112,11 @@ def layer(q, k_cache, v_cache, role, S_in, n_ctx, k, *, want_scores=False,
     ``rule`` selects S (reading R16 of oracle.c): "topk" (the top min(k, n)),
     "ratio" (the top min(k, ceil(param * n)), param in (0, 1]) or
     "threshold" (the tokens with pooled score >= param, the k highest if
-    more) or "topp" (the shortest prefix of the ranking whose softmax share
-    of the pooled scores reaches param in (0, 1], the k highest if longer);
-    S rows are ascending and padded with -1, and a sparse head skips -1
-    entries.
+    more), "topp" (the shortest prefix of the ranking whose softmax share
+    of the pooled scores reaches param in (0, 1], the k highest if longer)
+    or "block" (blocks of param tokens scored by their largest pooled score,
+    the floor(k / param) highest kept, reading R17); S rows are ascending
+    and padded with -1, and a sparse head skips -1 entries.
 
     q: [B,Hq,d]; k_cache, v_cache: [B,Hkv,max_ctx,d] (float32, or uint16
     holding bfloat16 bits); role: [Hkv] (1 retrieval / 0 sparse); S_in:

@@ -42,6 +42,12 @@
  *       TopP(p) keeps the shortest prefix of that ranking whose share of
  *       the softmax of the pooled scores over the whole context reaches p
  *       (the k highest if it is longer); shares are added in rank order.
+ *   R17 block-granular selection (the digest's block size 64 of the kernel,
+ *       with no rule for a block's score): the context is cut into blocks
+ *       of bs tokens (the last one may be shorter); a block's score is the
+ *       largest pooled score (R2) of its tokens; the floor(k / bs) highest
+ *       blocks (score desc, block index asc; all blocks if fewer) are kept,
+ *       and S lists their tokens ascending, padded with -1.
  *
  * Parity status: pinned (see the header of oracle/__init__.py for the list
  * of pins and the tests that hold them).
@@ -116,6 +122,7 @@ static void softmax_weighted_sum(const double* z, const int32_t* rows, int cnt,
 #define ORACLE_RULE_RATIO 1
 #define ORACLE_RULE_THRESHOLD 2
 #define ORACLE_RULE_TOPP 3
+#define ORACLE_RULE_BLOCK 4
 
 /*
  * One layer of the step (the per-layer body of Algorithm 1 in [Digest 3.4],
@@ -140,7 +147,9 @@ int oracle_layer_select(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
                         double* scores, int nthreads) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_ctx <= 0 || k <= 0) return ORACLE_ERR_ARG;
     if (rule != ORACLE_RULE_TOPK && rule != ORACLE_RULE_RATIO && rule != ORACLE_RULE_THRESHOLD &&
-        rule != ORACLE_RULE_TOPP)
+        rule != ORACLE_RULE_TOPP && rule != ORACLE_RULE_BLOCK)
+        return ORACLE_ERR_ARG;
+    if (rule == ORACLE_RULE_BLOCK && !(param >= 1.0 && param <= 4096.0 && param == floor(param) && k >= (int)param))
         return ORACLE_ERR_ARG;
     if ((rule == ORACLE_RULE_RATIO || rule == ORACLE_RULE_TOPP) && !(param > 0.0 && param <= 1.0))
         return ORACLE_ERR_ARG;
@@ -197,6 +206,38 @@ int oracle_layer_select(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
             if (scores) {
                 double* dst = scores + ((size_t)b * Hkv + g) * (size_t)max_ctx;
                 memcpy(dst, pooled, sizeof(double) * (size_t)n);
+            }
+            if (rule == ORACLE_RULE_BLOCK) {
+                /* reading R17: blocks of bs tokens, each scored by its largest
+                 * pooled score; the floor(k / bs) highest blocks, their tokens
+                 * listed ascending */
+                const int bs = (int)param;
+                const int nb = (n + bs - 1) / bs;
+                const int kb = k / bs < nb ? k / bs : nb;
+                int32_t* blocks = (int32_t*)malloc(sizeof(int32_t) * (size_t)(kb > 0 ? kb : 1));
+                if (!blocks) {
+                    free(z); free(pooled); free(order);
+#pragma omp atomic write
+                    status = ORACLE_ERR_MEM;
+                    continue;
+                }
+                for (int blk = 0; blk < nb; ++blk) {
+                    double m = pooled[blk * bs];
+                    for (int j = blk * bs + 1; j < n && j < blk * bs + bs; ++j)
+                        if (pooled[j] > m) m = pooled[j];
+                    order[blk].s = m;
+                    order[blk].j = blk;
+                }
+                qsort(order, (size_t)nb, sizeof(scored), cmp_desc_score_asc_index);
+                for (int r = 0; r < kb; ++r) blocks[r] = order[r].j;
+                qsort(blocks, (size_t)kb, sizeof(int32_t), cmp_int_asc);
+                int w = 0;
+                for (int r = 0; r < kb; ++r)
+                    for (int j = blocks[r] * bs; j < n && j < blocks[r] * bs + bs; ++j) s_out[w++] = j;
+                for (int r = w; r < k; ++r) s_out[r] = -1;
+                free(blocks);
+                free(z); free(pooled); free(order);
+                continue;
             }
             qsort(order, (size_t)n, sizeof(scored), cmp_desc_score_asc_index);
             int cnt = ke;                                   /* reading R16 */

@@ -459,3 +459,54 @@ def test_topp_rule_limits():
     np.testing.assert_array_equal(S_p, S_k)
     with pytest.raises(ValueError):
         oracle.layer(q, kc, vc, ones, None, n_ctx, k, rule="topp", param=0.0)
+
+
+# ---------------------------------------------------------------- block-granular selection (reading R17)
+
+def test_block_rule_with_one_token_blocks_is_topk():
+    rng = np.random.default_rng(37)
+    G, Hkv, d, n, k = 4, 2, 32, 150, 24
+    q, kc, vc, n_ctx = _f32_case(rng, 1, Hkv * G, Hkv, d, n)
+    ones = np.ones(Hkv, np.uint8)
+    _, S_b, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, k, rule="block", param=1)
+    _, S_k, _ = oracle.layer(q, kc, vc, ones, None, n_ctx, k)
+    np.testing.assert_array_equal(S_b, S_k)
+
+
+def test_block_rule_planted_maxima_closed_form():
+    """Light tokens score 0 (K orthogonal to q); planted tokens score 2, 1.5,
+    1.5 (a tie between two blocks) and 1 in known blocks of 8.  With
+    floor(k / 8) = 3 blocks kept: the block of the 2, then of the tied 1.5s
+    the two of them, i.e. blocks {5, 1, 9} - the 1's block (3) is out; with
+    2 blocks the tie goes to the lower block (1 before 9)."""
+    d, n, bs = 16, 84, 8                      # 11 blocks, the last one 4 tokens long
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 4.0
+    kc = np.zeros((1, 1, n, d), np.float32)
+    kc[0, 0, :, 1] = 1.0
+    plant = {43: 2.0, 12: 1.5, 77: 1.5, 30: 1.0}   # token -> score (blocks 5, 1, 9, 3)
+    for j, sc in plant.items():
+        kc[0, 0, j, 1] = 0.0
+        kc[0, 0, j, 0] = sc                   # score = 4 * sc / sqrt(16) = sc
+    vc = np.random.default_rng(38).standard_normal((1, 1, n, d)).astype(np.float32)
+    n_ctx = np.array([n], np.int32)
+    for k, blocks in ((24, [1, 5, 9]), (16, [1, 5]), (31, [1, 5, 9]), (32, [1, 3, 5, 9])):
+        _, S, _ = oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, n_ctx, k, rule="block", param=bs)
+        want = np.concatenate([np.arange(b * bs, min(n, b * bs + bs)) for b in blocks])
+        np.testing.assert_array_equal(S[0, 0, :want.size], want, err_msg=f"k={k}")
+        assert np.all(S[0, 0, want.size:] == -1), f"k={k}"
+    # the short last block (tokens 80..83) scores 0 like the other light blocks
+    # and, tied with them, comes last: it is kept only when every block is
+    _, S, _ = oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, n_ctx, 88, rule="block", param=bs)
+    np.testing.assert_array_equal(S[0, 0, :n], np.arange(n))
+    assert np.all(S[0, 0, n:] == -1)
+    _, S, _ = oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, n_ctx, 80, rule="block", param=bs)
+    np.testing.assert_array_equal(S[0, 0, :80], np.arange(80))
+
+
+def test_block_rule_rejects_bad_block_sizes():
+    rng = np.random.default_rng(39)
+    q, kc, vc, n_ctx = _f32_case(rng, 1, 2, 1, 16, 40)
+    for bs in (0, 2.5, 64):                   # 64 > k = 32
+        with pytest.raises(ValueError):
+            oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, n_ctx, 32, rule="block", param=bs)
