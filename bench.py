@@ -6,7 +6,7 @@ resident in HBM, captured once into a HIP graph and replayed.  Reported next
 to the dense all-heads decode step on the same GPU and the CPU oracle.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama3_128k]
-                    [--rule topk|ratio|threshold|topp --param P]
+                    [--rule topk|ratio|threshold|topp|block --param P]
 
 Prints one JSON line.  Algorithmic bytes per step (what the method must move;
 workspace traffic excluded):
@@ -129,9 +129,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--rule", default="topk", choices=["topk", "ratio", "threshold", "topp"],
+    ap.add_argument("--rule", default="topk", choices=["topk", "ratio", "threshold", "topp", "block"],
                     help="selection rule of the retrieval heads (default: top-k, the headline)")
-    ap.add_argument("--param", type=float, default=0.0, help="theta of the ratio rule, tau of the threshold rule, p of the Top-p rule")
+    ap.add_argument("--param", type=float, default=0.0, help="theta of the ratio rule, tau of the threshold rule, p of the Top-p rule, the block size of the block rule")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

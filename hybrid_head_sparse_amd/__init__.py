@@ -31,7 +31,7 @@ LYCHEE_ERR_WORKSPACE = -4
 LYCHEE_ERR_DEVICE_CHECK = -5
 LYCHEE_F32 = 0
 LYCHEE_BF16 = 1
-SELECT_RULES = {"topk": 0, "ratio": 1, "threshold": 2, "topp": 3}   # LYCHEE_SELECT_*
+SELECT_RULES = {"topk": 0, "ratio": 1, "threshold": 2, "topp": 3, "block": 4}   # LYCHEE_SELECT_*
 
 EXPORTED = (
     "lychee_workspace_bytes", "lychee_create", "lychee_decode_layer", "lychee_decode_layer_select",
@@ -177,8 +177,8 @@ class Handle:
 
         ``rule`` picks the retrieval heads' selection ("topk", "ratio" with
         theta = ``param``, "threshold" with tau = ``param``, "topp" with
-        p = ``param``); anything but "topk" goes through
-        lychee_decode_layer_select."""
+        p = ``param``, "block" with the block size ``param``); anything but
+        "topk" goes through lychee_decode_layer_select."""
         if rule not in SELECT_RULES:
             raise ValueError(f"unknown selection rule {rule!r}; expected one of {sorted(SELECT_RULES)}")
         d = self.dims

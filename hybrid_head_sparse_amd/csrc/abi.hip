@@ -11,7 +11,7 @@
 
 #include "../../include/lychee.h"
 #include "common.hpp"
-#include "topp.hpp"
+#include "rules.hpp"
 
 using namespace lychee;
 
@@ -246,6 +246,7 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
     ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
     const int G = d.n_q_heads / d.n_kv_heads;
     ap.sel_ratio = rule == LYCHEE_SELECT_RATIO ? param : 1.0;
+    ap.sel_keys_only = hybrid && rule == LYCHEE_SELECT_BLOCK ? 1u : 0u;
     // The kernel's selection key is the fp32 sum of the G query heads' raw
     // dot products, i.e. G sqrt(d) times the pooled score: tau maps there.
     ap.sel_tkey = rule == LYCHEE_SELECT_THRESHOLD
@@ -255,9 +256,10 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
     hipError_t e = launch_attend(ap, d.dtype, d.head_dim, G, hybrid, h->cus, h->per_cu, h->stream);
     if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-    if (hybrid && rule == LYCHEE_SELECT_TOPP) {
-        // the attention kernel wrote the top-min(k, n) sets; cut them to the Top-p prefix
-        TopPParams tp{};
+    if (hybrid && (rule == LYCHEE_SELECT_TOPP || rule == LYCHEE_SELECT_BLOCK)) {
+        // the attention kernel wrote the top-min(k, n) sets and every key:
+        // cut the sets to their Top-p prefix, or select blocks instead
+        RuleParams tp{};
         tp.S = S_out;
         tp.score = h->ws.score;
         tp.comp = h->ws.cand;
@@ -270,10 +272,12 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
         tp.Hkv = d.n_kv_heads;
         tp.max_ctx = d.max_ctx;
         tp.k = k;
+        tp.mode = rule == LYCHEE_SELECT_TOPP ? kRuleTopP : kRuleBlock;
+        tp.block = rule == LYCHEE_SELECT_BLOCK ? (int32_t)param : 0;
         tp.c_log2 = (float)(1.4426950408889634 / ((double)G * std::sqrt((double)d.head_dim)));
-        tp.P = (unsigned long long)(param * 0x1p52);
-        e = launch_topp_trim(tp, h->stream);
-        if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "Top-p trim launch failed: %s", hipGetErrorString(e));
+        tp.P = rule == LYCHEE_SELECT_TOPP ? (unsigned long long)(param * 0x1p52) : 0ull;
+        e = launch_rule_select(tp, h->stream);
+        if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "rule selection launch failed: %s", hipGetErrorString(e));
     }
     if (h->ev_stop && hipEventRecord(h->ev_stop, h->stream) != hipSuccess)
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
@@ -295,13 +299,20 @@ lychee_status lychee_decode_layer_select(lychee_handle* h, const void* q, const 
                                          double param) {
     // the rule is checked first (host-only, so it can be checked without a device)
     if (rule != LYCHEE_SELECT_TOPK && rule != LYCHEE_SELECT_RATIO && rule != LYCHEE_SELECT_THRESHOLD &&
-        rule != LYCHEE_SELECT_TOPP)
-        return fail(LYCHEE_ERR_INVALID_ARG, "rule must be LYCHEE_SELECT_TOPK, _RATIO, _THRESHOLD or _TOPP (got %d)",
-                    rule);
+        rule != LYCHEE_SELECT_TOPP && rule != LYCHEE_SELECT_BLOCK)
+        return fail(LYCHEE_ERR_INVALID_ARG,
+                    "rule must be LYCHEE_SELECT_TOPK, _RATIO, _THRESHOLD, _TOPP or _BLOCK (got %d)", rule);
     if (rule == LYCHEE_SELECT_RATIO && !(param > 0.0 && param <= 1.0))
         return fail(LYCHEE_ERR_INVALID_ARG, "the ratio rule's theta must be in (0, 1] (got %g)", param);
     if (rule == LYCHEE_SELECT_TOPP && !(param > 0.0 && param <= 1.0))
         return fail(LYCHEE_ERR_INVALID_ARG, "the Top-p rule's p must be in (0, 1] (got %g)", param);
+    if (rule == LYCHEE_SELECT_BLOCK) {
+        const bool pow2 = param == 16.0 || param == 32.0 || param == 64.0 || param == 128.0 || param == 256.0;
+        if (!pow2) return fail(LYCHEE_ERR_INVALID_ARG, "the block size must be 16, 32, 64, 128 or 256 (got %g)", param);
+        if (k < (int32_t)param || k / (int32_t)param > kMaxSelBlocks)
+            return fail(LYCHEE_ERR_INVALID_ARG, "the block rule needs block size <= k <= %d blocks (k = %d, block %g)",
+                        kMaxSelBlocks, k, param);
+    }
     if (rule == LYCHEE_SELECT_THRESHOLD && std::isnan(param))
         return fail(LYCHEE_ERR_INVALID_ARG, "the threshold rule's tau is NaN");
     if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");

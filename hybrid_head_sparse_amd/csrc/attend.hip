@@ -1231,8 +1231,14 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 __syncthreads();
                 stream_range(c_lo, c_hi, nullptr);
                 __syncthreads();
-                // every key to the score buffer (read only if the bound below fails)
+                // every key to the score buffer (read only if the bound below fails,
+                // or by the rule-selection kernel)
                 for (uint32_t i = tid; i < len; i += kAttendThreads) coherent_store(&sc[c_lo + i], u.st.keys[i]);
+                if (p.sel_keys_only) {     // a later kernel selects from the keys alone
+                    for (int i = tid; i < kHistBins; i += kAttendThreads) u.st.hist[i] = 0u;
+                    __syncthreads();
+                    continue;
+                }
                 // this pass's bound: its own crossing at its share s of k_eff plus
                 // a margin, the smaller of kSelMargin - 1 shares and 5 standard
                 // deviations of a Poisson count with mean s (plus 2), but never
@@ -1310,7 +1316,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // is not last, a helper for slice number = free arrivals before it.
             wait_stores_complete();
             __syncthreads();
-            if (tid == 0) {
+            if (tid == 0 && p.sel_keys_only) s_sel[0] = 0u;   // no top-k to resolve
+            if (tid == 0 && !p.sel_keys_only) {
                 const bool ends_here = h1 >= hi;
                 const unsigned long long o64 =
                     counter_add64(&p.ws.selctr[bg], kSelArrival | (ends_here ? kSelFreeArrival : 0ull));

@@ -52,9 +52,9 @@ constexpr int kResolveSlices = 8;
 constexpr unsigned long long kSelArrival = 1ull << 32;
 constexpr unsigned long long kSelFreeArrival = 1ull << 48;
 static_assert(kMaxWG < (1 << 16) && kMaxCtx <= (1ll << 32), "selection counter fields");
-// Workgroups per retrieval head of the Top-p trim kernel (each sums a slice
-// of the softmax normaliser; the last to arrive cuts the set).
-constexpr int kTopPSplit = 16;
+// Workgroups per retrieval head of the rule-selection kernel (Top-p and block
+// rules: each works on a slice of the head; the last to arrive cuts the set).
+constexpr int kRuleSplit = 16;
 
 // Cross-workgroup hand-off without cache-wide maintenance.  Data one
 // workgroup leaves for another inside the same launch is written with
@@ -101,8 +101,8 @@ struct Workspace {
     unsigned long long* cand;    // [BH * max_ctx]            selection candidates (key | index << 32)
     uint32_t* score;             // [BH * max_ctx]            every selection key of a retrieval head
                                  //                           (read when a head's bounds fail, and by
-                                 //                           the Top-p trim)
-    unsigned long long* prec;    // [BH * kTopPSplit * 2]     Top-p trim: per-slice normaliser partials
+                                 //                           the rule-selection kernel)
+    unsigned long long* prec;    // [BH * kRuleSplit * 4]     rule selection: per-slice partials
     // ---- zero-initialised region (restored to zero by every call) ----
     uint32_t* cnt1;              // [BH * kLevel2Max]         level-1 arrival counters
     uint32_t* cnt2;              // [BH]                      level-2 arrival counters
@@ -115,7 +115,7 @@ struct Workspace {
     uint32_t* rdone;             // [BH]                      slices whose resolver has read the head's
                                  //                           histogram and counters
     uint32_t* hist;              // [BH * kHistBins]          first-digit counts from each pass's bound up
-    uint32_t* pctr;              // [BH]                      Top-p trim: slices done
+    uint32_t* pctr;              // [BH]                      rule selection: slices done
     uint32_t* err;               // [4]
     void* zero_begin;
     size_t zero_bytes;
@@ -142,7 +142,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_rec2 = take(sizeof(float) * (size_t)BH * kLevel2Max * RS);
     size_t o_cand = take(sizeof(unsigned long long) * (size_t)BH * max_ctx);
     size_t o_score = take(sizeof(uint32_t) * (size_t)BH * max_ctx);
-    size_t o_prec = take(sizeof(unsigned long long) * (size_t)BH * kTopPSplit * 2);
+    size_t o_prec = take(sizeof(unsigned long long) * (size_t)BH * kRuleSplit * 4);
     size_t z0 = off;
     size_t o_cnt1 = take(sizeof(uint32_t) * (size_t)BH * kLevel2Max);
     size_t o_cnt2 = take(sizeof(uint32_t) * (size_t)BH);
@@ -196,6 +196,9 @@ struct AttendParams {
     // kept.  S is padded with -1.
     double sel_ratio;
     uint32_t sel_tkey;
+    // Retrieval heads only write every token's key to the score buffer and
+    // leave S to a later kernel (the block rule): no top-k.
+    uint32_t sel_keys_only;
 };
 
 // Host launcher (defined next to the kernel).  dtype: 0 fp32, 1 bf16.  The

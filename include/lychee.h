@@ -127,17 +127,31 @@ lychee_status lychee_decode_layer(lychee_handle* h,
  *              normaliser, summed as 52-bit fixed point, so a cut within that
  *              rounding of p may land one token either side.  Runs a second
  *              kernel after the attention kernel.
- * Ties go to the lower index under every rule. */
-enum { LYCHEE_SELECT_TOPK = 0, LYCHEE_SELECT_RATIO = 1, LYCHEE_SELECT_THRESHOLD = 2, LYCHEE_SELECT_TOPP = 3 };
+ *   BLOCK      block-granular selection (the digest's kernel works on blocks
+ *              of 64 tokens and states no rule for a block's score): blocks of
+ *              bs = param tokens (16, 32, 64, 128 or 256; the last block may
+ *              be shorter), a block scored by the largest s_j of its tokens,
+ *              the floor(k / bs) highest blocks kept (at most 4096 blocks;
+ *              k >= bs), their tokens listed ascending.  Runs the second
+ *              kernel too.
+ * Ties go to the lower index (token or block) under every rule. */
+enum {
+    LYCHEE_SELECT_TOPK = 0,
+    LYCHEE_SELECT_RATIO = 1,
+    LYCHEE_SELECT_THRESHOLD = 2,
+    LYCHEE_SELECT_TOPP = 3,
+    LYCHEE_SELECT_BLOCK = 4
+};
 
 /* lychee_decode_layer with a selection rule for the retrieval heads (above).
  * A retrieval row of S_out holds its selected tokens ascending, then -1 up to
  * k; a later sparse head skips the -1 entries.  Arguments as for
  * lychee_decode_layer, plus `rule` (a LYCHEE_SELECT_* value) and `param`
- * (theta for RATIO, tau for THRESHOLD, p for TOPP, unused for TOPK).
- * Returns LYCHEE_ERR_INVALID_ARG for an unknown rule, theta or p outside
- * (0, 1] or a NaN tau, after which nothing is enqueued.  With profile events
- * set, `stop` follows the Top-p kernel. */
+ * (theta for RATIO, tau for THRESHOLD, p for TOPP, the block size for BLOCK,
+ * unused for TOPK).  Returns LYCHEE_ERR_INVALID_ARG for an unknown rule, theta
+ * or p outside (0, 1], a NaN tau or a block size or k the block rule does not
+ * take, after which nothing is enqueued.  With profile events set, `stop`
+ * follows the second kernel of TOPP and BLOCK. */
 lychee_status lychee_decode_layer_select(lychee_handle* h,
                                          const void* q, const void* k_cache, const void* v_cache,
                                          const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out,

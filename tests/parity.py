@@ -16,7 +16,12 @@ Tolerances (stated for the method's parity bar):
     the Top-p rule the GPU's count c must be a valid cut of the oracle's
     cumulative shares to within 1e-5 (the top c - 1 shares sum to less
     than p + 1e-5 and the top c to at least p - 1e-5, or c = min(k, n)),
-    and its set must be the oracle's top c up to the band at its own cut.
+    and its set must be the oracle's top c up to the band at its own cut;
+    under the block rule each row must be the ascending expansion of exactly
+    min(floor(k / bs), ceil(n / bs)) whole blocks, and the block set must
+    equal the oracle's except for blocks whose score (the largest oracle
+    pooled score of their tokens) lies in the band around the last kept
+    block's score.
 The oracle receives the same S_in as the GPU (the GPU's S_out of the previous
 layer), so a tolerated boundary swap upstream cannot move a downstream
 sparse-head output.
@@ -49,6 +54,25 @@ def _band(s, cut):
     return np.abs(s - cut) <= tol
 
 
+def _compare_blocks(row, O, s, n, k, bs, b, g):
+    nb = -(-n // bs)
+    kb = min(k // bs, nb)
+    blk_score = np.array([s[i * bs:min(n, i * bs + bs)].max() for i in range(nb)])
+    valid = row[row != -1]
+    blocks = np.unique(valid // bs)
+    assert blocks.size == kb, f"block rule kept {blocks.size} blocks, expected {kb} at b={b} g={g}"
+    want = np.concatenate([np.arange(i * bs, min(n, i * bs + bs)) for i in blocks])
+    np.testing.assert_array_equal(row[:want.size], want, err_msg=f"block expansion at b={b} g={g}")
+    assert np.all(row[want.size:] == -1), f"block padding at b={b} g={g}"
+    o_blocks = np.unique(O // bs)
+    band = _band(blk_score, blk_score[o_blocks].min())
+    a_out = {i for i in blocks.tolist() if not band[i]}
+    o_out = {i for i in o_blocks.tolist() if not band[i]}
+    assert a_out == o_out, f"block set mismatch outside the band at b={b} g={g}: " \
+                           f"gpu-only {sorted(a_out - o_out)[:8]} oracle-only {sorted(o_out - a_out)[:8]}"
+    return len(set(blocks.tolist()) ^ set(o_blocks.tolist()))
+
+
 def compare_S(S_gpu, S_or, scores, role, n_ctx, k, ties=None, rule="topk", param=0.0):
     """Returns the number of band positions that differ (informational)."""
     B, Hkv, _ = S_gpu.shape
@@ -61,6 +85,9 @@ def compare_S(S_gpu, S_or, scores, role, n_ctx, k, ties=None, rule="topk", param
                 continue          # a sparse head forwards S_in (checked by the caller)
             O = S_or[b, g]
             O = O[O != -1]
+            if rule == "block":
+                band_diffs += _compare_blocks(S_gpu[b, g], O, scores[b, g, :n], n, k, int(param), b, g)
+                continue
             if rule == "topp":
                 cnt = int(np.count_nonzero(S_gpu[b, g] != -1))
                 assert 1 <= cnt <= ke, f"Top-p kept {cnt} of min(k, n) = {ke} at b={b} g={g}"

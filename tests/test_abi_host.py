@@ -130,7 +130,10 @@ def test_null_handle_is_rejected(lib):
     (hhs.SELECT_RULES["threshold"], float("nan"), "tau"),
     (hhs.SELECT_RULES["topp"], 0.0, "p must"),
     (hhs.SELECT_RULES["topp"], 1.0000001, "p must"),
-    (4, 0.5, "rule"),
+    (5, 0.5, "rule"),
+    (hhs.SELECT_RULES["block"], 48.0, "block size"),
+    (hhs.SELECT_RULES["block"], 512.0, "block size"),
+    (hhs.SELECT_RULES["block"], 64.5, "block size"),
 ])
 def test_bad_selection_rules_are_rejected(lib, rule, param, needle):
     # the rule is checked before the handle, so a NULL handle still reports it
@@ -140,8 +143,13 @@ def test_bad_selection_rules_are_rejected(lib, rule, param, needle):
 
 
 @pytest.mark.parametrize("rule, param", [(0, 0.0), (1, 1.0), (1, 1e-9), (2, float("inf")), (2, -float("inf")),
-                                         (2, -3.5), (3, 1.0), (3, 1e-12)])
+                                         (2, -3.5), (3, 1.0), (3, 1e-12), (4, 64.0), (4, 16.0)])
 def test_valid_selection_rules_reach_the_handle_check(lib, rule, param):
-    st = lib.lychee_decode_layer_select(None, None, None, None, None, None, None, None, None, 1, rule, param)
+    st = lib.lychee_decode_layer_select(None, None, None, None, None, None, None, None, None, 4096, rule, param)
     assert st == hhs.LYCHEE_ERR_INVALID_ARG
     assert "handle" in lib.lychee_last_error().decode()
+
+
+def test_block_rule_needs_k_of_at_least_one_block(lib):
+    st = lib.lychee_decode_layer_select(None, None, None, None, None, None, None, None, None, 32, 4, 64.0)
+    assert st == hhs.LYCHEE_ERR_INVALID_ARG and "block" in lib.lychee_last_error().decode()

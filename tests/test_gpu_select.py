@@ -1,6 +1,7 @@
 """Selection rules other than top-k on the GPU, against the oracle (reading R16
 of the oracle: the ratio, threshold and Top-p rules of the digest's ablation
-of selection methods, section 4.4.1 / Figure 6).
+of selection methods, section 4.4.1 / Figure 6; reading R17: block-granular
+selection).
 
 Each case runs layer 0 (all retrieval) under a rule and a layer 1 with half
 of the KV heads sparse under the same rule, so the sparse heads attend to a
@@ -160,3 +161,24 @@ def test_topp_rule_limits():
 def test_topp_rule_every_token_a_candidate():
     # k >= n: the shares of the whole context decide alone
     _two_layers(LOUD_SHORT, "topp", 0.4)
+
+
+@pytest.mark.parametrize("bs", [16, 64, 256])
+def test_block_rule(bs):
+    # 9001 = 140 * 64 + 41: a short last block
+    S0, _ = _two_layers(RAGGED, "block", bs)
+    for b, n in enumerate(synth.n_ctx(RAGGED)):
+        kb = min(RAGGED.k // bs, -(-int(n) // bs))
+        assert np.all(np.unique(S0[b, 0][S0[b, 0] >= 0] // bs).size == kb)
+
+
+def test_block_rule_every_block_and_short_context():
+    # k >= n: every block kept, S lists all tokens
+    S0, _ = _two_layers(SHORT, "block", 64)
+    for b, n in enumerate(synth.n_ctx(SHORT)):
+        assert np.all(S0[b, :, :n] == np.arange(n)) and np.all(S0[b, :, n:] == -1)
+
+
+def test_block_rule_at_128k_context():
+    w = synth.Workload("select_block_128k", 36, 1, 2, 32, 8, 128, 131072, 4096, "bf16", 4, hh_frac=0.01)
+    _two_layers(w, "block", 64)
