@@ -256,7 +256,7 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
     hipError_t e = launch_attend(ap, d.dtype, d.head_dim, G, hybrid, h->cus, h->per_cu, h->stream);
     if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-    if (hybrid && (rule == LYCHEE_SELECT_TOPP || rule == LYCHEE_SELECT_BLOCK)) {
+    if (hybrid && bits != 0 && (rule == LYCHEE_SELECT_TOPP || rule == LYCHEE_SELECT_BLOCK)) {
         // the attention kernel wrote the top-min(k, n) sets and every key:
         // cut the sets to their Top-p prefix, or select blocks instead
         RuleParams tp{};
