@@ -41,7 +41,14 @@ Pins (the tests that hold the oracle to something other than itself; all in
   * block selection (reading R17): blocks of one token are top-k; planted
     heavy tokens pick their blocks in closed form, ties between blocks go
     to the lower block; a short last block and k covering every block list
-    all tokens.
+    all tokens;
+  * the multi-step loop (reading R18): the append writes exactly the new
+    rows and grows n by one (bytes compared, the rest untouched, a full
+    cache refused); the correction attention with T = 1 equals the layer's
+    dense retrieval output, over identical keys gives the mean of the V
+    prefix 0..p, ignores rows after p and not rows up to p, and matches
+    torch's scaled_dot_product_attention with an explicit causal mask in
+    float64.
 """
 from __future__ import annotations
 
@@ -86,6 +93,10 @@ def _load():
         lib.oracle_layer.restype = i
         lib.oracle_layer_select.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p, i, i, ctypes.c_double, p, i]
         lib.oracle_layer_select.restype = i
+        lib.oracle_kv_append.argtypes = [i, i, i, i, i, p, p, p, p, p]
+        lib.oracle_kv_append.restype = i
+        lib.oracle_correction_attention.argtypes = [i, i, i, i, i, i, i, p, p, p, p, p, i]
+        lib.oracle_correction_attention.restype = i
         _lib = lib
     return _lib
 
@@ -150,6 +161,51 @@ def layer(q, k_cache, v_cache, role, S_in, n_ctx, k, *, want_scores=False,
     if rc != 0:
         raise ValueError(f"oracle_layer: {ERRORS.get(rc, rc)}")
     return out, S_out, scores
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, n_ctx):
+    """Algorithm 1's cache append (reading R18 of oracle.c), in place: row
+    n_ctx[b] of each KV head receives k_new / v_new [B, Hkv, d]; returns the
+    new n_ctx (a copy, each entry one larger)."""
+    k_new = np.ascontiguousarray(k_new)
+    v_new = np.ascontiguousarray(v_new)
+    dt = _dtype_code(k_cache)
+    if _dtype_code(k_new) != dt or _dtype_code(v_new) != dt or _dtype_code(v_cache) != dt:
+        raise TypeError("one dtype for the new rows and the caches")
+    if not (k_cache.flags.c_contiguous and v_cache.flags.c_contiguous):
+        raise ValueError("caches must be contiguous (appended in place)")
+    B, Hkv, max_ctx, d = k_cache.shape
+    if k_new.shape != (B, Hkv, d) or v_new.shape != (B, Hkv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    n = np.array(n_ctx, dtype=np.int32, copy=True)
+    rc = _load().oracle_kv_append(B, Hkv, d, max_ctx, dt, _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(n))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_append: {ERRORS.get(rc, rc)}")
+    return n
+
+
+def correction_attention(q, k_cache, v_cache, n_ctx, *, threads=0):
+    """Cache Correction's attention (reading R18 of oracle.c): q [B, T, Hq, d]
+    holds the last T positions' queries; returns out [B, T, Hq, d] float64,
+    row t attending causally to cache rows 0 .. n_ctx[b] - T + t."""
+    q = np.ascontiguousarray(q)
+    k_cache = np.ascontiguousarray(k_cache)
+    v_cache = np.ascontiguousarray(v_cache)
+    dt = _dtype_code(q)
+    if _dtype_code(k_cache) != dt or _dtype_code(v_cache) != dt:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    B, T, Hq, d = q.shape
+    _, Hkv, max_ctx, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or k_cache.shape[0] != B:
+        raise ValueError("shape mismatch")
+    n_ctx = np.ascontiguousarray(np.asarray(n_ctx, dtype=np.int32))
+    out = np.zeros((B, T, Hq, d), dtype=np.float64)
+    rc = _load().oracle_correction_attention(B, T, Hq, Hkv, d, max_ctx, dt, _ptr(q), _ptr(k_cache),
+                                             _ptr(v_cache), _ptr(n_ctx), _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_correction_attention: {ERRORS.get(rc, rc)}")
+    return out
 
 
 def step(layers, n_ctx, k, *, threads=0):

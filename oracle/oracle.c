@@ -48,6 +48,15 @@
  *       largest pooled score (R2) of its tokens; the floor(k / bs) highest
  *       blocks (score desc, block index asc; all blocks if fewer) are kept,
  *       and S lists their tokens ascending, padded with -1.
+ *   R18 the multi-step loop around the step (Algorithm 1's cache append,
+ *       and the Cache Correction of the digest's reasoning setup, a dense
+ *       re-prefill of the last 32 decoded tokens every 32 steps): only the
+ *       attention part is evaluated.  The append writes the new token's K
+ *       and V rows at position n of each (sequence, KV head) and makes the
+ *       context n + 1.  The correction attention gives each of the last T
+ *       positions p = n - T + t (t < T) of a sequence, for every query head,
+ *       dense causal attention over the cache rows 0..p (Eq. 1 with the
+ *       prefill's causal mask), with that position's own query.
  *
  * Parity status: pinned (see the header of oracle/__init__.py for the list
  * of pins and the tests that hold them).
@@ -318,4 +327,74 @@ int oracle_layer(int B, int Hq, int Hkv, int d, int max_ctx, int dtype,
                  int nthreads) {
     return oracle_layer_select(B, Hq, Hkv, d, max_ctx, dtype, q, kc, vc, role, S_in, S_out, out, n_ctx, k,
                                ORACLE_RULE_TOPK, 0.0, scores, nthreads);
+}
+
+/*
+ * Algorithm 1's cache append (reading R18): row n_ctx[b] of every KV head of
+ * sequence b receives k_new / v_new [B, Hkv, d] and n_ctx[b] grows by one.
+ * A full cache (n_ctx[b] == max_ctx) is an error and changes nothing.
+ */
+int oracle_kv_append(int B, int Hkv, int d, int max_ctx, int dtype,
+                     const void* k_new, const void* v_new, void* kc, void* vc, int32_t* n_ctx) {
+    if (B <= 0 || Hkv <= 0 || d <= 0 || max_ctx <= 0 || (dtype != 0 && dtype != 1)) return ORACLE_ERR_ARG;
+    if (!k_new || !v_new || !kc || !vc || !n_ctx) return ORACLE_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        if (n_ctx[b] < 0 || n_ctx[b] >= max_ctx) return ORACLE_ERR_NCTX;
+    const size_t es = dtype == 1 ? 2 : 4;
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < Hkv; ++g) {
+            const size_t dst = (((size_t)b * Hkv + g) * (size_t)max_ctx + (size_t)n_ctx[b]) * d * es;
+            const size_t src = ((size_t)b * Hkv + g) * (size_t)d * es;
+            memcpy((char*)kc + dst, (const char*)k_new + src, (size_t)d * es);
+            memcpy((char*)vc + dst, (const char*)v_new + src, (size_t)d * es);
+        }
+        n_ctx[b] += 1;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Cache Correction's attention (reading R18): for the last T positions of
+ * every sequence, p = n - T + t, each query head h (KV head floor(h / G))
+ * attends densely and causally to cache rows 0..p with scale 1/sqrt(d):
+ *   q    [B, T, Hq, d]      dtype, row t is position n - T + t
+ *   out  [B, T, Hq, d]      double
+ * Requires 1 <= T <= n_ctx[b] <= max_ctx.
+ */
+int oracle_correction_attention(int B, int T, int Hq, int Hkv, int d, int max_ctx, int dtype,
+                                const void* q, const void* kc, const void* vc,
+                                const int32_t* n_ctx, double* out, int nthreads) {
+    if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_ctx <= 0) return ORACLE_ERR_ARG;
+    if (Hq % Hkv != 0 || (dtype != 0 && dtype != 1)) return ORACLE_ERR_ARG;
+    if (!q || !kc || !vc || !n_ctx || !out) return ORACLE_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        if (n_ctx[b] < T || n_ctx[b] > max_ctx) return ORACLE_ERR_NCTX;
+    const int G = Hq / Hkv;
+    const double c = 1.0 / sqrt((double)d);
+    int status = ORACLE_OK;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bt = 0; bt < B * T; ++bt) {
+        const int b = bt / T, t = bt % T;
+        const int pos = n_ctx[b] - T + t;                 /* this row's position */
+        double* z = (double*)malloc(sizeof(double) * (size_t)(pos + 1));
+        if (!z) {
+#pragma omp atomic write
+            status = ORACLE_ERR_MEM;
+            continue;
+        }
+        for (int h = 0; h < Hq; ++h) {
+            const int g = h / G;                          /* reading R6 */
+            const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)max_ctx * d;
+            const size_t q_off = (((size_t)b * T + t) * Hq + h) * d;
+            for (int j = 0; j <= pos; ++j) z[j] = c * dot_row(q, q_off, kc, kv_base + (size_t)j * d, d, dtype);
+            softmax_weighted_sum(z, NULL, pos + 1, vc, kv_base, d, dtype, out + q_off);
+        }
+        free(z);
+    }
+    return status;
 }

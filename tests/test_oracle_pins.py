@@ -510,3 +510,92 @@ def test_block_rule_rejects_bad_block_sizes():
     for bs in (0, 2.5, 64):                   # 64 > k = 32
         with pytest.raises(ValueError):
             oracle.layer(q, kc, vc, np.ones(1, np.uint8), None, n_ctx, 32, rule="block", param=bs)
+
+
+# ---------------------------------------------------------------- multi-step loop (reading R18)
+
+def test_kv_append_writes_the_new_rows_and_grows_n():
+    rng = np.random.default_rng(40)
+    B, Hkv, d, max_ctx = 2, 3, 16, 10
+    for dtype in ("f32", "bf16"):
+        kc = rng.standard_normal((B, Hkv, max_ctx, d)).astype(np.float32)
+        vc = rng.standard_normal((B, Hkv, max_ctx, d)).astype(np.float32)
+        kn = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+        vn = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+        if dtype == "bf16":
+            kc, vc, kn, vn = (synth.to_bf16_bits(a) for a in (kc, vc, kn, vn))
+        k0, v0 = kc.copy(), vc.copy()
+        n = np.array([4, 9], np.int32)
+        n2 = oracle.kv_append(kn, vn, kc, vc, n)
+        np.testing.assert_array_equal(n2, n + 1)
+        for b in range(B):
+            np.testing.assert_array_equal(kc[b, :, n[b]], kn[b])
+            np.testing.assert_array_equal(vc[b, :, n[b]], vn[b])
+            others = np.ones(max_ctx, bool)
+            others[n[b]] = False
+            np.testing.assert_array_equal(kc[b][:, others], k0[b][:, others])
+            np.testing.assert_array_equal(vc[b][:, others], v0[b][:, others])
+        with pytest.raises(ValueError):           # the second sequence is now full
+            oracle.kv_append(kn, vn, kc, vc, n2)
+
+
+def _corr_case(rng, B, T, Hq, Hkv, d, max_ctx, n):
+    q = rng.standard_normal((B, T, Hq, d)).astype(np.float32)
+    kc = rng.standard_normal((B, Hkv, max_ctx, d)).astype(np.float32)
+    vc = rng.standard_normal((B, Hkv, max_ctx, d)).astype(np.float32)
+    return q, kc, vc, np.asarray(n, np.int32)
+
+
+def test_correction_attention_one_row_is_the_dense_decode_output():
+    rng = np.random.default_rng(41)
+    B, Hq, Hkv, d, max_ctx = 2, 8, 2, 32, 90
+    q, kc, vc, n = _corr_case(rng, B, 1, Hq, Hkv, d, max_ctx, [90, 57])
+    out = oracle.correction_attention(q, kc, vc, n)
+    ref, _, _ = oracle.layer(q[:, 0], kc, vc, np.ones(Hkv, np.uint8), None, n, 4)
+    np.testing.assert_allclose(out[:, 0], ref, rtol=0, atol=1e-13)
+
+
+def test_correction_attention_identical_keys_average_the_v_prefix():
+    rng = np.random.default_rng(42)
+    B, T, Hq, Hkv, d, max_ctx = 1, 5, 4, 2, 16, 40
+    q, kc, vc, n = _corr_case(rng, B, T, Hq, Hkv, d, max_ctx, [33])
+    kc[:] = kc[:, :, :1]                           # every key equal: uniform weights
+    out = oracle.correction_attention(q, kc, vc, n)
+    for t in range(T):
+        p = 33 - T + t
+        for h in range(Hq):
+            np.testing.assert_allclose(out[0, t, h], vc[0, h // 2, :p + 1].astype(np.float64).mean(axis=0),
+                                       rtol=0, atol=1e-12)
+
+
+def test_correction_attention_is_causal():
+    """Rows after a position never change its output; a row at or before it does."""
+    rng = np.random.default_rng(43)
+    B, T, Hq, Hkv, d, max_ctx = 1, 6, 4, 1, 16, 30
+    q, kc, vc, n = _corr_case(rng, B, T, Hq, Hkv, d, max_ctx, [30])
+    base = oracle.correction_attention(q, kc, vc, n)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[0, 0, 27:] += 3.0                          # positions 27..29
+    vc2[0, 0, 27:] -= 2.0
+    out = oracle.correction_attention(q, kc2, vc2, n)
+    # row t sits at position 24 + t: rows 0..2 (positions 24..26) see no change
+    np.testing.assert_array_equal(out[0, :3], base[0, :3])
+    assert np.all(np.abs(out[0, 3:] - base[0, 3:]).max(axis=-1) > 1e-3)
+
+
+def test_correction_attention_matches_torch_sdpa_with_a_causal_mask():
+    import torch
+    rng = np.random.default_rng(44)
+    B, T, Hq, Hkv, d, max_ctx = 2, 7, 8, 2, 32, 50
+    q, kc, vc, n = _corr_case(rng, B, T, Hq, Hkv, d, max_ctx, [50, 23])
+    out = oracle.correction_attention(q, kc, vc, n)
+    G = Hq // Hkv
+    for b in range(B):
+        nb = int(n[b])
+        Q = torch.from_numpy(q[b].astype(np.float64)).permute(1, 0, 2)          # [Hq, T, d]
+        K = torch.from_numpy(kc[b, :, :nb].astype(np.float64)).repeat_interleave(G, dim=0)   # [Hq, n, d]
+        V = torch.from_numpy(vc[b, :, :nb].astype(np.float64)).repeat_interleave(G, dim=0)
+        pos = torch.arange(nb - T, nb)[:, None]
+        mask = torch.arange(nb)[None, :] <= pos                                   # [T, n]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask)
+        np.testing.assert_allclose(out[b], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
