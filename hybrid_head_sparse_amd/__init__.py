@@ -35,7 +35,7 @@ SELECT_RULES = {"topk": 0, "ratio": 1, "threshold": 2, "topp": 3, "block": 4}   
 
 EXPORTED = (
     "lychee_workspace_bytes", "lychee_create", "lychee_decode_layer", "lychee_decode_layer_select",
-    "lychee_dense_decode_layer",
+    "lychee_dense_decode_layer", "lychee_kv_append", "lychee_correction_attention",
     "lychee_validate_layer", "lychee_set_stream", "lychee_set_profile_events",
     "lychee_check_device_errors", "lychee_destroy", "lychee_status_str", "lychee_last_error",
 )
@@ -73,6 +73,8 @@ def load() -> ctypes.CDLL:
         "lychee_decode_layer": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]),
         "lychee_decode_layer_select": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_double]),
         "lychee_dense_decode_layer": (i32, [vp, vp, vp, vp, vp, vp]),
+        "lychee_kv_append": (i32, [vp, vp, vp, vp, vp, vp]),
+        "lychee_correction_attention": (i32, [vp, vp, vp, vp, vp, i32, vp]),
         "lychee_validate_layer": (i32, [pd, vp, vp, vp, vp, vp, vp, vp, vp, i32]),
         "lychee_set_stream": (i32, [vp, vp]),
         "lychee_set_profile_events": (i32, [vp, vp, vp]),
@@ -203,6 +205,37 @@ class Handle:
         self._check_common(q, k_cache, v_cache, out, n_ctx)
         _check(load().lychee_dense_decode_layer(self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
                                                 _ptr(n_ctx)), "lychee_dense_decode_layer")
+
+    def kv_append(self, k_new, v_new, k_cache, v_cache, n_ctx):
+        """Append one token's K and V rows ([B, Hkv, d]) at position n_ctx[b]
+        and grow n_ctx on the device."""
+        d = self.dims
+        torch = self._torch
+        kv = (d.batch, d.n_kv_heads, d.max_ctx, d.head_dim)
+        self._check_tensor(k_new, "k_new", (d.batch, d.n_kv_heads, d.head_dim), self.tdtype)
+        self._check_tensor(v_new, "v_new", (d.batch, d.n_kv_heads, d.head_dim), self.tdtype)
+        self._check_tensor(k_cache, "k_cache", kv, self.tdtype)
+        self._check_tensor(v_cache, "v_cache", kv, self.tdtype)
+        self._check_tensor(n_ctx, "n_ctx", (d.batch,), torch.int32)
+        _check(load().lychee_kv_append(self._h, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(n_ctx)), "lychee_kv_append")
+
+    def correction_attention(self, q, k_cache, v_cache, n_ctx, out):
+        """Cache Correction's attention: q [B, T, Hq, d] (bf16) for the last T
+        positions, out [B, T, Hq, d] fp32."""
+        d = self.dims
+        torch = self._torch
+        if q.dim() != 4:
+            raise ValueError("q must be [B, T, Hq, d]")
+        T = int(q.shape[1])
+        kv = (d.batch, d.n_kv_heads, d.max_ctx, d.head_dim)
+        self._check_tensor(q, "q", (d.batch, T, d.n_q_heads, d.head_dim), self.tdtype)
+        self._check_tensor(k_cache, "k_cache", kv, self.tdtype)
+        self._check_tensor(v_cache, "v_cache", kv, self.tdtype)
+        self._check_tensor(n_ctx, "n_ctx", (d.batch,), torch.int32)
+        self._check_tensor(out, "out", (d.batch, T, d.n_q_heads, d.head_dim), torch.float32)
+        _check(load().lychee_correction_attention(self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(n_ctx), T,
+                                                  _ptr(out)), "lychee_correction_attention")
 
     def set_profile_events(self, start=None, stop=None):
         """Record torch.cuda.Event ``start``/``stop`` around each following attention kernel."""

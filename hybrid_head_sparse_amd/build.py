@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblychee.so")
-SOURCES = ["attend.hip", "rules.hip", "abi.hip"]
+SOURCES = ["attend.hip", "rules.hip", "correction.hip", "abi.hip"]
 ARCH = os.environ.get("LYCHEE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -12,6 +12,7 @@
 #include "../../include/lychee.h"
 #include "common.hpp"
 #include "rules.hpp"
+#include "correction.hpp"
 
 using namespace lychee;
 
@@ -329,6 +330,86 @@ lychee_status lychee_dense_decode_layer(lychee_handle* h, const void* q, const v
     return run_layer(h, q, k_cache, v_cache, nullptr, nullptr, nullptr, out, n_ctx, 1, false);
 }
 
+lychee_status lychee_kv_append(lychee_handle* h, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               int32_t* n_ctx) {
+    if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");
+    const lychee_dims& d = h->dims;
+    if (!k_new || !v_new || !k_cache || !v_cache || !n_ctx) return fail(LYCHEE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)n_ctx) & 3u)
+        return fail(LYCHEE_ERR_INVALID_ARG, "tensors must be 4-byte aligned");
+    const size_t es = elem_bytes(&d);
+    const size_t nnew = (size_t)d.batch * d.n_kv_heads * d.head_dim * es;
+    const size_t nkv = (size_t)d.batch * d.n_kv_heads * d.max_ctx * d.head_dim * es;
+    const Range rk = span(k_cache, nkv), rv = span(v_cache, nkv), rn = span(n_ctx, (size_t)d.batch * 4);
+    if (overlap(rk, rv) || overlap(rk, rn) || overlap(rv, rn) || overlap(rk, span(k_new, nnew)) ||
+        overlap(rk, span(v_new, nnew)) || overlap(rv, span(k_new, nnew)) || overlap(rv, span(v_new, nnew)))
+        return fail(LYCHEE_ERR_INVALID_ARG, "the caches, the new rows and n_ctx must not overlap");
+    AppendParams ap{};
+    ap.k_new = k_new;
+    ap.v_new = v_new;
+    ap.kc = k_cache;
+    ap.vc = v_cache;
+    ap.n_ctx = n_ctx;
+    ap.err = h->ws.err;
+    ap.B = d.batch;
+    ap.Hkv = d.n_kv_heads;
+    ap.d = d.head_dim;
+    ap.max_ctx = d.max_ctx;
+    ap.elem_bytes = (int32_t)es;
+    hipError_t e = launch_kv_append(ap, h->stream);
+    if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+lychee_status lychee_correction_attention(lychee_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* n_ctx, int32_t T, float* out) {
+    if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");
+    const lychee_dims& d = h->dims;
+    if (T < 1 || T > kCorrMaxT) return fail(LYCHEE_ERR_INVALID_ARG, "T must be in [1, %d] (got %d)", kCorrMaxT, T);
+    if (d.dtype != LYCHEE_BF16 || d.head_dim != 128)
+        return fail(LYCHEE_ERR_UNSUPPORTED, "the correction attention runs on bf16 caches with head_dim 128");
+    const int G = d.n_q_heads / d.n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(LYCHEE_ERR_UNSUPPORTED, "the correction attention needs n_q_heads / n_kv_heads in {1, 2, 4, 8}");
+    if (!q || !k_cache || !v_cache || !n_ctx || !out) return fail(LYCHEE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15u)
+        return fail(LYCHEE_ERR_INVALID_ARG, "q, the caches and out must be 16-byte aligned");
+    if ((uintptr_t)n_ctx & 3u) return fail(LYCHEE_ERR_INVALID_ARG, "n_ctx must be 4-byte aligned");
+    const size_t nq = (size_t)d.batch * T * d.n_q_heads * d.head_dim;
+    const size_t nkv = (size_t)d.batch * d.n_kv_heads * d.max_ctx * d.head_dim * 2;
+    const Range ro = span(out, nq * 4);
+    if (overlap(ro, span(q, nq * 2)) || overlap(ro, span(k_cache, nkv)) || overlap(ro, span(v_cache, nkv)) ||
+        overlap(ro, span(n_ctx, (size_t)d.batch * 4)))
+        return fail(LYCHEE_ERR_INVALID_ARG, "out overlaps an input");
+    const int BH = d.batch * d.n_kv_heads;
+    int nchunks = kCorrTargetWG / BH;
+    nchunks = nchunks < 1 ? 1 : nchunks;
+    const int by_len = d.max_ctx / 256;             // chunks of at least 256 keys
+    nchunks = nchunks > by_len ? (by_len < 1 ? 1 : by_len) : nchunks;
+    CorrParams cp{};
+    cp.q = q;
+    cp.kc = k_cache;
+    cp.vc = v_cache;
+    cp.n_ctx = n_ctx;
+    cp.out = out;
+    cp.rec_ml = h->ws.crec_ml;
+    cp.rec_o = h->ws.crec_o;
+    cp.err = h->ws.err;
+    cp.B = d.batch;
+    cp.Hkv = d.n_kv_heads;
+    cp.max_ctx = d.max_ctx;
+    cp.T = T;
+    cp.nchunks = nchunks;
+    cp.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+    if (h->ev_start && hipEventRecord(h->ev_start, h->stream) != hipSuccess)
+        return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
+    hipError_t e = launch_correction(cp, G, h->stream);
+    if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "correction launch failed: %s", hipGetErrorString(e));
+    if (h->ev_stop && hipEventRecord(h->ev_stop, h->stream) != hipSuccess)
+        return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
+    return ok();
+}
+
 lychee_status lychee_check_device_errors(lychee_handle* h) {
     if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");
     uint32_t flag = 0;
@@ -338,7 +419,8 @@ lychee_status lychee_check_device_errors(lychee_handle* h) {
     if (flag) {
         if (hipMemset(h->ws.err, 0, sizeof flag) != hipSuccess)
             return fail(LYCHEE_ERR_HIP, "clearing the device error flag failed");
-        return fail(LYCHEE_ERR_DEVICE_CHECK, "device error flag 0x%x (1: S_in entry outside [0, n_ctx) and not -1; 2: select count mismatch)",
+        return fail(LYCHEE_ERR_DEVICE_CHECK, "device error flag 0x%x (1: S_in entry outside [0, n_ctx) and not -1; 2: select count mismatch; "
+                    "4: n_ctx < T in a correction; 8: append to a full cache)",
                     flag);
     }
     return ok();

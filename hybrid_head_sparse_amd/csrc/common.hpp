@@ -103,6 +103,8 @@ struct Workspace {
                                  //                           (read when a head's bounds fail, and by
                                  //                           the rule-selection kernel)
     unsigned long long* prec;    // [BH * kRuleSplit * 4]     rule selection: per-slice partials
+    float* crec_ml;              // [CW * 32 G * 2]           correction attention: chunk partials
+    float* crec_o;               // [CW * 32 G * D]           (CW = max(512, BH) workgroups)
     // ---- zero-initialised region (restored to zero by every call) ----
     uint32_t* cnt1;              // [BH * kLevel2Max]         level-1 arrival counters
     uint32_t* cnt2;              // [BH]                      level-2 arrival counters
@@ -143,6 +145,9 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_cand = take(sizeof(unsigned long long) * (size_t)BH * max_ctx);
     size_t o_score = take(sizeof(uint32_t) * (size_t)BH * max_ctx);
     size_t o_prec = take(sizeof(unsigned long long) * (size_t)BH * kRuleSplit * 4);
+    const size_t CW = (size_t)(BH > 512 ? BH : 512);
+    size_t o_crml = take(sizeof(float) * CW * 32 * G * 2);
+    size_t o_cro = take(sizeof(float) * CW * 32 * G * D);
     size_t z0 = off;
     size_t o_cnt1 = take(sizeof(uint32_t) * (size_t)BH * kLevel2Max);
     size_t o_cnt2 = take(sizeof(uint32_t) * (size_t)BH);
@@ -163,6 +168,8 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.cand = (unsigned long long*)(p + o_cand);
         w.score = (uint32_t*)(p + o_score);
         w.prec = (unsigned long long*)(p + o_prec);
+        w.crec_ml = (float*)(p + o_crml);
+        w.crec_o = (float*)(p + o_cro);
         w.cnt1 = (uint32_t*)(p + o_cnt1);
         w.cnt2 = (uint32_t*)(p + o_cnt2);
         w.selctr = (unsigned long long*)(p + o_sc);

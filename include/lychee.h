@@ -180,9 +180,39 @@ lychee_status lychee_set_stream(lychee_handle* h, void* stream);
  * kernel and `stop` right after it, on the handle's stream.  NULL disables. */
 lychee_status lychee_set_profile_events(lychee_handle* h, void* start, void* stop);
 
+/* Algorithm 1's cache append, the step after a token's attention (the
+ * multi-step loop around the layer; digest section 3.4): row n_ctx[b] of
+ * every KV head of sequence b receives the new token's K and V rows, then
+ * n_ctx[b] grows by one, all on the device (so a captured loop of steps
+ * advances by itself).
+ *   k_new, v_new  [B, Hkv, d] dtype
+ *   k_cache, v_cache, n_ctx  as for lychee_decode_layer (written)
+ * A sequence whose cache is full (n_ctx[b] == max_ctx) is left unchanged and
+ * latches a flag reported by lychee_check_device_errors. */
+lychee_status lychee_kv_append(lychee_handle* h, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               int32_t* n_ctx);
+
+/* The attention of Cache Correction (digest section 4.2.2: after every 32
+ * decoded tokens, a dense prefill over those tokens refreshes their K and V;
+ * the projections need the model, the attention is this call).  Each of the
+ * last T positions p = n_ctx[b] - T + t of a sequence attends, for every query
+ * head h (KV head h / G), densely and causally to cache rows 0..p with scale
+ * 1/sqrt(d):
+ *   q     [B, T, Hq, d] bf16, row t is position n_ctx[b] - T + t
+ *   out   [B, T, Hq, d] fp32, fully overwritten
+ *   T     1..32;  1 <= T <= n_ctx[b] on the device (else a flag latches and
+ *         the rows are undefined)
+ * Runs on the matrix cores (bf16 operands, fp32 accumulation), so it needs a
+ * bf16 cache, head_dim 128 and n_q_heads / n_kv_heads in {1, 2, 4, 8}
+ * (LYCHEE_ERR_UNSUPPORTED otherwise).  Two kernels: context-chunk partials,
+ * then their log-sum-exp merge.  Profile events bracket both. */
+lychee_status lychee_correction_attention(lychee_handle* h, const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* n_ctx, int32_t T, float* out);
+
 /* Synchronise the stream, read and clear the device-side error flag.
  * Returns LYCHEE_ERR_DEVICE_CHECK if any call since the last check skipped an
- * out-of-range S_in entry. */
+ * out-of-range S_in entry, appended to a full cache or ran a correction over
+ * a context shorter than T. */
 lychee_status lychee_check_device_errors(lychee_handle* h);
 
 /* Release the handle (host memory only). */
