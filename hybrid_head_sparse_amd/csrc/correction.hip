@@ -6,25 +6,28 @@
 // densely and causally to cache rows 0..p with its own query.
 //
 // Correction attention.  Per KV head this is a (T G) x n x d contraction, so
-// it runs on the matrix cores: v_mfma_f32_32x32x8_bf16 (bf16 operands, fp32
-// accumulation).  A workgroup takes one (sequence, KV head) and one chunk of
+// it runs on the matrix cores: v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32
+// accumulation; the gfx950 form, twice the work of the 32x32x8 form per
+// instruction).  A workgroup takes one (sequence, KV head) and one chunk of
 // its context; wavefront w is query head g G + w and holds that head's T
 // queries (padded to 32) as the 32 columns of its tiles.  Per tile of 32 keys:
-//   S^T = K Q^T          (16 MFMAs over d = 128; K straight from memory,
+//   S^T = K Q^T          (8 MFMAs over d = 128; K straight from memory,
 //                         each lane a contiguous 128 bytes of one key row)
 //   causal mask, online softmax in the log2 domain (each lane holds 16 keys
 //   of one query; one exchange with the other half-wave gives the tile max)
-//   O += P V             (16 MFMAs: the 16 probabilities a lane holds are,
-//                         converted to bf16, exactly its A operand; V is
-//                         staged transposed in LDS, double-buffered, so each
-//                         B operand is one 8-byte LDS read)
-// The contraction over d uses the order lane half h -> d in [64 h, 64 h + 64)
-// for both K and Q (any common order of d gives the same dot products).  A
+//   O += P V             (8 MFMAs: the 16 probabilities a lane holds are,
+//                         converted to bf16, its A operands for the tile's
+//                         two 16-key steps; V is staged transposed in LDS,
+//                         double-buffered, so a B operand is two 8-byte reads)
+// A contraction may take its index in any order common to both operands: over
+// d, lane half h takes d in [64 h, 64 h + 64); over the keys of a 16-key step
+// s, element i of lane half h is key 16 s + 8 (i / 4) + 4 h + i % 4, which is
+// where the S^T accumulator already holds it.  A
 // chunk's per-query partials (max, sum, unnormalised O) go to the workspace
 // and a second kernel merges the chunks by the log-sum-exp rule.
 //
-// Lane layout of v_mfma_f32_32x32x8_bf16 (checked on the device): lane l
-// holds A[l % 32][4 (l / 32) + i], B[4 (l / 32) + i][l % 32] (i < 4) and
+// Lane layout of v_mfma_f32_32x32x16_bf16 (checked on the device): lane l
+// holds A[l % 32][8 (l / 32) + i], B[8 (l / 32) + i][l % 32] (i < 8) and
 // D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] in accumulator r < 16.
 
 #include "common.hpp"
@@ -33,24 +36,24 @@
 namespace lychee {
 namespace {
 
-typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kD = 128;               // head dim of the MFMA path
 constexpr int kTile = 32;             // keys per tile
 constexpr int kVtStride = kTile + 4;  // bf16 per transposed V row in LDS (padded)
 
-__device__ __forceinline__ short f2bf(float f) {       // round to nearest even
+__device__ __forceinline__ __bf16 f2bf(float f) {      // round to nearest even
     uint32_t u = __builtin_bit_cast(uint32_t, f);
     u += 0x7FFFu + ((u >> 16) & 1u);
-    return (short)(u >> 16);
+    return __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
 }
 
 // row of accumulator register r for lane half h
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 template <int G>
-__global__ void __launch_bounds__(64 * G) correction_partial_kernel(CorrParams p) {
+__global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_kernel(CorrParams p) {   // 2 waves per SIMD (G >= 4)
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, c32 = lane & 31;
     const int bg = blockIdx.x / p.nchunks, chunk = blockIdx.x - bg * p.nchunks;
     const int b = bg / p.Hkv, g = bg - b * p.Hkv;
@@ -72,35 +75,67 @@ __global__ void __launch_bounds__(64 * G) correction_partial_kernel(CorrParams p
     // this lane's query: t = c32 (rows t >= T repeat row T - 1, ignored at the end)
     const int tq = min(c32, T - 1);
     const int pos_q = n - T + c32;     // causal limit of query c32 (keys <= pos_q)
-    v4s qop[16];
+    v8bf qop[8];
     {
         const uint4* qr = reinterpret_cast<const uint4*>(
             reinterpret_cast<const uint16_t*>(p.q) + (((size_t)b * T + tq) * Hq + (size_t)g * G + w) * kD + 64 * h);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const uint4 v = qr[c];
-            qop[2 * c] = __builtin_bit_cast(v4s, make_uint2(v.x, v.y));
-            qop[2 * c + 1] = __builtin_bit_cast(v4s, make_uint2(v.z, v.w));
-        }
+        for (int c = 0; c < 8; ++c) qop[c] = __builtin_bit_cast(v8bf, qr[c]);
     }
     v16f acc_o[4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) acc_o[t4] = v16f{};
     float m_run = -INFINITY, l_part = 0.0f;
 
-    // stage the V tile starting at key k0 into s_vt[buf], transposed
-    auto stage_v = [&](int k0, int buf) {
-        constexpr int kChunks = kTile * kD / 8;              // 16-byte pieces of the tile
+    // the V tile starting at key k0: 16-byte pieces (8 columns of one key),
+    // loaded a tile ahead into registers, then stored transposed into
+    // s_vt[buf] at the end of the current tile.  With an even number of pieces
+    // per thread, a thread takes pairs of consecutive keys (pair j: keys 2 kp,
+    // 2 kp + 1 with kp = (tid + 64 G j) / 16) and writes both keys of a column
+    // as one 32-bit word; otherwise piece j is key (tid + 64 G j) / 16 alone.
+    constexpr int kPieces = kTile * kD / 8 / (64 * G);
+    constexpr bool kPairs = kPieces % 2 == 0;
+    auto piece_key = [&](int j) -> int {
+        if constexpr (kPairs) return 2 * ((threadIdx.x + 64 * G * (j >> 1)) >> 4) + (j & 1);
+        else return (threadIdx.x + 64 * G * j) >> 4;
+    };
+    auto piece_d0 = [&](int j) -> int {
+        if constexpr (kPairs) return ((threadIdx.x + 64 * G * (j >> 1)) & 15) * 8;
+        else return ((threadIdx.x + 64 * G * j) & 15) * 8;
+    };
+    auto load_v = [&](int k0, uint4* vr) {
 #pragma unroll
-        for (int ci = threadIdx.x; ci < kChunks; ci += 64 * G) {
-            const int key = ci >> 4, d0 = (ci & 15) * 8;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (k0 + key < c1) v = *reinterpret_cast<const uint4*>(vc + (kv_row0 + (size_t)(k0 + key)) * kD + d0);
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+        for (int j = 0; j < kPieces; ++j) {
+            const int key = piece_key(j), d0 = piece_d0(j);
+            vr[j] = make_uint4(0u, 0u, 0u, 0u);
+            if (k0 + key < c1) vr[j] = *reinterpret_cast<const uint4*>(vc + (kv_row0 + (size_t)(k0 + key)) * kD + d0);
+        }
+    };
+    auto store_v = [&](const uint4* vr, int buf) {
+        if constexpr (kPairs) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s_vt[buf][(d0 + 2 * i) * kVtStride + key] = (uint16_t)(wv[i] & 0xFFFFu);
-                s_vt[buf][(d0 + 2 * i + 1) * kVtStride + key] = (uint16_t)(wv[i] >> 16);
+            for (int j = 0; j < kPieces; j += 2) {
+                const int key = piece_key(j), d0 = piece_d0(j);      // key even; key + 1 in piece j + 1
+                const uint32_t a[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+                const uint32_t c[4] = {vr[j + 1].x, vr[j + 1].y, vr[j + 1].z, vr[j + 1].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    *reinterpret_cast<uint32_t*>(&s_vt[buf][(d0 + 2 * i) * kVtStride + key]) =
+                        (a[i] & 0xFFFFu) | (c[i] << 16);
+                    *reinterpret_cast<uint32_t*>(&s_vt[buf][(d0 + 2 * i + 1) * kVtStride + key]) =
+                        (a[i] >> 16) | (c[i] & 0xFFFF0000u);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kPieces; ++j) {
+                const int key = piece_key(j), d0 = piece_d0(j);
+                const uint32_t wv[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s_vt[buf][(d0 + 2 * i) * kVtStride + key] = (uint16_t)(wv[i] & 0xFFFFu);
+                    s_vt[buf][(d0 + 2 * i + 1) * kVtStride + key] = (uint16_t)(wv[i] >> 16);
+                }
             }
         }
     };
@@ -111,29 +146,33 @@ __global__ void __launch_bounds__(64 * G) correction_partial_kernel(CorrParams p
         for (int c = 0; c < 8; ++c) kr[c] = src[c];
     };
 
+    // Two register sets per operand, alternating: at tile it, K of tiles it and
+    // it + 1 and V of tile it + 1 are in registers (V of tile it is in LDS);
+    // the loads of tile it + 2 are issued during tile it, so each has about
+    // two tiles of work to arrive.
     const int ntiles = c1 > c0 ? (c1 - c0 + kTile - 1) / kTile : 0;
-    uint4 kcur[8], knext[8];
+    uint4 kA[8], kB[8], vA[kPieces], vB[kPieces];
     if (ntiles > 0) {
-        load_k(c0, kcur);
-        stage_v(c0, 0);
+        load_k(c0, kA);
+        load_v(c0, vA);
+        if (ntiles > 1) {
+            load_k(c0 + kTile, kB);
+            load_v(c0 + kTile, vB);
+        }
+        store_v(vA, 0);
     }
     __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
+    // tile it with K in kx, its V in LDS, the next tile's V in vy; vx is free
+    auto tile = [&](int it, uint4 (&kx)[8], uint4 (&vx)[kPieces], uint4 (&vy)[kPieces]) {
         const int k0 = c0 + it * kTile;
         const int buf = it & 1;
-        if (it + 1 < ntiles) {           // next tile in flight during this one
-            load_k(k0 + kTile, knext);
-            stage_v(k0 + kTile, buf ^ 1);
-        }
+        if (it + 2 < ntiles) load_v(k0 + 2 * kTile, vx);
         // S^T = K Q^T
         v16f s = v16f{};
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const v4s a0 = __builtin_bit_cast(v4s, make_uint2(kcur[c].x, kcur[c].y));
-            const v4s a1 = __builtin_bit_cast(v4s, make_uint2(kcur[c].z, kcur[c].w));
-            s = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a0, qop[2 * c], s, 0, 0, 0);
-            s = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a1, qop[2 * c + 1], s, 0, 0, 0);
-        }
+        for (int c = 0; c < 8; ++c)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kx[c]), qop[c], s, 0, 0, 0);
+        if (it + 2 < ntiles) load_k(k0 + 2 * kTile, kx);   // this set's K registers are free again
         // causal mask and the tile max of this lane's query
         float z[16];
         float mt = -INFINITY;
@@ -163,30 +202,36 @@ __global__ void __launch_bounds__(64 * G) correction_partial_kernel(CorrParams p
                 for (int t4 = 0; t4 < 4; ++t4) acc_o[t4][r] *= ar;
             }
         }
-        // probabilities (this lane's 16 keys of its query), as the A operand of P V
-        v4s pa[4];
+        // probabilities (this lane's 16 keys of its query): accumulators 8 s ..
+        // 8 s + 7 are the A operand of 16-key step s
+        v8bf pa[2];
         float ls = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float pr = z[r] == -INFINITY ? 0.0f : exp2f(z[r] - m_run);
             ls += pr;
-            pa[r >> 2][r & 3] = f2bf(pr);
+            pa[r >> 3][r & 7] = f2bf(pr);
         }
         l_part += ls;
-        // O += P V (B operand: 4 consecutive keys of one d column of V^T)
+        // O += P V (B operand of step s: keys 16 s + 4 h + 0..3 and 16 s + 8 + 4 h
+        // + 0..3 of one d column of V^T)
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const uint2 bv = *reinterpret_cast<const uint2*>(&s_vt[buf][(32 * t4 + c32) * kVtStride + 8 * ks + 4 * h]);
-                acc_o[t4] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(pa[ks], __builtin_bit_cast(v4s, bv), acc_o[t4], 0, 0, 0);
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint16_t* col = &s_vt[buf][(32 * t4 + c32) * kVtStride + 16 * ks + 4 * h];
+                const uint2 lo = *reinterpret_cast<const uint2*>(col);
+                const uint2 hi = *reinterpret_cast<const uint2*>(col + 8);
+                const v8bf bv = __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                acc_o[t4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bv, acc_o[t4], 0, 0, 0);
             }
         }
-        __syncthreads();                 // buf is restaged two tiles on; buf ^ 1 is complete
-        if (it + 1 < ntiles) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) kcur[c] = knext[c];
-        }
+        if (it + 1 < ntiles) store_v(vy, buf ^ 1);     // (buf ^ 1 was last read before the previous barrier)
+        __syncthreads();                 // buf ^ 1 complete; buf is restaged only after the next barrier
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+        tile(it, kA, vA, vB);
+        if (it + 1 < ntiles) tile(it + 1, kB, vB, vA);
     }
 
     // partials of this chunk: per query row (w, q): m (log2), l, unnormalised O
@@ -203,43 +248,58 @@ __global__ void __launch_bounds__(64 * G) correction_partial_kernel(CorrParams p
             p.rec_o[(rec + (size_t)w * 32 + acc_row(r, h)) * kD + 32 * t4 + c32] = acc_o[t4][r];
 }
 
-// Merge the chunks of one (sequence, query head): 32 rows x 128 columns, one
-// row and 16 columns per thread; chunks in order (log-sum-exp).
+// Merge the chunks of one query row (sequence, query head, position): 128
+// threads, one output column each.  The chunks' scales 2^(m_c - M) and the
+// normaliser go through LDS first; then every thread sums its column over the
+// chunks in order (coalesced 512-byte rows, independent loads).
 template <int G>
-__global__ void __launch_bounds__(256) correction_combine_kernel(CorrParams p) {
-    const int bg = blockIdx.x / G, w = blockIdx.x - bg * G;
+__global__ void __launch_bounds__(kD) correction_combine_kernel(CorrParams p) {
+    constexpr int kMaxChunksLds = 1024;
+    __shared__ float s_scale[kMaxChunksLds];
+    __shared__ float s_red[kD / 64];
+    const int row = blockIdx.x % 32, qh = blockIdx.x / 32;       // qh = bg * G + w
+    const int bg = qh / G, w = qh - bg * G;
     const int b = bg / p.Hkv, g = bg - b * p.Hkv;
-    const int row = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * 16;
     if (row >= p.T) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Hq = p.Hkv * G;
-    float M = -INFINITY;
-    for (int c = 0; c < p.nchunks; ++c) {
-        const size_t r = ((size_t)(bg * p.nchunks + c) * (32 * G) + (size_t)w * 32 + row);
-        M = fmaxf(M, p.rec_ml[r * 2]);
+    const int nc = min(p.nchunks, kMaxChunksLds);
+    auto rec_row = [&](int c) -> size_t { return (size_t)(bg * p.nchunks + c) * (32 * G) + (size_t)w * 32 + row; };
+    float m = -INFINITY;
+    for (int c = tid; c < nc; c += kD) m = fmaxf(m, p.rec_ml[rec_row(c) * 2]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    float M = s_red[0];
+#pragma unroll
+    for (int i = 1; i < kD / 64; ++i) M = fmaxf(M, s_red[i]);
+    float lsum = 0.0f;
+    for (int c = tid; c < nc; c += kD) {
+        const float mc = p.rec_ml[rec_row(c) * 2];
+        const float sc = mc == -INFINITY ? 0.0f : exp2f(mc - M);
+        s_scale[c] = sc;
+        lsum += sc * p.rec_ml[rec_row(c) * 2 + 1];
     }
-    float L = 0.0f, o[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[i] = 0.0f;
-    for (int c = 0; c < p.nchunks; ++c) {
-        const size_t r = ((size_t)(bg * p.nchunks + c) * (32 * G) + (size_t)w * 32 + row);
-        const float m = p.rec_ml[r * 2];
-        if (m == -INFINITY) continue;
-        const float sc = exp2f(m - M);
-        L += p.rec_ml[r * 2 + 1] * sc;
-        const float4* src = reinterpret_cast<const float4*>(p.rec_o + r * kD + d0);
+    for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+    __syncthreads();                   // s_red is reused; s_scale complete
+    if (lane == 0) s_red[wave] = lsum;
+    __syncthreads();
+    float L = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 v = src[i];
-            o[4 * i + 0] += v.x * sc;
-            o[4 * i + 1] += v.y * sc;
-            o[4 * i + 2] += v.z * sc;
-            o[4 * i + 3] += v.w * sc;
-        }
+    for (int i = 0; i < kD / 64; ++i) L += s_red[i];
+    float acc = 0.0f;
+    int c = 0;
+    for (; c + 8 <= nc; c += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = p.rec_o[rec_row(c + j) * kD + tid];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += v[j] * s_scale[c + j];
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    float4* dst = reinterpret_cast<float4*>(p.out + (((size_t)b * p.T + row) * Hq + (size_t)g * G + w) * kD + d0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_float4(o[4 * i] * inv, o[4 * i + 1] * inv, o[4 * i + 2] * inv, o[4 * i + 3] * inv);
+    for (; c < nc; ++c) acc += p.rec_o[rec_row(c) * kD + tid] * s_scale[c];
+    p.out[(((size_t)b * p.T + row) * Hq + (size_t)g * G + w) * kD + tid] = L > 0.0f ? acc / L : 0.0f;
 }
 
 // Algorithm 1's cache append: row n_ctx[b] of every (b, g) gets the new K and
@@ -273,7 +333,7 @@ hipError_t launch_g(const CorrParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(correction_partial_kernel<G>, dim3(p.B * p.Hkv * p.nchunks), dim3(64 * G), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(correction_combine_kernel<G>, dim3(p.B * p.Hkv * G), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(correction_combine_kernel<G>, dim3(p.B * p.Hkv * G * 32), dim3(kD), 0, stream, p);
     return hipGetLastError();
 }
 
