@@ -605,9 +605,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 const int mid = (a + z + 1) >> 1;
                 if (s_pref[mid] <= raw) a = mid; else z = mid - 1;
             }
-            static_assert(kCostRetrieval == 4 && kCostSparse == 7, "row snapping below uses the costs 4 and 7");
             const uint32_t h0 = s_pref[a], h1 = s_pref[a + 1], off = raw - h0;
-            const uint32_t up = is_retr(a) ? ((off + 3u) & ~3u) : 7u * ((off + 6u) / 7u);   // next row start
+            const uint32_t cwa = is_retr(a) ? kCostRetrieval : kCostSparse;
+            const uint32_t up = cwa * ((off + cwa - 1u) / cwa);   // next row start
             bnd = min(h0 + up, h1);
         }
         s_bound[ww] = bnd;
