@@ -21,10 +21,10 @@ constexpr int kWaves = kAttendThreads / 64;
 constexpr int kCombineFanIn = 32;     // level-1 combine groups of consecutive workgroups
 constexpr int kLevel2Max = kMaxWG / kCombineFanIn + 2;
 // Pool cost of one unit of work: a streamed key row (retrieval head) costs 4,
-// a gathered S row (sparse head) 8.  Gathers of scattered 256-byte rows run
-// at about half the streaming rate, and giving the sparse workgroups fewer
-// rows lets them finish while the retrieval heads' selection runs: 8 measured
-// best among 7, 8 and 9 (and retrieval costs 3, 5, 6, 8) on the 128K step.
+// a gathered S row (sparse head) 8 -- gathers of scattered 256-byte rows run
+// at about half the streaming rate.  8 measured best on the 128K step against
+// 7 and 9 (and against retrieval costs 3, 5, 6 and 8): a dearer sparse row
+// gives the sparse workgroups fewer rows and the retrieval workgroups more.
 constexpr uint32_t kCostRetrieval = 4;
 constexpr uint32_t kCostSparse = 8;
 constexpr uint32_t kMinCostPerWG = 64 * kCostSparse;   // never split the pool finer than this
