@@ -14,7 +14,10 @@
 //   S^T = K Q^T          (8 MFMAs over d = 128; K straight from memory,
 //                         each lane a contiguous 128 bytes of one key row)
 //   causal mask, online softmax in the log2 domain (each lane holds 16 keys
-//   of one query; one exchange with the other half-wave gives the tile max)
+//   of one query; one exchange with the other half-wave gives the tile max;
+//   a tile that every query sees whole skips the mask, and its exponent is
+//   one fma of the raw score); probabilities go to bf16 by the hardware
+//   round-to-nearest-even conversion
 //   O += P V             (8 MFMAs: the 16 probabilities a lane holds are,
 //                         converted to bf16, its A operands for the tile's
 //                         two 16-key steps; V is staged transposed in LDS,
@@ -42,12 +45,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kD = 128;               // head dim of the MFMA path
 constexpr int kTile = 32;             // keys per tile
 constexpr int kVtStride = kTile + 4;  // bf16 per transposed V row in LDS (padded)
-
-__device__ __forceinline__ __bf16 f2bf(float f) {      // round to nearest even
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
-}
 
 // row of accumulator register r for lane half h
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -176,12 +173,22 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
         // causal mask and the tile max of this lane's query
         float z[16];
         float mt = -INFINITY;
+        // every key of the tile visible to every query (wavefront-uniform):
+        // no mask, and the scale (positive) applies to the raw maximum
+        const bool full = k0 + kTile <= c1 && k0 + kTile - 1 <= n - T;
+        if (full) {
+            float ms = s[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = k0 + acc_row(r, h);
-            const bool ok = key < c1 && key <= pos_q;
-            z[r] = ok ? s[r] * p.scale_log2 : -INFINITY;
-            mt = fmaxf(mt, z[r]);
+            for (int r = 1; r < 16; ++r) ms = fmaxf(ms, s[r]);
+            mt = ms * p.scale_log2;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + acc_row(r, h);
+                const bool ok = key < c1 && key <= pos_q;
+                z[r] = ok ? s[r] * p.scale_log2 : -INFINITY;
+                mt = fmaxf(mt, z[r]);
+            }
         }
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float m_new = fmaxf(m_run, mt);
@@ -206,11 +213,20 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
         // 8 s + 7 are the A operand of 16-key step s
         v8bf pa[2];
         float ls = 0.0f;
+        if (full) {                      // m_run is finite here
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pr = z[r] == -INFINITY ? 0.0f : exp2f(z[r] - m_run);
-            ls += pr;
-            pa[r >> 3][r & 7] = f2bf(pr);
+            for (int r = 0; r < 16; ++r) {
+                const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.scale_log2, -m_run));
+                ls += pr;
+                pa[r >> 3][r & 7] = (__bf16)pr;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pr = z[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(z[r] - m_run);
+                ls += pr;
+                pa[r >> 3][r & 7] = (__bf16)pr;
+            }
         }
         l_part += ls;
         // O += P V (B operand of step s: keys 16 s + 4 h + 0..3 and 16 s + 8 + 4 h
