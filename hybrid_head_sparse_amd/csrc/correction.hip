@@ -100,13 +100,21 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
         if constexpr (kPairs) return ((threadIdx.x + 64 * G * (j >> 1)) & 15) * 8;
         else return ((threadIdx.x + 64 * G * j) & 15) * 8;
     };
+    // Every load is issued on every path (rows past the chunk are clamped to
+    // its last row, V pieces there are zeroed after the load): the compiler's
+    // wait counts are then exact, and a tile waits for its own operands only,
+    // not for the loads issued ahead of it.
     auto load_v = [&](int k0, uint4* vr) {
 #pragma unroll
         for (int j = 0; j < kPieces; ++j) {
             const int key = piece_key(j), d0 = piece_d0(j);
-            vr[j] = make_uint4(0u, 0u, 0u, 0u);
-            if (k0 + key < c1) vr[j] = *reinterpret_cast<const uint4*>(vc + (kv_row0 + (size_t)(k0 + key)) * kD + d0);
+            vr[j] = *reinterpret_cast<const uint4*>(vc + (kv_row0 + (size_t)min(k0 + key, c1 - 1)) * kD + d0);
         }
+    };
+    auto zero_v_tail = [&](int k0, uint4* vr) {       // V rows past the chunk contribute 0
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j)
+            if (k0 + piece_key(j) >= c1) vr[j] = make_uint4(0u, 0u, 0u, 0u);
     };
     auto store_v = [&](const uint4* vr, int buf) {
         if constexpr (kPairs) {
@@ -152,10 +160,9 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
     if (ntiles > 0) {
         load_k(c0, kA);
         load_v(c0, vA);
-        if (ntiles > 1) {
-            load_k(c0 + kTile, kB);
-            load_v(c0 + kTile, vB);
-        }
+        load_k(c0 + kTile, kB);
+        load_v(c0 + kTile, vB);
+        zero_v_tail(c0, vA);
         store_v(vA, 0);
     }
     __syncthreads();
@@ -163,13 +170,13 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
     auto tile = [&](int it, uint4 (&kx)[8], uint4 (&vx)[kPieces], uint4 (&vy)[kPieces]) {
         const int k0 = c0 + it * kTile;
         const int buf = it & 1;
-        if (it + 2 < ntiles) load_v(k0 + 2 * kTile, vx);
+        load_v(k0 + 2 * kTile, vx);
         // S^T = K Q^T
         v16f s = v16f{};
 #pragma unroll
         for (int c = 0; c < 8; ++c)
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kx[c]), qop[c], s, 0, 0, 0);
-        if (it + 2 < ntiles) load_k(k0 + 2 * kTile, kx);   // this set's K registers are free again
+        load_k(k0 + 2 * kTile, kx);   // this set's K registers are free again
         // causal mask and the tile max of this lane's query
         float z[16];
         float mt = -INFINITY;
@@ -242,13 +249,18 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
                 acc_o[t4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bv, acc_o[t4], 0, 0, 0);
             }
         }
-        if (it + 1 < ntiles) store_v(vy, buf ^ 1);     // (buf ^ 1 was last read before the previous barrier)
+        if (it + 1 < ntiles) {
+            zero_v_tail(k0 + kTile, vy);
+            store_v(vy, buf ^ 1);     // (buf ^ 1 was last read before the previous barrier)
+        }
         __syncthreads();                 // buf ^ 1 complete; buf is restaged only after the next barrier
     };
-    for (int it = 0; it < ntiles; it += 2) {
+    int it = 0;
+    for (; it + 1 < ntiles; it += 2) {
         tile(it, kA, vA, vB);
-        if (it + 1 < ntiles) tile(it + 1, kB, vB, vA);
+        tile(it + 1, kB, vB, vA);
     }
+    if (it < ntiles) tile(it, kA, vA, vB);
 
     // partials of this chunk: per query row (w, q): m (log2), l, unnormalised O
     const size_t rec = (size_t)blockIdx.x * (32 * G);
