@@ -10,7 +10,7 @@
 //
 // Work pooling.  All (head, row) work -- a row is one streamed key of a
 // retrieval head or one gathered S row of a sparse head -- is laid on one cost
-// axis (a gathered row weighs 7/4 of a streamed one) and cut into equal
+// axis (a gathered row weighs twice a streamed one) and cut into equal
 // contiguous ranges, one per persistent workgroup, as the digest's kernel
 // description asks (equal-size splits spread over all thread blocks).  Each
 // range yields one partial (m, l, o) record per head it touches; the last
