@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
     const int n = min(p.n_ctx[b], p.max_ctx);
     const int T = p.T;
     const int Hq = p.Hkv * G;
-    if (n < T) {                       // out of contract: flagged, partials stay empty
+    if (n < T) {                       // out of contract: flagged, the rows are undefined
         if (threadIdx.x == 0 && chunk == 0) atomicOr(p.err, 4u);
     }
     const int c0 = (int)(((long long)n * chunk) / p.nchunks);

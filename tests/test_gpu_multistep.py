@@ -81,7 +81,7 @@ def _correction_case(w: synth.Workload, T: int, seed: int, lens):
     return synth.to_bf16_bits(q), x["k"], x["v"], np.asarray(lens, np.int32)
 
 
-@pytest.mark.parametrize("T, G", [(32, 4), (7, 4), (1, 4), (32, 1), (32, 8)])
+@pytest.mark.parametrize("T, G", [(32, 4), (7, 4), (1, 4), (32, 1), (32, 8), (32, 2), (13, 2)])
 def test_correction_attention_matches_the_oracle(T, G):
     import torch
     Hkv = 8 if G < 8 else 4
@@ -99,6 +99,47 @@ def test_correction_attention_matches_the_oracle(T, G):
     assert np.all(np.isfinite(got))
     err = np.abs(got - ref).max()
     log(f"[correction T={T} G={G}] max|err| = {err:.2e}")
+    assert err <= OUT_TOL
+
+
+def test_correction_attention_over_a_context_of_exactly_T():
+    """n = T: the whole context is the causal triangle (row t sees rows 0..t),
+    beside a longer sequence in the same call."""
+    import torch
+    T = 32
+    w = synth.Workload("corr_tri", 68, 2, 1, 32, 8, 128, 4096, 64, "bf16", 0, ctx_list=(T, 300), hh_frac=0.01)
+    q, kc, vc, lens = _correction_case(w, T, 78, w.ctx_list)
+    h = _handle(2, 32, 8, 128, 4096, "bf16")
+    out = torch.full((2, T, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
+    h.correction_attention(to_device(q, "bf16"), to_device(kc, "bf16"), to_device(vc, "bf16"),
+                           torch.from_numpy(lens).cuda(), out)
+    torch.cuda.synchronize()
+    h.check_device_errors()
+    err = np.abs(out.cpu().numpy() - oracle.correction_attention(q, kc, vc, lens)).max()
+    log(f"[correction n = T = {T}] max|err| = {err:.2e}")
+    assert err <= OUT_TOL
+
+
+def test_correction_attention_over_a_context_shorter_than_T_is_flagged():
+    """n < T is outside the contract: the device flag latches (the rows are
+    undefined, so only the flag is checked) and later calls run normally."""
+    import torch
+    import hybrid_head_sparse_amd as hhs
+    T = 8
+    w = synth.Workload("corr_short", 69, 1, 1, 32, 8, 128, 1024, 64, "bf16", 0, ctx_list=(600,), hh_frac=0.01)
+    q, kc, vc, lens2 = _correction_case(w, T, 79, [600])
+    h = _handle(1, 32, 8, 128, 1024, "bf16")
+    q_d, kc_d, vc_d = to_device(q, "bf16"), to_device(kc, "bf16"), to_device(vc, "bf16")
+    out = torch.empty((1, T, 32, 128), dtype=torch.float32, device="cuda")
+    h.correction_attention(q_d, kc_d, vc_d, torch.tensor([5], dtype=torch.int32, device="cuda"), out)
+    with pytest.raises(hhs.LycheeError):
+        h.check_device_errors()
+    # the same cache and queries within the contract
+    h.correction_attention(q_d, kc_d, vc_d, torch.from_numpy(lens2).cuda(), out)
+    torch.cuda.synchronize()
+    h.check_device_errors()
+    err = np.abs(out.cpu().numpy() - oracle.correction_attention(q, kc, vc, lens2)).max()
+    log(f"[correction n < T flagged, then n = 600] max|err| = {err:.2e}")
     assert err <= OUT_TOL
 
 
