@@ -200,3 +200,103 @@ def test_append_then_correct_then_decode_chain():
                                "bf16")
     log(f"[loop] decode layer at n = {int(n[0])}: max|err| = {err1:.2e}, band diffs {band}")
     h.check_device_errors()
+
+
+def _raw(t):
+    """The tensor's bit patterns (the cache holds NaN rows past the context,
+    which compare unequal to themselves as floats)."""
+    import torch
+    return t.view({torch.bfloat16: torch.int16, torch.float32: torch.int32}.get(t.dtype, t.dtype))
+
+
+def test_loop_kernels_replay_from_a_graph():
+    """Append, correction, and a hybrid layer under the Top-p and the block
+    rule (each with the rule-selection kernel after the attention kernel),
+    captured once into a HIP graph: three replays, with the cache and n_ctx
+    restored eagerly between them, each reproduce the eager run bitwise, and
+    the eager layers meet the parity bar against the oracle."""
+    import torch
+    w = synth.Workload("loop_graph", 71, 1, 1, 32, 8, 128, 4096, 256, "bf16", 0, ctx_list=(3000,), hh_frac=0.01)
+    rng = np.random.default_rng(81)
+    x = synth.layer_inputs(w, 0)
+    h = _handle(1, 32, 8, 128, 4096, "bf16", k_max=256)
+    kc0, vc0 = to_device(x["k"], "bf16"), to_device(x["v"], "bf16")
+    n0 = torch.tensor([3000], dtype=torch.int32, device="cuda")
+    kc, vc, n_d = kc0.clone(), vc0.clone(), n0.clone()
+    T, k = 6, 256
+    kn = to_device(synth.to_bf16_bits(rng.standard_normal((1, 8, 128)).astype(np.float32) / np.sqrt(128)), "bf16")
+    vn = to_device(synth.to_bf16_bits(rng.standard_normal((1, 8, 128)).astype(np.float32)), "bf16")
+    qc = to_device(synth.to_bf16_bits(rng.standard_normal((1, T, 32, 128)).astype(np.float32) / np.sqrt(128)), "bf16")
+    q1_np = synth.to_bf16_bits(rng.standard_normal((1, 32, 128)).astype(np.float32) / np.sqrt(128))
+    q1 = to_device(q1_np, "bf16")
+    # S_in of the hybrid layers: an all-retrieval layer over the grown cache, outside the graph
+    S0 = torch.empty((1, 8, k), dtype=torch.int32, device="cuda")
+    o0 = torch.empty((1, 32, 128), dtype=torch.float32, device="cuda")
+    role = np.array([1, 0, 0, 0, 0, 1, 0, 0], np.uint8)
+    oc = torch.empty((1, T, 32, 128), dtype=torch.float32, device="cuda")
+    Sp, Sb = torch.empty_like(S0), torch.empty_like(S0)
+    op, ob = torch.empty_like(o0), torch.empty_like(o0)
+
+    def body():
+        h.kv_append(kn, vn, kc, vc, n_d)
+        h.correction_attention(qc, kc, vc, n_d, oc)
+        h.decode_layer(q1, kc, vc, role, S0, Sp, op, n_d, k, rule="topp", param=0.05)
+        h.decode_layer(q1, kc, vc, role, S0, Sb, ob, n_d, k, rule="block", param=32)
+
+    def restore():
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        n_d.copy_(n0)
+
+    outs = (kc, n_d, oc, Sp, op, Sb, ob)
+    # eager reference (S0 from the grown cache first)
+    h.kv_append(kn, vn, kc, vc, n_d)
+    h.decode_layer(q1, kc, vc, np.ones(8, np.uint8), None, S0, o0, n_d, k)
+    restore()
+    body()
+    torch.cuda.synchronize()
+    h.check_device_errors()
+    ref = [t.cpu().clone() for t in outs]
+    # capture on a side stream after a warm-up there, as torch requires
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        h.set_stream(cap)
+        restore()
+        body()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    restore()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        h.set_stream(torch.cuda.current_stream())
+        body()
+    h.set_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for rep in range(3):
+        restore()
+        for t in (oc, op, ob):
+            t.fill_(float("nan"))
+        for t in (Sp, Sb):
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(("k_cache", "n_ctx", "correction", "S topp", "out topp", "S block", "out block"),
+                              outs, ref):
+            assert torch.equal(_raw(t.cpu()), _raw(r)), f"replay {rep}: {name} differs from the eager run"
+        log(f"[loop graph] replay {rep} bitwise equal to the eager run")
+    h.check_device_errors()
+    # the eager append byte for byte, and the eager layers against the oracle
+    # over the grown cache
+    kc_np, vc_np = x["k"].copy(), x["v"].copy()
+    n_np = oracle.kv_append(_bits(kn), _bits(vn), kc_np, vc_np, np.array([3000], np.int32))
+    np.testing.assert_array_equal(_bits(ref[0]), kc_np)
+    np.testing.assert_array_equal(ref[1].numpy(), n_np)
+    inputs = {"q": q1_np, "k": kc_np, "v": vc_np}
+    S0_np = S0.cpu().numpy()
+    for rule, param, S_t, o_t in (("topp", 0.05, ref[3], ref[4]), ("block", 32, ref[5], ref[6])):
+        err, band = compare_layer(o_t.numpy(), S_t.numpy(), inputs, role, S0_np, n_np, k, "bf16", rule=rule,
+                                  param=param)
+        log(f"[loop graph] {rule} layer: max|err| = {err:.2e}, band diffs {band}")
