@@ -211,8 +211,8 @@ def _raw(t):
 
 def test_loop_kernels_replay_from_a_graph():
     """Append, correction, and a hybrid layer under the Top-p and the block
-    rule (each with the rule-selection kernel after the attention kernel),
-    captured once into a HIP graph: three replays, with the cache and n_ctx
+    rule (each with the rule-selection kernel after the attention kernel) and
+    under the Ratio and Threshold rules (in the attention kernel), captured once into a HIP graph: three replays, with the cache and n_ctx
     restored eagerly between them, each reproduce the eager run bitwise, and
     the eager layers meet the parity bar against the oracle."""
     import torch
@@ -234,21 +234,23 @@ def test_loop_kernels_replay_from_a_graph():
     o0 = torch.empty((1, 32, 128), dtype=torch.float32, device="cuda")
     role = np.array([1, 0, 0, 0, 0, 1, 0, 0], np.uint8)
     oc = torch.empty((1, T, 32, 128), dtype=torch.float32, device="cuda")
-    Sp, Sb = torch.empty_like(S0), torch.empty_like(S0)
-    op, ob = torch.empty_like(o0), torch.empty_like(o0)
+    Sp, Sb, Sr, St = (torch.empty_like(S0) for _ in range(4))
+    op, ob, orr, ot = (torch.empty_like(o0) for _ in range(4))
 
     def body():
         h.kv_append(kn, vn, kc, vc, n_d)
         h.correction_attention(qc, kc, vc, n_d, oc)
         h.decode_layer(q1, kc, vc, role, S0, Sp, op, n_d, k, rule="topp", param=0.05)
         h.decode_layer(q1, kc, vc, role, S0, Sb, ob, n_d, k, rule="block", param=32)
+        h.decode_layer(q1, kc, vc, role, S0, Sr, orr, n_d, k, rule="ratio", param=0.02)
+        h.decode_layer(q1, kc, vc, role, S0, St, ot, n_d, k, rule="threshold", param=0.01)
 
     def restore():
         kc.copy_(kc0)
         vc.copy_(vc0)
         n_d.copy_(n0)
 
-    outs = (kc, n_d, oc, Sp, op, Sb, ob)
+    outs = (kc, n_d, oc, Sp, op, Sb, ob, Sr, orr, St, ot)
     # eager reference (S0 from the grown cache first)
     h.kv_append(kn, vn, kc, vc, n_d)
     h.decode_layer(q1, kc, vc, np.ones(8, np.uint8), None, S0, o0, n_d, k)
@@ -276,15 +278,15 @@ def test_loop_kernels_replay_from_a_graph():
     torch.cuda.synchronize()
     for rep in range(3):
         restore()
-        for t in (oc, op, ob):
+        for t in (oc, op, ob, orr, ot):
             t.fill_(float("nan"))
-        for t in (Sp, Sb):
+        for t in (Sp, Sb, Sr, St):
             t.fill_(-7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, t, r in zip(("k_cache", "n_ctx", "correction", "S topp", "out topp", "S block", "out block"),
-                              outs, ref):
+        for name, t, r in zip(("k_cache", "n_ctx", "correction", "S topp", "out topp", "S block", "out block",
+                               "S ratio", "out ratio", "S threshold", "out threshold"), outs, ref):
             assert torch.equal(_raw(t.cpu()), _raw(r)), f"replay {rep}: {name} differs from the eager run"
         log(f"[loop graph] replay {rep} bitwise equal to the eager run")
     h.check_device_errors()
@@ -296,7 +298,8 @@ def test_loop_kernels_replay_from_a_graph():
     np.testing.assert_array_equal(ref[1].numpy(), n_np)
     inputs = {"q": q1_np, "k": kc_np, "v": vc_np}
     S0_np = S0.cpu().numpy()
-    for rule, param, S_t, o_t in (("topp", 0.05, ref[3], ref[4]), ("block", 32, ref[5], ref[6])):
+    for rule, param, S_t, o_t in (("topp", 0.05, ref[3], ref[4]), ("block", 32, ref[5], ref[6]),
+                                  ("ratio", 0.02, ref[7], ref[8]), ("threshold", 0.01, ref[9], ref[10])):
         err, band = compare_layer(o_t.numpy(), S_t.numpy(), inputs, role, S0_np, n_np, k, "bf16", rule=rule,
                                   param=param)
         log(f"[loop graph] {rule} layer: max|err| = {err:.2e}, band diffs {band}")
