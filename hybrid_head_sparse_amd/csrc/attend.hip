@@ -1240,12 +1240,12 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     continue;
                 }
                 // this pass's bound: its own crossing at its share s of k_eff plus
-                // a margin, the smaller of kSelMargin - 1 shares and 5 standard
+                // a margin, the smaller of kSelMargin - 1 shares and 4 standard
                 // deviations of a Poisson count with mean s (plus 2), but never
-                // under 4 deviations plus 4 (a pass of a few rows keeps them all)
+                // under 3 deviations plus 4 (a pass of a few rows keeps them all)
                 const float share = (float)ke * (float)len / (float)n;
                 const float rs = sqrtf(share);
-                const float margin = fmaxf(fminf((float)(kSelMargin - 1u) * share, 5.0f * rs + 2.0f), 4.0f * rs + 4.0f);
+                const float margin = fmaxf(fminf((float)(kSelMargin - 1u) * share, 4.0f * rs + 2.0f), 3.0f * rs + 4.0f);
                 // (a need beyond the pass's rows gives bound 0: every key kept)
                 const uint32_t need = (uint32_t)fminf((float)len + 1.0f, ceilf(share + margin));
                 // the pass's bound Tw: the crossing of its histogram at `need`

@@ -37,11 +37,14 @@ constexpr int kHistBins = 1 << kHistBits;
 constexpr int kCandLds = 4096;                // threshold-digit candidates resolved in LDS
 // A workgroup appends the keys of a pass whose first digit reaches its own
 // crossing at its proportional share s of the budget, k_eff * rows / n, plus
-// a margin: the smaller of kSelMargin - 1 shares and 5 Poisson standard
-// deviations of s plus 2, raised to at least 4 deviations plus 4 (for passes
+// a margin: the smaller of kSelMargin - 1 shares and 4 Poisson standard
+// deviations of s plus 2, raised to at least 3 deviations plus 4 (for passes
 // of a few rows, whose share is tiny).  That is a lower bound of the head's
 // threshold digit unless the pass holds more than that many of the head's
 // top-k_eff keys; the selector checks it and otherwise reads every key.
+// Measured on the 128K step against 5 deviations (floor 4): 4 takes fewer
+// candidates and wins (1102 -> 1076 us); 3.5 and 3 fall back often enough to
+// lose (1185 and 1295 us).
 constexpr uint32_t kSelMargin = 2;
 // Polls (about 1 us each) a helper spends waiting for the head's last arrival
 // before leaving its slice of the top-k to it.
