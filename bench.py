@@ -36,7 +36,13 @@ import numpy as np
 import synth
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "attend_llama3_128k_counters.json")
+METRICS = {
+    "llama3_128k": "decode-attn us/step + achieved HBM GB/s, Llama3-8B shape, 128K ctx, k=4096",
+    "llama3_32k": "decode-attn us/step + achieved HBM GB/s, Llama3-8B shape, 32K ctx, k=4096",
+    "llama3_ragged_b8": "decode-attn us/step + achieved HBM GB/s, Llama3-8B shape, batch 8, ragged 32K-64K ctx, k=2048",
+    "qwen3_128k_k1024": "decode-attn us/step + achieved HBM GB/s, Qwen3-8B shape, 128K ctx, k=1024, tie groups",
+    "qwen3_128k_k4096": "decode-attn us/step + achieved HBM GB/s, Qwen3-8B shape, 128K ctx, k=4096, tie groups",
+}
 
 
 def algorithmic_bytes(w: synth.Workload, roles: np.ndarray, lens: np.ndarray, valid=None):
@@ -63,11 +69,10 @@ def algorithmic_bytes(w: synth.Workload, roles: np.ndarray, lens: np.ndarray, va
     return hyb, dense
 
 
-def load_inputs(w, roles, lens, keep_host_layers: int, threads: int):
-    """Generate every layer on the host and move it to the GPU; keep host
-    copies of the first `keep_host_layers` layers for the CPU baseline."""
+def load_inputs(w, roles, lens, threads: int):
+    """Generate every layer on the host and move it to the GPU."""
     import torch
-    dev, host = [], []
+    dev = []
     for l in range(w.layers):
         x = synth.layer_inputs(w, l, threads=threads)
         if w.dtype == "bf16":
@@ -75,44 +80,67 @@ def load_inputs(w, roles, lens, keep_host_layers: int, threads: int):
         else:
             conv = lambda a: torch.from_numpy(a).cuda()
         dev.append({key: conv(x[key]) for key in ("q", "k", "v")})
-        if l < keep_host_layers:
-            host.append(x)
         print(f"[bench] layer {l} resident", file=sys.stderr, flush=True)
-    return dev, host
+    return dev
 
 
-def cpu_baseline(w, roles, lens, host_layers, budget_s: float, threads: int, rule="topk", param=0.0):
-    """Time the oracle (as it stands) on the first layers of the step, chained
-    through S, repeating that chain until `budget_s` of CPU work; scale to the
-    whole step by pooled work units (n per retrieval head, k_eff per sparse head)."""
+def host_info():
+    """Logical CPUs the OS reports and the CPU model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
+def cpu_baseline(w, roles, lens, dev, threads: int, reps: int = 3, rule="topk", param=0.0):
+    """Time the oracle (as it stands) over the whole step: every layer, S
+    chained, on `threads` host threads; each layer's inputs are copied back
+    from the GPU untimed and the oracle runs `reps` times on them.  The step
+    time of repetition r is the sum over layers of the r-th run; the median
+    over repetitions is reported."""
     import oracle
-    units = []
+    per = np.zeros((reps, w.layers))
+    S = None
     for l in range(w.layers):
-        R = int(roles[l].sum())
-        units.append(sum(R * int(n) + (w.n_kv_heads - R) * min(w.k, int(n)) for n in lens))
-    nl = len(host_layers)
-    t_total, passes = 0.0, 0
-    while passes == 0 or t_total < budget_s:
-        S = None
-        for l, x in enumerate(host_layers):
+        x = {key: (t.view(torch_int16()).cpu().numpy().view(np.uint16) if w.dtype == "bf16" else t.cpu().numpy())
+             for key, t in dev[l].items()}
+        for r in range(reps):
             t0 = time.perf_counter()
-            _, S, _ = oracle.layer(x["q"], x["k"], x["v"], roles[l], S, lens, w.k, threads=threads, rule=rule,
-                                   param=param)
-            t_total += time.perf_counter() - t0
-        passes += 1
-    frac = passes * sum(units[:nl]) / sum(units)
-    est_us = t_total / frac * 1e6
-    return {"value": est_us, "unit": "us/step", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} passes over layers 0..{nl - 1} of {w.layers} (chained S), {t_total:.2f} s measured, "
-                      f"scaled by pooled work units ({frac:.4f} steps); inputs generated outside the timing"}
+            _, S_new, _ = oracle.layer(x["q"], x["k"], x["v"], roles[l], S, lens, w.k, threads=threads, rule=rule,
+                                       param=param)
+            per[r, l] = time.perf_counter() - t0
+        S = S_new
+        del x
+        print(f"[bench] oracle layer {l}: {per[:, l].min() * 1e3:.1f} ms", file=sys.stderr, flush=True)
+    steps = per.sum(axis=1)
+    nproc, model = host_info()
+    return {"value": float(np.median(steps)) * 1e6, "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {w.layers}-layer step (S chained), median of {reps} repetitions per layer "
+                      f"summed per repetition (step times {', '.join(f'{v:.3f}' for v in steps)} s); inputs "
+                      f"copied back from the GPU outside the timing",
+            "nproc": nproc, "cpu_model": model,
+            "threads_note": "the oracle's OpenMP threads: the host CPU share of one GPU (16), or every CPU if fewer"}
 
 
-def counters_traffic():
+def torch_int16():
+    import torch
+    return torch.int16
+
+
+def counters_traffic(workload: str):
     """HBM traffic of the attention kernel from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source (else None)."""
-    if not os.path.exists(COUNTERS_FILE):
+    summary of this workload, if it was taken on the current kernel source
+    (else None)."""
+    path = os.path.join(ROOT, "profiles", f"attend_{workload}_counters.json")
+    if not os.path.exists(path):
         return None
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         c = json.load(f)
     from hybrid_head_sparse_amd.profiling import kernel_code_digest
     if c.get("kernel_code_sha256") != kernel_code_digest():
@@ -126,7 +154,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_128k", choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="oracle repetitions per layer for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--rule", default="topk", choices=["topk", "ratio", "threshold", "topp", "block"],
@@ -147,8 +175,7 @@ def main():
     roles = synth.roles(w)
     lens = synth.n_ctx(w)
     threads = min(16, os.cpu_count() or 1)
-    keep = 0 if args.no_cpu_baseline else min(w.layers, 8)
-    dev, host = load_inputs(w, roles, lens, keep, threads)
+    dev = load_inputs(w, roles, lens, threads)
     B, Hq, Hkv, d, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.k
     n_ctx = torch.from_numpy(lens).cuda()
     S = [torch.full((B, Hkv, k), -1, dtype=torch.int32, device="cuda") for _ in range(w.layers)]
@@ -246,9 +273,14 @@ def main():
     hyb_bytes, dense_bytes = algorithmic_bytes(w, roles, lens, valid)
     step_bytes = sum(hyb_bytes)
     att_mean = [statistics.mean(v) for v in att_ms]
+    # The roofline's launch time: the graph-timed step (HIP events on the
+    # replay stream) over its launches -- one attention kernel per layer, plus
+    # the rule kernel of the Top-p and block rules, which is counted in.  The
+    # per-launch event times of eager calls add the launch overhead of an
+    # eager call and are reported beside it.
     att_all_bytes = sum(hyb_bytes)                    # per step, over all attention launches
-    att_all_ms = sum(att_mean)
-    achieved = att_all_bytes / (att_all_ms * 1e-3) / 1e9
+    avg_launch_ms = ms_per_step / w.layers
+    achieved = att_all_bytes / (ms_per_step * 1e-3) / 1e9
     l0_ms = att_mean[0]
     l0_achieved = hyb_bytes[0] / (l0_ms * 1e-3) / 1e9
 
@@ -284,12 +316,12 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, roles, lens, host, args.cpu_budget, threads, args.rule, args.param)
+        cpu = cpu_baseline(w, roles, lens, dev, threads, args.cpu_reps, args.rule, args.param)
 
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     n_retr = int(roles.sum())
     result = {
-        "metric": "decode-attn us/step + achieved HBM GB/s, Llama3-8B shape, 128K ctx, k=4096",
+        "metric": METRICS.get(w.name, f"decode-attn us/step + achieved HBM GB/s, {w.name}"),
         "value": ms_per_step * 1e3,
         "unit": "us/step",
         "n_gpus": 1,
@@ -317,8 +349,10 @@ def main():
         "speedup_vs_dense": (dense_res["us_per_step"] / (ms_per_step * 1e3)) if dense_res else None,
         "roofline": {"kernel": "attend_kernel (hybrid, all launches of the step)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": counters_traffic() if args.rule == "topk" else None,
-                     "bytes_per_launch": att_all_bytes / w.layers, "avg_launch_us": att_all_ms / w.layers * 1e3},
+                     "traffic": counters_traffic(w.name) if args.rule == "topk" else None,
+                     "bytes_per_launch": att_all_bytes / w.layers, "avg_launch_us": avg_launch_ms * 1e3,
+                     "avg_launch_source": "graph-timed step / launches per step",
+                     "eager_event_launch_us": statistics.mean(att_mean) * 1e3},
         "roofline_all_retrieval_layer": {"kernel": "attend_kernel (hybrid), layer 0: every KV head retrieval",
                                          "achieved": l0_achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                          "frac": l0_achieved / HBM_PEAK_GBPS, "bytes_per_launch": hyb_bytes[0],

@@ -420,7 +420,8 @@ lychee_status lychee_check_device_errors(lychee_handle* h) {
         if (hipMemset(h->ws.err, 0, sizeof flag) != hipSuccess)
             return fail(LYCHEE_ERR_HIP, "clearing the device error flag failed");
         return fail(LYCHEE_ERR_DEVICE_CHECK, "device error flag 0x%x (1: S_in entry outside [0, n_ctx) and not -1; 2: select count mismatch; "
-                    "4: n_ctx < T in a correction; 8: append to a full cache)",
+                    "4: n_ctx < T in a correction; 8: append to a full cache; 16: n_ctx outside [1, max_ctx]; "
+                    "32: S_in entries not strictly ascending (a duplicate))",
                     flag);
     }
     return ok();

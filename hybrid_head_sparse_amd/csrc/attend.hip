@@ -430,6 +430,41 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t*
     return base + inc - v;
 }
 
+// Inclusive max-scan of signed values across the 64 lanes (the pattern of
+// wave_inclusive_scan; lanes without a DPP source take INT32_MIN).
+__device__ __forceinline__ int32_t wave_inclusive_max(int32_t x) {
+    constexpr int32_t lo = -2147483647 - 1;
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, 0x111, 0xF, 0xF, false));   // row_shr:1
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, 0x112, 0xF, 0xF, false));   // row_shr:2
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, 0x114, 0xF, 0xF, false));   // row_shr:4
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, 0x118, 0xF, 0xF, false));   // row_shr:8
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, 0x142, 0xA, 0xF, false));   // row_bcast:15
+    x = max(x, __builtin_amdgcn_update_dpp(lo, x, 0x143, 0xC, 0xF, false));   // row_bcast:31
+    return x;
+}
+
+// Block-wide exclusive max-scan of one value per thread (INT32_MIN for the
+// first thread); *total gets the block's maximum.
+__device__ int32_t block_exclusive_max(int32_t v, uint32_t* s_wave, int32_t* total) {
+    constexpr int32_t lo = -2147483647 - 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int32_t inc = wave_inclusive_max(v);
+    const int32_t up = __shfl_up(inc, 1);
+    const int32_t exc = lane ? up : lo;
+    __syncthreads();
+    if (lane == 63) s_wave[wave] = (uint32_t)inc;
+    __syncthreads();
+    int32_t base = lo, tot = lo;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) {
+        const int32_t c = (int32_t)s_wave[wv];
+        base = (wv < wave) ? max(base, c) : base;
+        tot = max(tot, c);
+    }
+    *total = tot;
+    return max(base, exc);
+}
+
 // Crossing of a histogram spread over the block, PER bins per thread held in
 // `cnt` (thread t holds the bins of descending rank t*PER .. t*PER+PER-1, i.e.
 // bin nbins-1-rank): finds D with (count above D) < need <= (count >= D).
@@ -531,10 +566,18 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         int nb[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) nb[i] = p.n_ctx[min(tid * PER + i, p.B - 1)];
+        bool bad_n = false;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             if (tid * PER + i < p.B) {
-                const int n = nb[i];
+                // a context outside [1, max_ctx] breaks the contract: it is
+                // clamped to [0, max_ctx] (a sequence of 0 rows gets zeros and
+                // an empty set, written below) and latches error bit 16
+                int n = nb[i];
+                if (n < 1 || n > p.max_ctx) {
+                    bad_n = true;
+                    n = n < 0 ? 0 : (n > p.max_ctx ? p.max_ctx : n);
+                }
                 // min(k, n), or under the ratio rule min(k, ceil(theta n)) (at least one)
                 const double t = ceil(p.sel_ratio * (double)n);
                 const uint32_t kr = t < 1.0 ? 1u : (t > (double)n ? (uint32_t)n : (uint32_t)t);
@@ -542,6 +585,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 s_ke[tid * PER + i] = min((uint32_t)min(p.k, n), kr);
             }
         }
+        if (bad_n && blockIdx.x == 0) atomicOr(p.ws.err, 16u);
         __syncthreads();
         uint32_t u_[PER];
         uint32_t tot = 0;
@@ -580,6 +624,25 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     if (w >= P) return;
 
     auto is_retr = [&](int hb) -> bool { return !HYBRID || ((p.role_bits >> (hb % p.Hkv)) & 1ull); };
+    // Heads of a sequence with no context (out of contract, flagged in the
+    // prologue) own no rows: workgroup bg % P writes their zero output and
+    // their S_out row (-1 for a retrieval head, a copy of S_in for a sparse
+    // one).
+    for (int bg = w; bg < BH; bg += P) {
+        const int b = bg / p.Hkv, g = bg - b * p.Hkv;
+        if (s_nctx[b] != 0) continue;
+        float* ob = p.out + ((size_t)b * Hq + (size_t)g * G) * D;
+        for (int i = tid; i < G * D; i += kAttendThreads) ob[i] = 0.0f;
+        if (HYBRID) {
+            int32_t* so = p.S_out + (size_t)bg * p.k;
+            const int32_t* si = p.S_in ? p.S_in + (size_t)bg * p.k : nullptr;
+            if (is_retr(bg)) {
+                for (int i = tid; i < p.k; i += kAttendThreads) so[i] = -1;
+            } else if (si && si != so) {
+                for (int i = tid; i < p.k; i += kAttendThreads) so[i] = si[i];
+            }
+        }
+    }
     auto head_of = [&](uint32_t c) -> int {     // last (b, g) whose cost range starts at or before c
         int cnt = 0;                              // (wave-parallel: the starts are increasing)
         for (int base = 0; base < BH; base += 64) {
@@ -1085,6 +1148,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #pragma unroll
             for (int e = 0; e < EPL; ++e) o[h][e] = 0.0f;
         bool bad_index = false;
+        bool bad_order = false;        // a sparse head's S_in entries not strictly ascending
         uint32_t key_base = 0;         // position of u.st.keys[0] (retrieval selection keys)
 
         // Load the K/V fragments of the tile starting at position tb of
@@ -1334,6 +1398,17 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             const int32_t* Srow = p.S_in + (size_t)bg * p.k;
             int32_t* Sout = (p.S_out != p.S_in) ? p.S_out + (size_t)bg * p.k : nullptr;
             constexpr int PER = kIdxChunk / kAttendThreads;
+            // Order check: the entries other than -1 must be strictly
+            // ascending (the form S_out has), so a duplicate sits next to its
+            // twin once the -1 holes are skipped.  run_max is the largest
+            // entry before the chunk: the entry before this range if it is
+            // not a hole (a twin across the range boundary with holes between
+            // goes unseen), then the chunks before.
+            int32_t run_max = -2147483647 - 1;
+            if (seg_lo > 0) {
+                const int32_t pv = Srow[seg_lo - 1];
+                if (pv != -1) run_max = pv;
+            }
             for (uint32_t c_lo = seg_lo; c_lo < seg_hi; c_lo += kIdxChunk) {
                 const uint32_t c_hi = min(seg_hi, c_lo + (uint32_t)kIdxChunk);
                 __syncthreads();
@@ -1349,6 +1424,26 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     }
                 }
                 __syncthreads();
+                {   // thread t checks the chunk's entries PER t .. PER t + PER - 1
+                    int32_t e[PER];
+                    int32_t lm = -2147483647 - 1;
+#pragma unroll
+                    for (int j = 0; j < PER; ++j) {
+                        const uint32_t at = (uint32_t)(tid * PER + j);
+                        e[j] = c_lo + at < c_hi ? u.st.idx[at] : -1;
+                        lm = e[j] != -1 ? max(lm, e[j]) : lm;
+                    }
+                    int32_t cmax;
+                    int32_t m = max(run_max, block_exclusive_max(lm, s_wave, &cmax));
+#pragma unroll
+                    for (int j = 0; j < PER; ++j) {
+                        if (e[j] != -1) {
+                            bad_order |= e[j] <= m;
+                            m = max(m, e[j]);
+                        }
+                    }
+                    run_max = max(run_max, cmax);
+                }
                 stream_range(c_lo, c_hi, u.st.idx);
             }
             // entries past min(k, n) (the -1 padding of a short context) belong
@@ -1358,6 +1453,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
         }
         if (bad_index) atomicOr(p.ws.err, 1u);
+        if (bad_order) atomicOr(p.ws.err, 32u);
 
         // ---- merge the 4 rows of each wavefront, then the 4 wavefronts ----
         const float lrow = row_sum_same_head<G>(l_run);           // head xl, this row

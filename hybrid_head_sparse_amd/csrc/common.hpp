@@ -70,6 +70,29 @@ constexpr int kRuleSplit = 16;
 // so whoever observes the counter can read the data.  This replaces release /
 // acquire fences, whose buffer_wbl2 / buffer_inv are L2-wide and were measured
 // to dominate the launch when every workgroup executes them.
+//
+// Why it is ordered, and the invariant every edit must keep:
+//   1. every datum one workgroup hands to another within a launch is written
+//      with coherent_store (or an agent-scope atomic) and read with
+//      coherent_load (or an atomic) -- a plain store may sit dirty in the
+//      producer's XCD-local L2 and a plain load may hit a stale line in the
+//      consumer's, and relaxed agent-scope accesses are coherent per
+//      location but order nothing between locations;
+//   2. the producer executes wait_stores_complete() after its last such store
+//      and then __syncthreads() before the counter RMW.  On gfx9 vmcnt counts
+//      stores as well as loads, and an sc1 store leaves vmcnt only once the
+//      agent coherence point has acknowledged it, so the data is visible
+//      device-wide before any wave of the workgroup can pass the barrier
+//      and issue the counter RMW.  The asm statement's "memory" clobber keeps
+//      the compiler from sinking stores below it;
+//   3. the consumer reads the handed-off data only after the RMW's returned
+//      value (or a coherent_load of the counter) has been compared and the
+//      outcome passed through __syncthreads().  The barrier's workgroup
+//      fences stop the compiler hoisting the data loads above it, and a wave
+//      issues in order without speculating loads, so the loads leave after
+//      the counter was seen.
+// Data handed to the next launch (S_out, out) needs none of this: the
+// end-of-kernel release and the next kernel's acquire order it.
 template <typename V>
 __device__ __forceinline__ void coherent_store(V* p, V v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -134,7 +157,12 @@ struct Workspace {
 inline int record_floats(int G, int D) { return G * (D + 2); }
 
 // Carve a workspace for the given dims from `base` (nullptr -> sizes only).
-inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int max_ctx, int k_max) {
+// The zero-initialised region comes first, so the layouts of different dims
+// agree on where it starts (the allocation-free entry point relies on it).
+// Without `with_correction` the correction attention's chunk records are left
+// out (crec_ml / crec_o null): enough for the decode layer alone.
+inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int max_ctx, int k_max,
+                                 bool with_correction = true) {
     (void)k_max;
     const int BH = B * Hkv;
     const int G = Hq / Hkv;
@@ -145,14 +173,6 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         off += (bytes + 255) & ~(size_t)255;
         return at;
     };
-    size_t o_rec1 = take(sizeof(float) * (size_t)(kMaxWG + BH) * RS);
-    size_t o_rec2 = take(sizeof(float) * (size_t)BH * kLevel2Max * RS);
-    size_t o_cand = take(sizeof(unsigned long long) * (size_t)BH * max_ctx);
-    size_t o_score = take(sizeof(uint32_t) * (size_t)BH * max_ctx);
-    size_t o_prec = take(sizeof(unsigned long long) * (size_t)BH * kRuleSplit * 4);
-    const size_t CW = (size_t)(BH > 512 ? BH : 512);
-    size_t o_crml = take(sizeof(float) * CW * 32 * G * 2);
-    size_t o_cro = take(sizeof(float) * CW * 32 * G * D);
     size_t z0 = off;
     size_t o_cnt1 = take(sizeof(uint32_t) * (size_t)BH * kLevel2Max);
     size_t o_cnt2 = take(sizeof(uint32_t) * (size_t)BH);
@@ -163,18 +183,27 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_hist = take(sizeof(uint32_t) * (size_t)BH * kHistBins);
     size_t o_pctr = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_err = take(sizeof(uint32_t) * 4);
+    const size_t z1 = off;
+    size_t o_rec1 = take(sizeof(float) * (size_t)(kMaxWG + BH) * RS);
+    size_t o_rec2 = take(sizeof(float) * (size_t)BH * kLevel2Max * RS);
+    size_t o_cand = take(sizeof(unsigned long long) * (size_t)BH * max_ctx);
+    size_t o_score = take(sizeof(uint32_t) * (size_t)BH * max_ctx);
+    size_t o_prec = take(sizeof(unsigned long long) * (size_t)BH * kRuleSplit * 4);
+    const size_t CW = (size_t)(BH > 512 ? BH : 512);
+    size_t o_crml = with_correction ? take(sizeof(float) * CW * 32 * G * 2) : 0;
+    size_t o_cro = with_correction ? take(sizeof(float) * CW * 32 * G * D) : 0;
     Workspace w{};
     char* p = (char*)base;
     w.total_bytes = off;
-    w.zero_bytes = off - z0;
+    w.zero_bytes = z1 - z0;
     if (p) {
         w.rec1 = (float*)(p + o_rec1);
         w.rec2 = (float*)(p + o_rec2);
         w.cand = (unsigned long long*)(p + o_cand);
         w.score = (uint32_t*)(p + o_score);
         w.prec = (unsigned long long*)(p + o_prec);
-        w.crec_ml = (float*)(p + o_crml);
-        w.crec_o = (float*)(p + o_cro);
+        w.crec_ml = with_correction ? (float*)(p + o_crml) : nullptr;
+        w.crec_o = with_correction ? (float*)(p + o_cro) : nullptr;
         w.cnt1 = (uint32_t*)(p + o_cnt1);
         w.cnt2 = (uint32_t*)(p + o_cnt2);
         w.selctr = (unsigned long long*)(p + o_sc);

@@ -54,7 +54,7 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, c32 = lane & 31;
     const int bg = blockIdx.x / p.nchunks, chunk = blockIdx.x - bg * p.nchunks;
     const int b = bg / p.Hkv, g = bg - b * p.Hkv;
-    const int n = min(p.n_ctx[b], p.max_ctx);
+    const int n = max(0, min(p.n_ctx[b], p.max_ctx));
     const int T = p.T;
     const int Hq = p.Hkv * G;
     if (n < T) {                       // out of contract: flagged, the rows are undefined

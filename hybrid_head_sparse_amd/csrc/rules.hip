@@ -112,7 +112,12 @@ __global__ void __launch_bounds__(kRuleThreads) rule_select_kernel(RuleParams p)
     if (!((p.role_bits >> g) & 1ull)) return;          // sparse head: S was forwarded
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool topp = p.mode == kRuleTopP;
-    const int n = min(p.n_ctx[b], p.max_ctx);           // (1 <= n_ctx <= max_ctx by contract)
+    const int n = max(0, min(p.n_ctx[b], p.max_ctx));   // (1 <= n_ctx <= max_ctx by contract)
+    if (n == 0) {                                        // out of contract (the attention kernel
+        if (q == 0)                                      // flagged it): an empty set
+            for (int i = threadIdx.x; i < p.k; i += kRuleThreads) p.S[(size_t)bg * p.k + i] = -1;
+        return;
+    }
     const uint32_t ke = (uint32_t)min(p.k, n);
     const uint32_t bs = (uint32_t)p.block;
     const uint32_t nb = topp ? 0u : ((uint32_t)n + bs - 1u) / bs;

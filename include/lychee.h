@@ -55,7 +55,7 @@ typedef enum {
     LYCHEE_ERR_UNSUPPORTED = -2,   /* valid request outside the compiled variants */
     LYCHEE_ERR_HIP = -3,           /* a HIP runtime call or kernel launch failed */
     LYCHEE_ERR_WORKSPACE = -4,     /* workspace too small or misaligned */
-    LYCHEE_ERR_DEVICE_CHECK = -5   /* device-side contract violation seen (S_in entry out of range) */
+    LYCHEE_ERR_DEVICE_CHECK = -5   /* device-side contract violation seen (see lychee_check_device_errors) */
 } lychee_status;
 
 typedef enum { LYCHEE_F32 = 0, LYCHEE_BF16 = 1 } lychee_dtype;
@@ -95,6 +95,8 @@ lychee_status lychee_create(const lychee_dims* dims, void* workspace, size_t wor
  *              sparse head's row must lie in [0, n_ctx[b]) or be -1 (padding
  *              of a set shorter than min(k, n_ctx[b]), skipped) for the first
  *              min(k, n_ctx[b]) positions; later entries are copied, not read.
+ *              The entries other than -1 must be strictly ascending (the form
+ *              S_out has), which rules out duplicates.
  *              A sparse head whose entries are all padding outputs zeros.
  *   S_out      [B, Hkv, k] int32; retrieval rows get the new set (ascending,
  *              -1 padded), sparse rows a copy of S_in's row.  S_out may equal
@@ -102,8 +104,17 @@ lychee_status lychee_create(const lychee_dims* dims, void* workspace, size_t wor
  *   out        [B, Hq, d] fp32, fully overwritten
  *   n_ctx      [B] int32 on the device, 1 <= n_ctx[b] <= max_ctx
  *   k          1 <= k <= k_max
- * Entries of S_in outside [0, n_ctx[b]) other than -1 are skipped (never read
- * through) and latch a flag reported by lychee_check_device_errors. */
+ * Device-side contract checks (each latches a flag that
+ * lychee_check_device_errors reports; nothing is read out of bounds):
+ *   - an S_in entry outside [0, n_ctx[b]) other than -1 is skipped;
+ *   - S_in entries (other than -1) that are not strictly ascending inside a
+ *     row, e.g. a duplicate, are flagged and attended as given (a duplicated
+ *     row counts twice).  A pair whose two entries fall in the parts of the
+ *     row that different workgroups take, with only -1 entries between
+ *     them, is not seen;
+ *   - n_ctx[b] outside [1, max_ctx] is clamped to [0, max_ctx]; a sequence
+ *     clamped to 0 rows gets zeros in out, -1 in its retrieval rows of S_out
+ *     and a copy of S_in in its sparse rows. */
 lychee_status lychee_decode_layer(lychee_handle* h,
                                   const void* q, const void* k_cache, const void* v_cache,
                                   const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out,
@@ -211,8 +222,10 @@ lychee_status lychee_correction_attention(lychee_handle* h, const void* q, const
 
 /* Synchronise the stream, read and clear the device-side error flag.
  * Returns LYCHEE_ERR_DEVICE_CHECK if any call since the last check skipped an
- * out-of-range S_in entry, appended to a full cache or ran a correction over
- * a context shorter than T. */
+ * out-of-range S_in entry, saw S_in entries out of ascending order (a
+ * duplicate), clamped an n_ctx outside [1, max_ctx], appended to a full cache
+ * or ran a correction over a context shorter than T; the detail string
+ * (lychee_last_error) lists the flag bits. */
 lychee_status lychee_check_device_errors(lychee_handle* h);
 
 /* Release the handle (host memory only). */

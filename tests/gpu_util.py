@@ -45,22 +45,29 @@ def run_layer(handle, x, role, S_in_dev, n_ctx_dev, k, *, S_out_dev=None, rule="
     return res
 
 
-def plant_boundary_groups(w: synth.Workload, x: dict, k: int, ties: dict):
-    """Copy each head's oracle k-th-ranked K row into 7 lower-ranked positions,
-    some below and some above its index, so an exact tie group straddles the
-    top-k boundary.  Mutates x["k"] and appends the groups to ``ties``."""
+def plant_boundary_groups(w: synth.Workload, x: dict, k: int, ties: dict, heads=None, layer: int = 0):
+    """Copy the oracle k-th-ranked K row of each KV head in ``heads`` (default:
+    all) into 7 lower-ranked positions, some below and some above its index,
+    so an exact tie group straddles the top-k boundary.  Mutates x["k"] and
+    appends the groups to ``ties``."""
     lens = synth.n_ctx(w)
-    ones = np.ones(w.n_kv_heads, np.uint8)
-    _, S, scores = oracle.layer(x["q"], x["k"], x["v"], ones, None, lens, k, want_scores=True)
-    rng = np.random.default_rng([w.seed, 4242])
+    heads = list(range(w.n_kv_heads)) if heads is None else [int(g) for g in heads]
+    if not heads:
+        return x
+    G = w.group
+    hq = [g * G + i for g in heads for i in range(G)]
+    ones = np.ones(len(heads), np.uint8)
+    _, S, scores = oracle.layer(np.ascontiguousarray(x["q"][:, hq]), np.ascontiguousarray(x["k"][:, heads]),
+                                np.ascontiguousarray(x["v"][:, heads]), ones, None, lens, k, want_scores=True)
+    rng = np.random.default_rng([w.seed, 4242, layer])
     for b in range(w.batch):
         n = int(lens[b])
         ke = min(k, n)
         if ke >= n:
             continue
-        for g in range(w.n_kv_heads):
-            O = S[b, g, :ke]
-            s = scores[b, g, :n]
+        for gi, g in enumerate(heads):
+            O = S[b, gi, :ke]
+            s = scores[b, gi, :n]
             order = sorted(O.tolist(), key=lambda j: (-s[j], j))
             jk = order[-1]
             busy = np.zeros(n, bool)

@@ -25,6 +25,21 @@ Tolerances (stated for the method's parity bar):
 The oracle receives the same S_in as the GPU (the GPU's S_out of the previous
 layer), so a tolerated boundary swap upstream cannot move a downstream
 sparse-head output.
+
+Normalised output bound (beside the absolute one).  With q, K ~ N(0,1)/sqrt(d)
+and V ~ N(0,1) a retrieval head's output over n keys is about the mean of n V
+rows, of size ~1/sqrt(n) (max |out| ~ 0.009 at n = 128K), so the absolute 2e-2
+bar alone would pass out = 0 or a merge that drops a group of partial
+records.  So every comparison also requires, per (sequence, KV head),
+    max |out_gpu - out_oracle| <= 1e-3 * max |out_oracle|
+over the head's G query heads (a head whose oracle output is exactly zero
+must come out exactly zero).  The decode kernel takes the same bf16 inputs
+and works in fp32 (dot products, exp2, accumulation), so its relative error
+is ~1e-6..1e-5; losing 1/32 of a head's rows moves the output by ~3% and
+out = 0 by 100%, both far outside 1e-3.  The correction attention rounds its
+probabilities to bf16 for the matrix cores (relative error up to 2^-9 per
+weight), so its bound is 1e-2 * max |out_oracle| per (sequence, position,
+KV head) (CORR_REL).
 """
 from __future__ import annotations
 
@@ -33,8 +48,41 @@ import numpy as np
 import oracle
 
 OUT_TOL = {"f32": 1e-4, "bf16": 2e-2}
+OUT_REL = 1e-3
+CORR_REL = 1e-2
 BAND_REL = 1e-3
 TOPP_TOL = 1e-5
+
+
+def check_relative(out_gpu, out_or, group: int, rel: float = OUT_REL, what: str = "out"):
+    """Normalised bound: for every (leading index..., KV head) block of `group`
+    consecutive query heads, max |err| <= rel * max |out_oracle| of the block.
+    The last two axes of the arrays are (query head, d).  Returns the largest
+    ratio max|err| / max|out_oracle| over the blocks (0 where both are 0)."""
+    a = np.asarray(out_gpu, dtype=np.float64)
+    o = np.asarray(out_or, dtype=np.float64)
+    *lead, Hq, d = o.shape
+    shape = (*lead, Hq // group, group * d)
+    e = np.abs(a - o).reshape(shape).max(axis=-1)
+    m = np.abs(o).reshape(shape).max(axis=-1)
+    bad = e > rel * m
+    if np.any(bad):
+        i = np.unravel_index(int(np.argmax(np.where(bad, e - rel * m, -np.inf))), bad.shape)
+        raise AssertionError(f"{what}: normalised error at block {tuple(int(v) for v in i)}: "
+                             f"max|err| {e[i]:.3e} > {rel:g} * max|oracle| {m[i]:.3e}")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(m > 0, e / np.where(m > 0, m, 1.0), 0.0)
+    return float(r.max())
+
+
+class LayerStats(tuple):
+    """(max abs error, band differences), plus .rel: the largest normalised
+    error max|err| / max|out_oracle| over the (sequence, KV head) blocks."""
+
+    def __new__(cls, err, band, rel):
+        t = tuple.__new__(cls, (err, band))
+        t.rel = rel
+        return t
 
 
 def check_S_row(S_gpu_row, n, k, count=None):
@@ -141,9 +189,11 @@ def compare_layer(out_gpu, S_gpu, inputs, role, S_in, n_ctx, k, dtype, ties=None
     err = np.abs(out_gpu.astype(np.float64) - out_or)
     assert np.all(np.isfinite(out_gpu)), "non-finite output"
     assert err.max() <= OUT_TOL[dtype], f"max |out err| {err.max():.3e} > {OUT_TOL[dtype]}"
+    G = out_gpu.shape[1] // S_gpu.shape[1]
+    rel = check_relative(out_gpu, out_or, G)
     for b in range(S_gpu.shape[0]):
         for g in range(S_gpu.shape[1]):
             if not role[g]:
                 np.testing.assert_array_equal(S_gpu[b, g], S_in[b, g], err_msg="sparse head must forward S")
     band = compare_S(S_gpu, S_or, scores, role, n_ctx, k, ties, rule, param)
-    return float(err.max()), band
+    return LayerStats(float(err.max()), band, rel)

@@ -11,7 +11,7 @@ import pytest
 import oracle
 import synth
 from gpu_util import log, make_handle, run_layer, to_device
-from parity import OUT_TOL, compare_layer
+from parity import OUT_TOL, check_relative, compare_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -144,7 +144,10 @@ def test_dense_baseline_matches_oracle():
         handle.dense_decode_layer(q, kc, vc, out, torch.from_numpy(lens).cuda())
         torch.cuda.synchronize()
         ref, _, _ = oracle.layer(x["q"], x["k"], x["v"], np.ones(w.n_kv_heads, np.uint8), None, lens, 1)
-        assert np.abs(out.cpu().numpy() - ref).max() <= OUT_TOL[dt]
+        got = out.cpu().numpy()
+        assert np.abs(got - ref).max() <= OUT_TOL[dt]
+        rel = check_relative(got, ref, w.group, what="dense")
+        log(f"[dense {w.name}] max|err| {np.abs(got - ref).max():.2e} normalised {rel:.2e}")
 
 
 def test_maximum_context():
@@ -180,3 +183,72 @@ def test_clustered_top_keys_take_the_full_scan_path():
     compare_layer(out, S, x, role, None, lens, w.k, w.dtype)
     assert set(range(300)) <= set(S[0, 0].tolist())
     handle.check_device_errors()
+
+
+def test_context_outside_the_contract_is_clamped_and_flagged():
+    """n_ctx = max_ctx + 1 is clamped to max_ctx (the output is the oracle's
+    at max_ctx); n_ctx = 0 gives zeros, -1 retrieval rows and copied sparse
+    rows; both latch the device flag."""
+    import torch
+    import hybrid_head_sparse_amd as hhs
+    w = _w("bad_n", 92, 2, 2, 32, 8, 128, 1000, 64, "bf16", 4, ctx_list=(1000, 700), hh_frac=0.01)
+    handle = make_handle(w)
+    lens = synth.n_ctx(w)
+    roles = synth.roles(w)
+    good = torch.from_numpy(lens).cuda()
+    bad = torch.tensor([1001, 0], dtype=torch.int32, device="cuda")
+    x0 = synth.layer_inputs(w, 0)
+    _, S0, S0_dev = run_layer(handle, x0, roles[0], None, good, w.k)
+    handle.check_device_errors()
+    row0 = {key: np.ascontiguousarray(v[:1]) for key, v in x0.items()}
+    out, S, _ = run_layer(handle, x0, roles[0], None, bad, w.k)
+    compare_layer(out[:1], S[:1], row0, roles[0], None, lens[:1], w.k, w.dtype)
+    assert np.all(out[1] == 0.0) and np.all(S[1] == -1)
+    with pytest.raises(hhs.LycheeError) as ei:
+        handle.check_device_errors()
+    assert ei.value.status == hhs.LYCHEE_ERR_DEVICE_CHECK
+    x1 = synth.layer_inputs(w, 1)
+    out1, S1, _ = run_layer(handle, x1, roles[1], S0_dev, bad, w.k)
+    row1 = {key: np.ascontiguousarray(v[:1]) for key, v in x1.items()}
+    compare_layer(out1[:1], S1[:1], row1, roles[1], S0[:1], lens[:1], w.k, w.dtype)
+    assert np.all(out1[1] == 0.0)
+    for g in range(w.n_kv_heads):
+        want = np.full(w.k, -1, np.int32) if roles[1][g] else S0[1, g]
+        np.testing.assert_array_equal(S1[1, g], want)
+    with pytest.raises(hhs.LycheeError):
+        handle.check_device_errors()
+    handle.check_device_errors()      # cleared
+    log(f"[bad_n] n_ctx [1001, 0] clamped to [1000, 0] and flagged; roles of layer 1 {roles[1].tolist()}")
+
+
+@pytest.mark.parametrize("n,k,where", [(1000, 16, (5,)), (20000, 4096, (128, 1024, 2047, 2048, 3001))])
+def test_duplicate_S_entries_are_flagged(n, k, where):
+    """S_in rows whose entries (other than -1) are not strictly ascending --
+    here a duplicate next to its twin, with and without -1 holes between --
+    latch the device flag; the duplicated row is attended twice, as the
+    oracle does, and a row with holes but no duplicate does not flag."""
+    import torch
+    import hybrid_head_sparse_amd as hhs
+    w = _w(f"dup_S_{k}", 93, 1, 2, 8, 2, 128, n, k, "bf16", 0, ctx_list=(n,))
+    handle = make_handle(w)
+    lens = synth.n_ctx(w)
+    n_ctx_dev = torch.from_numpy(lens).cuda()
+    x = synth.layer_inputs(w, 1)
+    base = (np.arange(k, dtype=np.int64) * (n // k)).astype(np.int32)
+    S_in = np.stack([base, base])[None].copy()
+    S_in[0, 1, ::3] = -1                         # holes, still ascending: no flag
+    sparse = np.zeros(2, np.uint8)
+    out, S, _ = run_layer(handle, x, sparse, torch.from_numpy(S_in).cuda(), n_ctx_dev, k)
+    compare_layer(out, S, x, sparse, S_in, lens, k, w.dtype)
+    handle.check_device_errors()
+    dup = S_in.copy()
+    for i in where:
+        dup[0, 0, i] = dup[0, 0, i - 1]          # adjacent twin
+    dup[0, 1, where[0] + 1] = -1                 # twin across a hole
+    dup[0, 1, where[0] + 2] = dup[0, 1, where[0]] if dup[0, 1, where[0]] != -1 else dup[0, 1, where[0] - 1]
+    out, S, _ = run_layer(handle, x, sparse, torch.from_numpy(dup).cuda(), n_ctx_dev, k)
+    compare_layer(out, S, x, sparse, dup, lens, k, w.dtype)
+    with pytest.raises(hhs.LycheeError) as ei:
+        handle.check_device_errors()
+    assert ei.value.status == hhs.LYCHEE_ERR_DEVICE_CHECK and "flag 0x20 " in str(ei.value)
+    log(f"[dup_S k={k}] duplicates at {list(where)} flagged")

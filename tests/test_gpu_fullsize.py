@@ -80,5 +80,7 @@ def test_llama3_128k_full_step_in_a_graph():
 
     for l in range(w.layers):
         x = synth.layer_inputs(w, l, threads=16)
-        err, band = compare_layer(ref_out[l], ref_S[l], x, roles[l], ref_S[l - 1] if l else None, lens, k, w.dtype)
-        log(f"[{w.name}] layer {l} roles={int(roles[l].sum())} retrieval  max|err|={err:.2e} band-diffs={band}")
+        st = compare_layer(ref_out[l], ref_S[l], x, roles[l], ref_S[l - 1] if l else None, lens, k, w.dtype,
+                           threads=16)
+        log(f"[{w.name}] layer {l} roles={int(roles[l].sum())} retrieval  max|err|={st[0]:.2e} "
+            f"normalised={st.rel:.2e} band-diffs={st[1]}")

@@ -12,7 +12,7 @@ import pytest
 import oracle
 import synth
 from gpu_util import log, to_device
-from parity import compare_layer
+from parity import CORR_REL, check_relative, compare_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -98,7 +98,8 @@ def test_correction_attention_matches_the_oracle(T, G):
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
     err = np.abs(got - ref).max()
-    log(f"[correction T={T} G={G}] max|err| = {err:.2e}")
+    rel = check_relative(got, ref, G, CORR_REL, "correction")
+    log(f"[correction T={T} G={G}] max|err| = {err:.2e} normalised {rel:.2e}")
     assert err <= OUT_TOL
 
 
@@ -115,8 +116,10 @@ def test_correction_attention_over_a_context_of_exactly_T():
                            torch.from_numpy(lens).cuda(), out)
     torch.cuda.synchronize()
     h.check_device_errors()
-    err = np.abs(out.cpu().numpy() - oracle.correction_attention(q, kc, vc, lens)).max()
-    log(f"[correction n = T = {T}] max|err| = {err:.2e}")
+    got, ref = out.cpu().numpy(), oracle.correction_attention(q, kc, vc, lens)
+    err = np.abs(got - ref).max()
+    rel = check_relative(got, ref, 4, CORR_REL, "correction")
+    log(f"[correction n = T = {T}] max|err| = {err:.2e} normalised {rel:.2e}")
     assert err <= OUT_TOL
 
 
@@ -138,8 +141,10 @@ def test_correction_attention_over_a_context_shorter_than_T_is_flagged():
     h.correction_attention(q_d, kc_d, vc_d, torch.from_numpy(lens2).cuda(), out)
     torch.cuda.synchronize()
     h.check_device_errors()
-    err = np.abs(out.cpu().numpy() - oracle.correction_attention(q, kc, vc, lens2)).max()
-    log(f"[correction n < T flagged, then n = 600] max|err| = {err:.2e}")
+    got, ref = out.cpu().numpy(), oracle.correction_attention(q, kc, vc, lens2)
+    err = np.abs(got - ref).max()
+    rel = check_relative(got, ref, 4, CORR_REL, "correction")
+    log(f"[correction n < T flagged, then n = 600] max|err| = {err:.2e} normalised {rel:.2e}")
     assert err <= OUT_TOL
 
 
@@ -157,8 +162,10 @@ def test_correction_attention_at_128k_context():
     torch.cuda.synchronize()
     h.check_device_errors()
     ref = oracle.correction_attention(q, kc, vc, lens, threads=16)
-    err = np.abs(out.cpu().numpy() - ref).max()
-    log(f"[correction 128K T={T}] max|err| = {err:.2e}")
+    got = out.cpu().numpy()
+    err = np.abs(got - ref).max()
+    rel = check_relative(got, ref, 4, CORR_REL, "correction")
+    log(f"[correction 128K T={T}] max|err| = {err:.2e} normalised {rel:.2e} (max|out| {np.abs(ref).max():.2e})")
     assert err <= OUT_TOL
 
 
@@ -186,8 +193,10 @@ def test_append_then_correct_then_decode_chain():
     torch.cuda.synchronize()
     h.check_device_errors()
     assert n_d.cpu().tolist() == n.tolist() == [1505]
-    err = np.abs(out.cpu().numpy() - oracle.correction_attention(q, kc, vc, n)).max()
-    log(f"[loop] correction after {T} appends: max|err| = {err:.2e}")
+    got, ref = out.cpu().numpy(), oracle.correction_attention(q, kc, vc, n)
+    err = np.abs(got - ref).max()
+    rel = check_relative(got, ref, 4, CORR_REL, "correction")
+    log(f"[loop] correction after {T} appends: max|err| = {err:.2e} normalised {rel:.2e}")
     assert err <= OUT_TOL
     # the next decode step's layer over the grown cache (all retrieval)
     q1 = synth.to_bf16_bits(rng.standard_normal((1, 32, 128)).astype(np.float32) / np.sqrt(128))

@@ -2,15 +2,21 @@
 
 Each layer runs through the C ABI (binding) on the device and through the
 oracle on the host with the same inputs and the same S_in (the GPU's S_out of
-the previous layer); the bar is the one in tests/parity.py.  The small
-workloads run their whole step; the large ones run the first layers of the
-step (the full-size launch configuration of the benchmark is covered by
-test_gpu_fullsize.py)."""
+the previous layer: teacher forcing); the bar is the one in tests/parity.py,
+including the normalised output bound.  Every workload runs its whole step:
+the tiny cases, the 32-layer 32K step (also free-running: the oracle chains
+its own S and the drift from the GPU chain is reported and bounded), the
+first layers of the 128K step (all 32 layers, in the benchmark's launch
+configuration, are in test_gpu_fullsize.py), the 32-layer ragged batch-8
+step, and the 36-layer Qwen3-shaped 128K step at k = 1024 and k = 4096 with a
+tie group planted across the top-k boundary of every retrieval head of every
+layer."""
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from gpu_util import log, make_handle, plant_boundary_groups, run_layer
 from parity import compare_layer
@@ -18,24 +24,36 @@ from parity import compare_layer
 pytestmark = pytest.mark.gpu
 
 
-def _chain(w: synth.Workload, n_layers: int, plant: bool = False):
+def _chain(w: synth.Workload, n_layers: int, plant: bool = False, free_running: bool = False):
     import torch
     handle = make_handle(w)
     roles = synth.roles(w)
     lens = synth.n_ctx(w)
     n_ctx_dev = torch.from_numpy(lens).cuda()
     S_prev_dev, S_prev = None, None
+    S_free = None                      # the oracle's own chain (free running)
     stats = []
     for l in range(n_layers):
         log(f"[{w.name}] layer {l} roles={roles[l].tolist()} k={w.k}")
-        x = synth.layer_inputs(w, l, tie_info=bool(w.tie_frac) or plant)
+        x = synth.layer_inputs(w, l, tie_info=bool(w.tie_frac) or plant, threads=16)
         ties = x.pop("ties", None)
         if plant:
-            plant_boundary_groups(w, x, w.k, ties)
+            plant_boundary_groups(w, x, w.k, ties, heads=np.nonzero(roles[l])[0], layer=l)
         out, S, S_dev = run_layer(handle, x, roles[l], S_prev_dev, n_ctx_dev, w.k)
-        err, band = compare_layer(out, S, x, roles[l], S_prev, lens, w.k, w.dtype, ties=ties)
-        stats.append((l, err, band))
-        log(f"    max|err|={err:.2e} band-diffs={band}")
+        st = compare_layer(out, S, x, roles[l], S_prev, lens, w.k, w.dtype, ties=ties, threads=16)
+        msg = f"    max|err|={st[0]:.2e} normalised={st.rel:.2e} band-diffs={st[1]}"
+        if free_running:
+            out_f, S_free, _ = oracle.layer(x["q"], x["k"], x["v"], roles[l], S_free, lens, w.k, threads=16)
+            same = np.mean([len(set(S[b, g].tolist()) & set(S_free[b, g].tolist())) / min(w.k, int(lens[b]))
+                            for b in range(w.batch) for g in range(w.n_kv_heads)])
+            drift = float(np.abs(out.astype(np.float64) - out_f).max() / np.abs(out_f).max())
+            msg += f" | free-running oracle: S overlap {same:.5f}, max|out diff|/max|out| {drift:.2e}"
+            # a tolerated band swap upstream is inherited, never amplified into a different set
+            assert same >= 0.99, f"free-running S overlap {same:.5f} at layer {l}"
+            stats.append((l, st[0], st.rel, st[1], same, drift))
+        else:
+            stats.append((l, st[0], st.rel, st[1]))
+        log(msg)
         S_prev_dev, S_prev = S_dev, S
     handle.check_device_errors()
     return stats
@@ -54,18 +72,44 @@ def test_tiny_gqa_longer_chain_all_roles():
     _chain(synth.WORKLOADS["tiny_gqa"].replace(layers=6, n_retrieval=5), 6)
 
 
-def test_llama3_32k_full_step():
-    _chain(synth.WORKLOADS["llama3_32k"], 32)
+def test_llama3_32k_full_step_teacher_forced_and_free_running():
+    _chain(synth.WORKLOADS["llama3_32k"], 32, free_running=True)
 
 
 def test_llama3_128k_first_layers():
     _chain(synth.WORKLOADS["llama3_128k"], 6)
 
 
-def test_llama3_ragged_b8_first_layers():
-    _chain(synth.WORKLOADS["llama3_ragged_b8"], 4)
+def test_llama3_ragged_b8_full_step():
+    w = synth.WORKLOADS["llama3_ragged_b8"]
+    _chain(w, w.layers)
 
 
-@pytest.mark.parametrize("name", ["qwen3_128k_k1024", "qwen3_128k_k4096"])
-def test_qwen3_ties_with_planted_boundary_groups(name):
-    _chain(synth.WORKLOADS[name], 4, plant=True)
+def test_qwen3_ties_full_steps_with_planted_boundary_groups():
+    """Both budgets over the same inputs, layer by layer: one input draw per
+    layer, planted separately for each k (the k-th ranked row differs)."""
+    import torch
+    ws = [synth.WORKLOADS["qwen3_128k_k1024"], synth.WORKLOADS["qwen3_128k_k4096"]]
+    w0 = ws[0]
+    assert all(w.replace(name=w0.name, k=w0.k) == w0 for w in ws), "the two budgets share their inputs"
+    roles = synth.roles(w0)
+    lens = synth.n_ctx(w0)
+    n_ctx_dev = torch.from_numpy(lens).cuda()
+    handles = [make_handle(w) for w in ws]
+    prev = [(None, None) for _ in ws]
+    for l in range(w0.layers):
+        base = synth.layer_inputs(w0, l, tie_info=True, threads=16)
+        retr = np.nonzero(roles[l])[0]
+        for i, w in enumerate(ws):
+            x = {"q": base["q"], "k": base["k"].copy(), "v": base["v"]}
+            ties = {key: list(v) for key, v in base["ties"].items()}
+            plant_boundary_groups(w, x, w.k, ties, heads=retr, layer=l)
+            S_prev_dev, S_prev = prev[i]
+            out, S, S_dev = run_layer(handles[i], x, roles[l], S_prev_dev, n_ctx_dev, w.k)
+            st = compare_layer(out, S, x, roles[l], S_prev, lens, w.k, w.dtype, ties=ties, threads=16)
+            log(f"[{w.name}] layer {l} roles={roles[l].tolist()} max|err|={st[0]:.2e} "
+                f"normalised={st.rel:.2e} band-diffs={st[1]} planted heads={retr.tolist()}")
+            prev[i] = (S_dev, S)
+            del x
+    for h in handles:
+        h.check_device_errors()

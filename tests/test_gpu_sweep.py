@@ -71,3 +71,8 @@ def test_sweep_trends_on_a_reduced_grid():
     for name, ok in sweep.checks(rows):
         log(f"[sweep] {'PASS' if ok else 'FAIL'}: {name}")
         assert ok, name
+    # the pages' 4/8 claim is reported, not asserted (where it fails is measured, not hidden)
+    name, ok, losers = sweep.half_sparse_claim(rows)
+    log(f"[sweep] {'PASS' if ok else 'FAIL'}: {name}")
+    for r in losers:
+        log(f"[sweep]   4/8 loses: batch {r['batch']} n {r['n']}: {r['us']:.1f} vs dense {r['dense_us']:.1f} us")
