@@ -38,6 +38,7 @@ EXPORTED = (
     "lychee_dense_decode_layer", "lychee_kv_append", "lychee_correction_attention",
     "lychee_validate_layer", "lychee_set_stream", "lychee_set_profile_events",
     "lychee_check_device_errors", "lychee_destroy", "lychee_status_str", "lychee_last_error",
+    "lychee_decode_layer_static",
 )
 
 
@@ -82,6 +83,7 @@ def load() -> ctypes.CDLL:
         "lychee_destroy": (None, [vp]),
         "lychee_status_str": (ctypes.c_char_p, [i32]),
         "lychee_last_error": (ctypes.c_char_p, []),
+        "lychee_decode_layer_static": (i32, [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -119,6 +121,21 @@ def validate_layer(dims: Dims, q, k_cache, v_cache, role_mask, S_in, S_out, out,
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def decode_layer_static(dims: Dims, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k, stream=None):
+    """lychee_decode_layer_static: one hybrid layer without a handle or a
+    workspace (the library's per-GPU scratch); tensors as for
+    Handle.decode_layer, ``stream`` a torch stream (default: the current one)."""
+    import torch
+    role = np.ascontiguousarray(np.asarray(role_mask, dtype=np.uint8).reshape(-1))
+    if role.size != dims.n_kv_heads:
+        raise ValueError(f"role_mask has {role.size} entries, expected {dims.n_kv_heads}")
+    st = stream if stream is not None else torch.cuda.current_stream()
+    _check(load().lychee_decode_layer_static(ctypes.byref(dims), ctypes.c_void_p(st.cuda_stream), _ptr(q),
+                                             _ptr(k_cache), _ptr(v_cache), role.ctypes.data_as(ctypes.c_void_p),
+                                             _ptr(S_in), _ptr(S_out), _ptr(out), _ptr(n_ctx), int(k)),
+           "lychee_decode_layer_static")
 
 
 class Handle:

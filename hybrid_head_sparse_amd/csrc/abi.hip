@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "../../include/lychee.h"
@@ -29,9 +30,36 @@ struct lychee_handle {
     hipEvent_t ev_stop;
 };
 
+// Scratch of the allocation-free entry point (lychee_decode_layer_static):
+// one copy per GPU, held until the process ends.  In host code the name is a
+// host-side stand-in, never a device address: the device address comes from
+// hipGetSymbolAddress, once per device (g_static below).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Clears `words` 32-bit words (the workspace's zero region) with plain vector
+// stores: a kernel rather than a memset node, so the call can be captured.
+__global__ void __launch_bounds__(256) zero_fill_kernel(uint32_t* p, size_t words) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
 namespace {
 
 thread_local std::string g_last_error;
+
+// Per-device state of the allocation-free entry point.  `zero_prefix`: bytes
+// at the start of the device's scratch known to be zero once the work already
+// enqueued completes (every call restores its zero region, which starts at
+// offset 0; a call whose zero region is longer clears the difference first).
+constexpr int kMaxDevices = 64;
+struct StaticScratch {
+    bool ready;
+    void* ptr;
+    size_t zero_prefix;
+    int cus;
+};
+StaticScratch g_static[kMaxDevices];
+std::mutex g_static_mutex;
 
 lychee_status fail(lychee_status s, const char* fmt, ...) {
     char buf[512];
@@ -320,6 +348,64 @@ lychee_status lychee_decode_layer_select(lychee_handle* h, const void* q, const 
     lychee_status s = lychee_validate_layer(&h->dims, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k);
     if (s != LYCHEE_OK) return s;
     return run_layer(h, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k, true, rule, param);
+}
+
+lychee_status lychee_decode_layer_static(const lychee_dims* dims, void* stream, const void* q, const void* k_cache,
+                                         const void* v_cache, const uint8_t* role_mask, const int32_t* S_in,
+                                         int32_t* S_out, float* out, const int32_t* n_ctx, int32_t k) {
+    lychee_status s = lychee_validate_layer(dims, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k);
+    if (s != LYCHEE_OK) return s;
+    const Workspace need = carve_workspace(nullptr, dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                                           dims->max_ctx, dims->k_max, false);
+    if (need.total_bytes > kScratchBytes)
+        return fail(LYCHEE_ERR_WORKSPACE,
+                    "these dims need %zu bytes of scratch; the allocation-free entry point has %zu (use "
+                    "lychee_decode_layer with a workspace)", need.total_bytes, kScratchBytes);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(LYCHEE_ERR_HIP, "cannot query the current HIP device");
+    if (dev < 0 || dev >= kMaxDevices) return fail(LYCHEE_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    hipStream_t st = (hipStream_t)stream;
+    lychee_handle h{};
+    {
+        std::lock_guard<std::mutex> lock(g_static_mutex);
+        StaticScratch& ss = g_static[dev];
+        if (!ss.ready) {
+            void* ptr = nullptr;
+            hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !ptr)
+                return fail(LYCHEE_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+            int cus = 0;
+            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+                return fail(LYCHEE_ERR_HIP, "cannot query the compute units of device %d", dev);
+            ss.ptr = ptr;
+            ss.cus = cus;
+            ss.zero_prefix = 0;
+            ss.ready = true;
+        }
+        h.dims = *dims;
+        h.ws_base = ss.ptr;
+        h.ws_bytes = kScratchBytes;
+        h.ws = carve_workspace(ss.ptr, dims->batch, dims->n_q_heads, dims->n_kv_heads, dims->head_dim, dims->max_ctx,
+                               dims->k_max, false);
+        h.stream = st;
+        h.device = dev;
+        h.cus = ss.cus;
+        h.per_cu = 1;
+        // The zero region starts at offset 0 in every layout and ends with the
+        // error-flag words, which calls latch rather than restore (and which
+        // need not start at zero here: nothing reads them): the calls keep
+        // [0, err) at zero.  Clear what earlier calls have not left at zero.
+        const size_t keep_zero = (size_t)((char*)h.ws.err - (char*)ss.ptr);
+        if (keep_zero > ss.zero_prefix) {
+            const size_t from = ss.zero_prefix, words = (keep_zero - from) / 4;
+            hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)((words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024)),
+                               dim3(256), 0, st, (uint32_t*)((char*)ss.ptr + from), words);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "clearing the scratch failed: %s", hipGetErrorString(e));
+        }
+        ss.zero_prefix = keep_zero;
+    }
+    return run_layer(&h, q, k_cache, v_cache, role_mask, S_in, S_out, out, n_ctx, k, true);
 }
 
 lychee_status lychee_dense_decode_layer(lychee_handle* h, const void* q, const void* k_cache, const void* v_cache,

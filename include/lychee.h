@@ -169,6 +169,32 @@ lychee_status lychee_decode_layer_select(lychee_handle* h,
                                          float* out, const int32_t* n_ctx, int32_t k, int32_t rule,
                                          double param);
 
+/* For callers that cannot allocate device memory or own a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): lychee_decode_layer without a handle or workspace.  Same
+ * arguments, layouts, results and host-side checks as lychee_decode_layer,
+ * plus the dims (host) and the HIP stream (hipStream_t as void*; NULL = the
+ * null stream).  The kernels' scratch (partial records, counters, selection
+ * candidates) lives in a 64 MiB device array inside the library, one per GPU,
+ * held until the process ends; this call allocates and frees nothing.
+ *   - Dims whose decode scratch exceeds 64 MiB return LYCHEE_ERR_WORKSPACE
+ *     before anything is enqueued.  The scratch is about 12 bytes per cached
+ *     row (batch * n_kv_heads * max_ctx) plus 4 * 66 * G * (d + 2) + 16 KiB
+ *     per (sequence, KV head) plus 4 MiB: the Llama3-8B shape fits at
+ *     batch 1 up to max_ctx 2^18 and at batch 8 up to 64K.
+ *   - The first call on a device (and any call whose layout needs a longer
+ *     zeroed region than earlier calls left) enqueues one small clearing
+ *     kernel before the attention kernel.
+ *   - Every call on one GPU uses that GPU's one array: calls that may overlap
+ *     on a GPU (different streams without ordering, several threads) race and
+ *     give wrong results.  Order them on one stream.
+ *   - Device-side contract flags latch inside the array and are not
+ *     reported; check a suspect input through lychee_decode_layer. */
+lychee_status lychee_decode_layer_static(const lychee_dims* dims, void* stream,
+                                         const void* q, const void* k_cache, const void* v_cache,
+                                         const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out,
+                                         float* out, const int32_t* n_ctx, int32_t k);
+
 /* Dense all-heads decode attention over the same layout (every head attends
  * to all n_ctx[b] tokens, Eq. 1 without selection): the baseline the hybrid
  * step is compared with.  Same argument meanings as above. */

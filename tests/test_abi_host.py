@@ -153,3 +153,19 @@ def test_valid_selection_rules_reach_the_handle_check(lib, rule, param):
 def test_block_rule_needs_k_of_at_least_one_block(lib):
     st = lib.lychee_decode_layer_select(None, None, None, None, None, None, None, None, None, 32, 4, 64.0)
     assert st == hhs.LYCHEE_ERR_INVALID_ARG and "block" in lib.lychee_last_error().decode()
+
+
+def test_static_entry_rejects_dims_beyond_its_scratch(lib):
+    """The allocation-free entry point checks its arguments and its scratch
+    limit on the host, before anything touches a device."""
+    p = _good_ptrs()
+    big = _dims(batch=16, max_ctx=131072)                      # 128 heads x 128K rows: > 64 MiB
+    role = (ctypes.c_uint8 * 8)(*([1] * 8))
+    st = lib.lychee_decode_layer_static(ctypes.byref(big), None, p["q"], p["k_cache"], p["v_cache"], role, None,
+                                        p["S_out"], p["out"], p["n_ctx"], 64)
+    assert st == hhs.LYCHEE_ERR_WORKSPACE
+    assert "64" in lib.lychee_last_error().decode() or "scratch" in lib.lychee_last_error().decode()
+    bad = _dims()
+    st = lib.lychee_decode_layer_static(ctypes.byref(bad), None, None, p["k_cache"], p["v_cache"], role, None,
+                                        p["S_out"], p["out"], p["n_ctx"], 64)
+    assert st == hhs.LYCHEE_ERR_INVALID_ARG
