@@ -21,7 +21,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblychee.so")
+# LYCHEE_LIB selects another build of the same library (the phase-timestamp
+# build liblychee_trace.so, for hybrid_head_sparse_amd.timeline)
+LIB_PATH = os.environ.get("LYCHEE_LIB") or os.path.join(_HERE, "liblychee.so")
 
 LYCHEE_OK = 0
 LYCHEE_ERR_INVALID_ARG = -1
@@ -89,6 +91,9 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if hasattr(lib, "lychee_set_trace"):          # the phase-timestamp build
+        lib.lychee_set_trace.restype = i32
+        lib.lychee_set_trace.argtypes = [vp, vp, ctypes.c_uint32]
     _lib = lib
     return lib
 
@@ -259,6 +264,14 @@ class Handle:
         sp = None if start is None else ctypes.c_void_p(start.cuda_event)
         ep = None if stop is None else ctypes.c_void_p(stop.cuda_event)
         _check(load().lychee_set_profile_events(self._h, sp, ep), "lychee_set_profile_events")
+
+    def set_trace(self, buffer=None, launch: int = 0):
+        """Phase timestamps of the following attention launches into the
+        uint64 tensor ``buffer`` (trace build only; None stops)."""
+        lib = load()
+        if not hasattr(lib, "lychee_set_trace"):
+            raise RuntimeError("set_trace needs the trace build (LYCHEE_LIB=.../liblychee_trace.so)")
+        _check(lib.lychee_set_trace(self._h, _ptr(buffer), int(launch)), "lychee_set_trace")
 
     def check_device_errors(self):
         _check(load().lychee_check_device_errors(self._h), "lychee_check_device_errors")

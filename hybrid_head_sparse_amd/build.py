@@ -1,6 +1,9 @@
 """Compile the gfx950 library liblychee.so in-tree with hipcc.
 
-    python -m hybrid_head_sparse_amd.build
+    python -m hybrid_head_sparse_amd.build            # liblychee.so
+    python -m hybrid_head_sparse_amd.build --trace    # liblychee_trace.so: the same
+        library with phase timestamps in the attention kernel (a measuring aid,
+        read by hybrid_head_sparse_amd.timeline)
 """
 from __future__ import annotations
 
@@ -14,6 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblychee.so")
+TRACE_BUILD = os.path.join(HERE, "_build_trace")
+TRACE_LIB = os.path.join(HERE, "liblychee_trace.so")
 SOURCES = ["attend.hip", "rules.hip", "correction.hip", "abi.hip"]
 ARCH = os.environ.get("LYCHEE_OFFLOAD_ARCH", "gfx950")
 
@@ -32,9 +37,9 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+def _compile(src: str, trace: bool = False) -> str:
+    obj = os.path.join(TRACE_BUILD if trace else BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *HIPCC_FLAGS, *(["-DLYCHEE_TRACE"] if trace else []), "-I", os.path.join(ROOT, "include"), "-c",
            os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -42,21 +47,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, trace: bool = False) -> str:
+    out = TRACE_LIB if trace else LIB
+    os.makedirs(TRACE_BUILD if trace else BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, trace), SOURCES))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    build(trace="--trace" in sys.argv[1:])
     sys.exit(0)

@@ -26,8 +26,11 @@ struct lychee_handle {
     int device;
     int cus;             // compute units of the device
     int per_cu;          // persistent workgroups per compute unit
+    uint32_t cost_sparse; // pool cost of a gathered row
     hipEvent_t ev_start;
     hipEvent_t ev_stop;
+    unsigned long long* trace;   // phase timestamps (LYCHEE_TRACE build), or null
+    uint32_t trace_launch;
 };
 
 // Scratch of the allocation-free entry point (lychee_decode_layer_static):
@@ -225,8 +228,17 @@ lychee_status lychee_create(const lychee_dims* dims, void* workspace, size_t wor
     }
     h->cus = cus;
     h->per_cu = per_cu;
+    // pool cost of a gathered S row against a streamed row's kCostRetrieval:
+    // kCostSparse, or LYCHEE_POOL_COST_SPARSE (4..12) when set
+    h->cost_sparse = kCostSparse;
+    if (const char* env = getenv("LYCHEE_POOL_COST_SPARSE")) {
+        const int v = atoi(env);
+        if (v >= 4 && v <= 12) h->cost_sparse = (uint32_t)v;
+    }
     h->ev_start = nullptr;
     h->ev_stop = nullptr;
+    h->trace = nullptr;
+    h->trace_launch = 0;
     if (hipMemsetAsync(h->ws.zero_begin, 0, h->ws.zero_bytes, h->stream) != hipSuccess) {
         delete h;
         return fail(LYCHEE_ERR_HIP, "clearing the workspace counters failed");
@@ -278,6 +290,9 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
     ap.sel_keys_only = hybrid && rule == LYCHEE_SELECT_BLOCK ? 1u : 0u;
     // The kernel's selection key is the fp32 sum of the G query heads' raw
     // dot products, i.e. G sqrt(d) times the pooled score: tau maps there.
+    ap.trace = h->trace;
+    ap.trace_launch = h->trace_launch;
+    ap.cost_sparse = h->cost_sparse;
     ap.sel_tkey = rule == LYCHEE_SELECT_THRESHOLD
                       ? float_key((float)(param * (double)G * std::sqrt((double)d.head_dim)))
                       : 0u;
@@ -391,6 +406,7 @@ lychee_status lychee_decode_layer_static(const lychee_dims* dims, void* stream, 
         h.device = dev;
         h.cus = ss.cus;
         h.per_cu = 1;
+        h.cost_sparse = kCostSparse;
         // The zero region starts at offset 0 in every layout and ends with the
         // error-flag words, which calls latch rather than restore (and which
         // need not start at zero here: nothing reads them): the calls keep
@@ -514,5 +530,14 @@ lychee_status lychee_check_device_errors(lychee_handle* h) {
 }
 
 void lychee_destroy(lychee_handle* h) { delete h; }
+
+#ifdef LYCHEE_TRACE
+lychee_status lychee_set_trace(lychee_handle* h, void* buffer, uint32_t launch) {
+    if (!h) return fail(LYCHEE_ERR_INVALID_ARG, "handle is NULL");
+    h->trace = (unsigned long long*)buffer;
+    h->trace_launch = launch;
+    return ok();
+}
+#endif
 
 }  // extern "C"

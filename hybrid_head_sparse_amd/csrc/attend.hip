@@ -52,6 +52,29 @@
 namespace lychee {
 namespace {
 
+// Phase timestamps of the LYCHEE_TRACE build (thread 0 of each workgroup);
+// compiled out otherwise.
+#ifdef LYCHEE_TRACE
+#define LYCHEE_STAMP(slot)                                                                                 \
+    do {                                                                                                   \
+        if (p.trace && threadIdx.x == 0)                                                                   \
+            p.trace[((size_t)p.trace_launch * gridDim.x + blockIdx.x) * kTraceSlots + (slot)] =            \
+                __builtin_amdgcn_s_memrealtime();                                                          \
+    } while (0)
+#define LYCHEE_TRACE_SET(slot, v)                                                                          \
+    do {                                                                                                   \
+        if (p.trace && threadIdx.x == 0)                                                                   \
+            p.trace[((size_t)p.trace_launch * gridDim.x + blockIdx.x) * kTraceSlots + (slot)] = (v);       \
+    } while (0)
+#else
+#define LYCHEE_STAMP(slot) \
+    do {                   \
+    } while (0)
+#define LYCHEE_TRACE_SET(slot, v) \
+    do {                          \
+    } while (0)
+#endif
+
 constexpr int kDppRowRor8 = 0x128;
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor2 = 0x122;
@@ -265,7 +288,7 @@ constexpr int merge_lds_floats() { return G * kMergeMax + 2 * G; }
 // Wavefront w owns heads w, w+4, ..: its lanes load (m, l) of one or two
 // records each, reduce M = max m and L = sum l 2^(m - M) across the wavefront,
 // and leave the per-record scales 2^(m - M) in LDS.  The o loads of the first
-// 32/OPT records are issued before that and land while it runs; the output
+// CH records (a whole level-1 group of 32 when G D <= 512) are issued before that and land while it runs; the output
 // pass then reads the scales as wavefront-uniform (broadcast) LDS words.  If
 // `out` is non-null the normalised output o / l is written there (query heads
 // contiguous, D floats each); otherwise the merged record goes to `dst` with
@@ -274,7 +297,8 @@ template <int D, int G>
 __device__ void merge_records(const float* recs, int count, float* dst, float* out, float* s_ml) {
     constexpr int RS = G * (D + 2);
     constexpr int OPT = (G * D + kAttendThreads - 1) / kAttendThreads;   // outputs per thread
-    constexpr int CH = 32 / OPT;                                        // records per load batch
+    constexpr int CH = 32 / OPT;                                        // records per load batch (a level-1
+                                                                        // group of 32 in one round trip)
     constexpr int HPW = (G + kWaves - 1) / kWaves;                      // heads per wavefront
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float* s_sc = s_ml;                     // [G][kMergeMax]
@@ -394,6 +418,12 @@ __device__ __forceinline__ unsigned long long composite(uint32_t key, uint32_t i
     return ((unsigned long long)(key & ((1u << kLowBits) - 1u)) << kIdxBits) | (unsigned long long)(kIdxMask - idx);
 }
 __device__ __forceinline__ uint32_t comp_index(unsigned long long c) { return kIdxMask - (uint32_t)(c & kIdxMask); }
+// The whole selection order as one 64-bit value: the key, then the smaller
+// index first (kIdxMask - idx): a key wins iff this value is at least the
+// k-th largest one.
+__device__ __forceinline__ unsigned long long full_order(uint32_t key, uint32_t idx) {
+    return ((unsigned long long)key << 32) | (unsigned long long)(kIdxMask - idx);
+}
 __device__ __forceinline__ uint32_t comp_digit(unsigned long long c, int shift, int bits) {
     return (uint32_t)(c >> shift) & ((1u << bits) - 1u);
 }
@@ -535,26 +565,40 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         };
         uint32_t h[256];
     };
+    struct FastLds {                          // the candidate resolver (fast_resolve)
+        union {
+            uint32_t h12[HYBRID ? kHistBins : 1];     // the head's first-digit histogram (up to the crossing)
+            uint32_t map[HYBRID ? kFastBatch : 1];    // then: the candidate row of each entry of a batch
+        };
+        uint32_t wm[HYBRID ? kMaxWG : 1];         // workgroup words: candidates | bound << 20
+        uint32_t coff[HYBRID ? kMaxWG + 1 : 1];   // flat offset of each workgroup's candidates
+        uint32_t key[HYBRID ? kFastBatch : 1];    // a batch of candidates, entry f at [f]
+        uint32_t idx[HYBRID ? kFastBatch : 1];
+        alignas(16) unsigned long long comp[HYBRID ? kFastGroup : 1];   // the threshold digit's composites
+        uint32_t jc[HYBRID ? kFastPer * kWaves : 1];   // winners per (step, wavefront), then their prefix
+    };
     union Lds {
         StreamLds st;
         SelectLds se;
+        FastLds fr;
     };
     __shared__ __attribute__((aligned(16))) Lds u;
     __shared__ uint32_t s_pref[kMaxBH + 1];
     __shared__ uint32_t s_bound[kMaxWG + 1];   // cost position where each workgroup's range starts
+    __shared__ uint32_t s_first[kMaxBH + 1];   // first workgroup of each head
     __shared__ int32_t s_nctx[kMaxBH];
     __shared__ uint32_t s_ke[kMaxBH];          // tokens a retrieval head of sequence b selects
     __shared__ uint32_t s_wave[kWaves];
     __shared__ uint32_t s_res[4];
-    __shared__ uint32_t s_ctr;
-    __shared__ uint32_t s_lcnt;       // a pass's kept keys staged so far
     __shared__ int s_flag[2];
-    __shared__ uint32_t s_sel[4];     // selection arrival: role, candidates of the head, slice or helpers, slices taken
+    __shared__ uint32_t s_sel[4];     // selection arrival: 1 if this workgroup resolves the head's top-k
     __shared__ int s_rel;
     __shared__ uint32_t s_ceq;        // resolver: threshold-digit composites appended so far
+    __shared__ unsigned long long s_cut;   // resolver: the smallest winning full_order of the threshold digit
 
+    LYCHEE_STAMP(kTrEntry);
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
     const int row = lane >> 4, x = lane & 15;
     const int xh = x >> LOG2G, xl = x & (G - 1);
     const int BH = p.B * p.Hkv;
@@ -597,7 +641,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 const int b = bg / p.Hkv, g = bg - b * p.Hkv;
                 const int n = s_nctx[b];
                 const bool retr = !HYBRID || ((p.role_bits >> g) & 1ull);
-                cost = retr ? kCostRetrieval * (uint32_t)n : kCostSparse * (uint32_t)min(p.k, n);
+                cost = retr ? kCostRetrieval * (uint32_t)n : p.cost_sparse * (uint32_t)min(p.k, n);
             }
             u_[i] = cost;
             tot += cost;
@@ -617,11 +661,14 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     const uint32_t U = s_pref[BH];
     int P = (int)gridDim.x;
     {
-        const uint32_t pmax = U / kMinCostPerWG;
+        const uint32_t pmax = U / (64u * p.cost_sparse);   // never split the pool finer than 64 gathered rows
         if ((uint32_t)P > pmax) P = (int)(pmax < 1 ? 1 : pmax);
     }
     const int w = blockIdx.x;
-    if (w >= P) return;
+    if (w >= P) {
+        LYCHEE_STAMP(kTrExit);
+        return;
+    }
 
     auto is_retr = [&](int hb) -> bool { return !HYBRID || ((p.role_bits >> (hb % p.Hkv)) & 1ull); };
     // Heads of a sequence with no context (out of contract, flagged in the
@@ -651,10 +698,17 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         }
         return cnt - 1;
     };
-    // Workgroup boundaries: the equal split of the cost axis, moved up to the
-    // next row boundary of the head it falls in (so every range holds whole
-    // rows).  Every workgroup tabulates all P+1 of them once, in parallel.
-    const uint32_t qU = U / (uint32_t)P, rU = U % (uint32_t)P;   // ww * rU < P^2 <= 2^22
+    // Workgroup boundaries, head-aligned: head h gets the workgroups
+    // [first(h), first(h+1)) with first(h) = round(P pref(h) / U) (cumulative
+    // rounding: the counts sum to P and follow the heads' costs), and its
+    // rows are split evenly among them, so a workgroup pays one head's fixed
+    // costs (query loads, S staging, record, selection hand-off) once.  A
+    // head whose share rounds to no workgroup falls into the range of the
+    // workgroup before it, which then spans heads (many small heads).  Every
+    // workgroup tabulates all P+1 boundaries once, in parallel.
+    for (int h = tid; h <= BH; h += kAttendThreads)
+        s_first[h] = U ? (uint32_t)(((unsigned long long)P * s_pref[h] + U / 2u) / U) : 0u;
+    __syncthreads();
     for (int ww = tid; ww <= P; ww += kAttendThreads) {
         uint32_t bnd;
         if (ww == 0) {
@@ -662,16 +716,16 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         } else if (ww >= P) {
             bnd = U;
         } else {
-            const uint32_t raw = (uint32_t)ww * qU + ((uint32_t)ww * rU) / (uint32_t)P;   // = floor(ww U / P)
-            int a = 0, z = BH - 1;                 // head holding raw (serial search per thread)
+            int a = 0, z = BH - 1;                 // last head with first(h) <= ww
             while (a < z) {
                 const int mid = (a + z + 1) >> 1;
-                if (s_pref[mid] <= raw) a = mid; else z = mid - 1;
+                if (s_first[mid] <= (uint32_t)ww) a = mid; else z = mid - 1;
             }
-            const uint32_t h0 = s_pref[a], h1 = s_pref[a + 1], off = raw - h0;
-            const uint32_t cwa = is_retr(a) ? kCostRetrieval : kCostSparse;
-            const uint32_t up = cwa * ((off + cwa - 1u) / cwa);   // next row start
-            bnd = min(h0 + up, h1);
+            const uint32_t h0 = s_pref[a], h1 = s_pref[a + 1];
+            const uint32_t cwa = is_retr(a) ? kCostRetrieval : p.cost_sparse;
+            const uint32_t rows = (h1 - h0) / cwa;
+            const uint32_t i = (uint32_t)ww - s_first[a], nwh = s_first[a + 1] - s_first[a];   // nwh >= 1
+            bnd = h0 + cwa * (uint32_t)(((unsigned long long)i * rows) / nwh);
         }
         s_bound[ww] = bnd;
     }
@@ -692,6 +746,10 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         w1 = n1;
     };
     const uint32_t lo = s_bound[w], hi = s_bound[w + 1];
+    LYCHEE_STAMP(kTrPrologue);
+#ifdef LYCHEE_TRACE
+    uint32_t tr_flags = 0, tr_heads = 0;
+#endif
 
     // Classify the candidates this thread holds (slot e is candidate
     // base + tid + 256 e; slots from nslots on, or past C, hold none): key above
@@ -728,8 +786,11 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     };
 
     // Exact top-k of one retrieval head, for the slices [j0, j1) of its
-    // context (slice j starts at bitmap word j W / kResolveSlices, rounded
-    // down to 4 words): the final first-digit histogram gives the threshold
+    // context, by the full-scan path (force_fb: every key of the head re-read
+    // from the score buffer; the fallback of fast_resolve below, for heads
+    // whose candidates or threshold group exceed its LDS).  Slice j starts at
+    // bitmap word j W / kResolveSlices, rounded down to 4 words.  Without
+    // force_fb (not used by this kernel) the final first-digit histogram gives the threshold
     // digit T and the count above it; every key with digit >= T is in the
     // candidate list.  Every slice's resolver reads all of them and reaches the
     // same T and the same winners among the keys of digit T; it marks only the
@@ -737,7 +798,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     // first position in S) and writes its part of S_out.  The resolver that
     // finishes reading the head's histogram and counters last, over all
     // slices, restores them to zero.
-    auto resolve_topk = [&](int hb, int n, uint32_t ke, uint32_t C, uint32_t j0, uint32_t j1) {
+    auto resolve_topk = [&](int hb, int n, uint32_t ke, uint32_t C, uint32_t j0, uint32_t j1, bool force_fb) {
         int32_t* srow = p.S_out + (size_t)hb * p.k;
         const unsigned long long* cand = p.ws.cand + (size_t)hb * p.max_ctx;
         const uint32_t* sc = p.ws.score + (size_t)hb * p.max_ctx;
@@ -843,7 +904,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // exact from T up and the candidates hold every key from T up, so T
             // is the head's threshold digit.  Otherwise a pass held more than its
             // margin of the head's top keys: count and use every key instead.
-            fb = bmaxv > T_;
+            fb = force_fb || bmaxv > T_;
             release_head();
             uint32_t Cs = C;
             if (fb) {
@@ -1096,22 +1157,352 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         __syncthreads();
     };
 
-    // A retrieval head's top-k is resolved in kResolveSlices slices of its
-    // context.  Slice j goes to the head's free selection arrival number j (one
-    // whose range ends in the head), a helper, or to the last arrival: the
-    // helper polls, once its own work is done, for the last arrival, which
-    // still has its record and merges to do, and takes the slice if it gets
-    // there first.  Each of the two adds its vote to the slice's rclaim word
-    // once: 1 = helper, ready; 2 = helper, gave up waiting; 4 = last.  The
-    // first ready vote resolves; the second vote restores the word to zero.
-    // The last arrival takes the slices that have no helper without a vote.
-    int pend_bg = -1;              // head this workgroup waits for after its range
-    uint32_t pend_nw = 0, pend_ke = 0, pend_slice = 0;
-    int pend_n = 0;
-    auto vote = [&](int word, uint32_t v) -> uint32_t {   // one lane; returns the earlier votes
-        const uint32_t old = counter_add(&p.ws.rclaim[word], v);
-        if (old != 0u) counter_reset(&p.ws.rclaim[word]);
-        return old;
+    // Crossing of the LDS histogram u.se.h12 at `need` (see block_crossing).
+    auto crossing_h12 = [&](uint32_t need) {
+        uint32_t hc[kHistPerThread];
+        // thread t takes descending ranks 16t.. = bins 4095-16t down to 4080-16t
+        const uint4* hv = reinterpret_cast<const uint4*>(u.se.h12 + kHistBins - kHistPerThread * (tid + 1));
+#pragma unroll
+        for (int c = 0; c < kHistPerThread / 4; ++c) {
+            const uint4 v4 = hv[c];
+            hc[kHistPerThread - 1 - 4 * c] = v4.x;
+            hc[kHistPerThread - 2 - 4 * c] = v4.y;
+            hc[kHistPerThread - 3 - 4 * c] = v4.z;
+            hc[kHistPerThread - 4 - 4 * c] = v4.w;
+        }
+        block_crossing<kHistPerThread>(hc, kHistBins, need, s_wave, s_res);
+    };
+
+    // Exact top-k of one retrieval head (Eq. 2: the k_eff largest pooled
+    // scores, ties to the lower token index), resolved by the head's last
+    // selection arrival from the candidates the head's workgroups appended
+    // (each in its own region, in position order, with its candidate count
+    // and largest pass bound in its word):
+    //  1. the head's histogram and the words in one round of loads; the
+    //     crossing at k_eff gives the threshold digit T.  A workgroup whose
+    //     bound lies above T kept too few keys and left its counts in
+    //     [T, bound) out of the histogram: its rows are re-read from the
+    //     score buffer and counted, and the crossing is taken again -- exact
+    //     now, since every key of digit >= T is counted -- and its keys from
+    //     the final T up replace its candidates;
+    //  2. the candidates, workgroup after workgroup (so in position order),
+    //     are gathered kFastBatch at a time: a map gives each flat entry its
+    //     row, every thread loads its kFastPer entries at once and writes
+    //     them to LDS lane-consecutively, and the keys of digit T are
+    //     collected as composites (rest of the key, then the inverted index);
+    //  3. the cut: the (k_eff - count above T)-th largest composite;
+    //  4. an ordered compaction of each batch: ballots count the winners of
+    //     every (step, wavefront), one block scan gives each its first
+    //     position, and the winners are written in flat order.
+    // The code runs once per head and launch: loads are issued in batches
+    // (one round trip each) and the loops stay rolled elsewhere.  Heads whose
+    // threshold-digit keys overflow kFastGroup return true and take
+    // resolve_topk's full scan instead (from the caller's single call site,
+    // so that both stay inlined and the kernel's parameters stay in
+    // registers).
+    auto fast_resolve = [&](int hb, int n, uint32_t ke, uint32_t h0, int wf, int nw) -> bool {
+        int32_t* srow = p.S_out + (size_t)hb * p.k;
+        const unsigned long long* cand = p.ws.cand + (size_t)hb * p.max_ctx;
+        const uint32_t* sc = p.ws.score + (size_t)hb * p.max_ctx;
+        uint32_t* gh = p.ws.hist + (size_t)hb * kHistBins;
+        const uint32_t hh1 = h0 + kCostRetrieval * (uint32_t)n;   // the head's end on the cost axis
+        uint32_t* s_wm = u.fr.wm;
+        uint32_t* s_coff = u.fr.coff;
+        auto rows_of = [&](int i, uint32_t& r0, uint32_t& r1) {   // rows of the head's i-th workgroup
+            r0 = (max(s_bound[wf + i], h0) - h0) / kCostRetrieval;
+            r1 = (min(s_bound[wf + i + 1], hh1) - h0) / kCostRetrieval;
+        };
+        __syncthreads();
+        // 1. histogram (restored to zero once read) and words
+        {
+            uint32_t gv[kHistPerThread];                         // every load in flight at once
+#pragma unroll
+            for (int j = 0; j < kHistPerThread; ++j) gv[j] = coherent_load(&gh[tid + kAttendThreads * j]);
+            constexpr int WPT = kMaxWG / kAttendThreads;
+            uint32_t wv[WPT];
+#pragma unroll
+            for (int e = 0; e < WPT; ++e) {
+                const int i = tid + kAttendThreads * e;
+                wv[e] = i < nw ? coherent_load(&p.ws.wmeta[wf + i + hb]) : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < kHistPerThread; ++j) {
+                u.fr.h12[tid + kAttendThreads * j] = gv[j];
+                coherent_store(&gh[tid + kAttendThreads * j], 0u);
+            }
+#pragma unroll
+            for (int e = 0; e < WPT; ++e) {
+                const int i = tid + kAttendThreads * e;
+                if (i < nw) s_wm[i] = wv[e];
+            }
+        }
+        if (ke == (uint32_t)n && p.sel_tkey == 0u) {          // every token
+            for (uint32_t i = tid; i < (uint32_t)n; i += kAttendThreads) srow[i] = (int32_t)i;
+            for (int i = n + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
+            __syncthreads();
+            return false;
+        }
+        __syncthreads();
+        LYCHEE_STAMP(kTrResolve0 + 0);
+        auto crossing = [&]() {
+            uint32_t hc[kHistPerThread];
+            // thread t takes descending ranks 16t.. = bins 4095-16t down to 4080-16t
+            const uint4* hv = reinterpret_cast<const uint4*>(u.fr.h12 + kHistBins - kHistPerThread * (tid + 1));
+#pragma unroll
+            for (int c = 0; c < kHistPerThread / 4; ++c) {
+                const uint4 v4 = hv[c];
+                hc[kHistPerThread - 1 - 4 * c] = v4.x;
+                hc[kHistPerThread - 2 - 4 * c] = v4.y;
+                hc[kHistPerThread - 3 - 4 * c] = v4.z;
+                hc[kHistPerThread - 4 - 4 * c] = v4.w;
+            }
+            block_crossing<kHistPerThread>(hc, kHistBins, ke, s_wave, s_res);
+        };
+        auto count_failing = [&](uint32_t Tc) -> uint32_t {
+            uint32_t f = 0;
+            for (int i = tid; i < nw; i += kAttendThreads) f += (s_wm[i] >> 20) > Tc ? 1u : 0u;
+            uint32_t nf;
+            (void)block_exclusive_scan(f, s_wave, &nf);
+            return nf;
+        };
+        crossing();
+        uint32_t Td = s_res[0], c_above = s_res[1];
+        if (count_failing(Td)) {
+            // counts in [T, bound) of the workgroups whose bound lies above T
+            for (int i = 0; i < nw; ++i) {                       // (uniform loop)
+                const uint32_t bi = s_wm[i] >> 20;
+                if (bi <= Td) continue;
+                uint32_t r0, r1;
+                rows_of(i, r0, r1);
+#pragma unroll 8
+                for (uint32_t j = r0 + tid; j < r1; j += kAttendThreads) {
+                    const uint32_t d = key_digit(coherent_load(&sc[j]));
+                    if (d >= Td && d < bi) atomicAdd(&u.fr.h12[d], 1u);
+                }
+            }
+            __syncthreads();
+            crossing();
+            Td = s_res[0];
+            c_above = s_res[1];
+            // their keys from the final T up replace their candidates
+            const uint32_t kb = (uint32_t)digit_first_key(Td);
+            unsigned long long* cw = p.ws.cand + (size_t)hb * p.max_ctx;
+            for (int i = 0; i < nw; ++i) {                       // (uniform loop)
+                if ((s_wm[i] >> 20) <= Td) continue;
+                uint32_t r0, r1;
+                rows_of(i, r0, r1);
+                uint32_t written = 0;
+                for (uint32_t base = r0; base < r1; base += kAttendThreads * 8) {
+                    uint32_t m8 = 0, kv[8];
+                    for (int e = 0; e < 8; ++e) {                // thread t: rows base + 8t .. 8t + 7
+                        const uint32_t j = base + 8u * (uint32_t)tid + (uint32_t)e;
+                        kv[e] = j < r1 ? coherent_load(&sc[j]) : 0u;
+                        m8 |= (uint32_t)(j < r1 && kv[e] >= kb) << e;
+                    }
+                    uint32_t tot;
+                    uint32_t at = written + block_exclusive_scan((uint32_t)__popc(m8), s_wave, &tot);
+                    for (int e = 0; e < 8; ++e)
+                        if ((m8 >> e) & 1u) coherent_store(&cw[r0 + at++], pack_cand(kv[e], base + 8u * (uint32_t)tid + (uint32_t)e));
+                    written += tot;
+                }
+                if (tid == 0) s_wm[i] = written | (Td << 20);
+                __syncthreads();
+            }
+            wait_stores_complete();
+            __syncthreads();
+        }
+        LYCHEE_STAMP(kTrResolve0 + 1);
+        // 2. candidates: flat offsets of the workgroups' runs
+        uint32_t C;
+        {
+            uint32_t mine = 0;
+            const int per = (nw + kAttendThreads - 1) / kAttendThreads;   // contiguous per thread
+            for (int e = 0; e < per; ++e) {
+                const int i = tid * per + e;
+                mine += i < nw ? (s_wm[i] & 0xFFFFFu) : 0u;
+            }
+            uint32_t at = block_exclusive_scan(mine, s_wave, &C);
+            for (int e = 0; e < per; ++e) {
+                const int i = tid * per + e;
+                if (i < nw) {
+                    s_coff[i] = at;
+                    at += s_wm[i] & 0xFFFFFu;
+                }
+            }
+            if (tid == 0) s_coff[nw] = C;
+            if (tid == 0) s_ceq = 0u;
+        }
+        __syncthreads();
+        LYCHEE_STAMP(kTrResolve0 + 5);
+        LYCHEE_TRACE_SET(13, (unsigned long long)C | ((unsigned long long)Td << 32));
+        const uint32_t klo = (uint32_t)digit_first_key(Td);       // key range of digit T
+        const uint32_t khi = (uint32_t)(digit_first_key(Td + 1u) - 1ull);
+        const uint32_t tkey = p.sel_tkey;
+        const uint32_t nbatch = (C + kFastBatch - 1u) / kFastBatch;
+        const uint32_t last = (uint32_t)p.k - 1u;
+        const unsigned long long lt_mask = (1ull << lane) - 1ull;   // lanes below this one
+        unsigned long long cut = 0ull;                            // winners: full_order >= cut
+        uint32_t total = 0;
+        // Entry f of a batch (flat order) sits at LDS slot f = 256 j + tid:
+        // thread t holds entries t, t + 256, .. (kFastPer of them), so every
+        // LDS access below is lane-consecutive.  Pass 0 gathers each batch
+        // and collects the threshold digit's composites, then takes the cut;
+        // pass 1 emits the winners of each batch in flat order (gathering
+        // again only when there is more than one batch).
+        for (int pass = 0; pass < 2; ++pass) {
+            for (uint32_t bb = 0; bb < nbatch; ++bb) {
+                const uint32_t b0 = bb * (uint32_t)kFastBatch, len = min((uint32_t)kFastBatch, C - b0);
+                if (pass == 0 || nbatch > 1u) {
+                    // source row of every entry: thread t writes workgroup t's run
+                    for (int i = tid; i < nw; i += kAttendThreads) {
+                        const uint32_t ci = s_coff[i];
+                        const uint32_t f0 = max(ci, b0), f1 = max(f0, min(s_coff[i + 1], b0 + len));
+                        const uint32_t r = (max(s_bound[wf + i], h0) - h0) / kCostRetrieval + (f0 - ci);
+                        for (uint32_t f = f0; f < f1; ++f) u.fr.map[f - b0] = r + (f - f0);
+                    }
+                    __syncthreads();
+                    // all kFastPer loads in flight at once (straight-line code
+                    // kept short: reads, loads, writes; rows past the batch
+                    // load the head's first entry, unused)
+                    {
+                        uint32_t at[kFastPer];
+#pragma unroll
+                        for (int j = 0; j < kFastPer; ++j) at[j] = u.fr.map[kAttendThreads * j + tid];
+                        unsigned long long e[kFastPer];
+#pragma unroll
+                        for (int j = 0; j < kFastPer; ++j)
+                            e[j] = coherent_load(&cand[kAttendThreads * j + tid < len ? at[j] : 0u]);
+#pragma unroll
+                        for (int j = 0; j < kFastPer; ++j) {
+                            u.fr.key[kAttendThreads * j + tid] = (uint32_t)e[j];
+                            u.fr.idx[kAttendThreads * j + tid] = (uint32_t)(e[j] >> 32);
+                        }
+                    }
+                    LYCHEE_STAMP(kTrResolve0 + 10);
+                    if (pass == 0) {
+                        // keys of digit T (own entries only: no barrier needed
+                        // before reading them back), placed by one block scan
+                        uint32_t mm = 0;
+#pragma unroll 1
+                        for (int j0 = 0; j0 < kFastPer; j0 += 8) {
+                            uint32_t kk[8];
+#pragma unroll
+                            for (int e2 = 0; e2 < 8; ++e2) kk[e2] = u.fr.key[kAttendThreads * (j0 + e2) + tid];
+#pragma unroll
+                            for (int e2 = 0; e2 < 8; ++e2)
+                                mm |= (uint32_t)(kAttendThreads * (j0 + e2) + tid < len && kk[e2] >= klo &&
+                                                 kk[e2] <= khi) << (j0 + e2);
+                        }
+                        uint32_t gtot;
+                        uint32_t q = s_ceq + block_exclusive_scan((uint32_t)__popc(mm), s_wave, &gtot);
+                        while (mm) {
+                            const int j = __builtin_ctz(mm);
+                            mm &= mm - 1u;
+                            const uint32_t f = kAttendThreads * j + tid;
+                            if (q < (uint32_t)kFastGroup) u.fr.comp[q] = full_order(u.fr.key[f], u.fr.idx[f]);
+                            ++q;
+                        }
+                        __syncthreads();
+                        if (tid == 0) s_ceq += gtot;
+                    }
+                    __syncthreads();
+                    LYCHEE_STAMP(kTrResolve0 + 8);
+                }
+                if (pass == 0) continue;
+                // winners of each (j, wavefront) step (lane j keeps step j's
+                // count), then their flat prefix
+                uint32_t mk = 0, cj = 0;
+#pragma unroll 1
+                for (int j0 = 0; j0 < kFastPer; j0 += 8) {
+                    uint32_t kk[8], ii[8];
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) {
+                        const uint32_t f = kAttendThreads * (j0 + e2) + tid;
+                        kk[e2] = u.fr.key[f];
+                        ii[e2] = u.fr.idx[f];
+                    }
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) {
+                        const uint32_t f = kAttendThreads * (j0 + e2) + tid;
+                        const bool wv = f < len && full_order(kk[e2], ii[e2]) >= cut;
+                        const uint32_t c = (uint32_t)__popcll(__ballot(wv));
+                        mk |= (uint32_t)wv << (j0 + e2);
+                        cj = lane == j0 + e2 ? c : cj;
+                    }
+                }
+                if (lane < kFastPer) u.fr.jc[lane * kWaves + wave] = cj;
+                __syncthreads();
+                LYCHEE_STAMP(kTrResolve0 + 9);
+                uint32_t tot;
+                const uint32_t pre = block_exclusive_scan(tid < kFastPer * kWaves ? u.fr.jc[tid] : 0u, s_wave, &tot);
+                if (tid < kFastPer * kWaves) u.fr.jc[tid] = pre;
+                __syncthreads();
+#pragma unroll 1
+                for (int j0 = 0; j0 < kFastPer; j0 += 8) {
+                    uint32_t base[8], ii[8];
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) {
+                        base[e2] = u.fr.jc[(j0 + e2) * kWaves + wave];
+                        ii[e2] = u.fr.idx[kAttendThreads * (j0 + e2) + tid];
+                    }
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) {
+                        const bool wv = (mk >> (j0 + e2)) & 1u;
+                        const unsigned long long bw = __ballot(wv);
+                        if (wv) srow[min(total + base[e2] + (uint32_t)__popcll(bw & lt_mask), last)] = (int32_t)ii[e2];
+                    }
+                }
+                total += tot;
+                __syncthreads();
+            }
+            if (pass == 1) break;
+            LYCHEE_STAMP(kTrResolve0 + 3);
+            const uint32_t g = s_ceq;
+            LYCHEE_TRACE_SET(14, (unsigned long long)g | ((unsigned long long)c_above << 32));
+            LYCHEE_TRACE_SET(15, (unsigned long long)ke | ((unsigned long long)nw << 32));
+            if (g > (uint32_t)kFastGroup || c_above > ke || ke - c_above > g) {
+                // more keys of digit T than LDS holds (or counts that disagree): full scan
+                __syncthreads();
+                return true;
+            }
+            // the cut among digit T: the r_left-th largest composite (winners >= cut)
+            const uint32_t r_left = ke - c_above;
+            if (r_left == 0u) {                                    // none of digit T
+                cut = khi == 0xFFFFFFFFu ? ~0ull : (unsigned long long)(khi + 1u) << 32;
+            } else if (r_left == g) {                              // all of digit T
+                cut = (unsigned long long)klo << 32;
+            } else {
+                // rank every composite against all (at most kFastGroup / 256 = 4
+                // per thread), 8 composites read per round trip
+                for (uint32_t q0 = tid; q0 < g; q0 += kAttendThreads) {
+                    const unsigned long long mine = u.fr.comp[q0];
+                    uint32_t above = 0, q = 0;
+                    for (; q + 8u <= g; q += 8u) {
+                        unsigned long long c8[8];
+#pragma unroll
+                        for (int e2 = 0; e2 < 8; ++e2) c8[e2] = u.fr.comp[q + e2];
+#pragma unroll
+                        for (int e2 = 0; e2 < 8; ++e2) above += c8[e2] > mine;
+                    }
+                    for (; q < g; ++q) above += u.fr.comp[q] > mine;
+                    if (above == r_left - 1u) s_cut = mine;
+                }
+                __syncthreads();
+                cut = s_cut;
+            }
+            // the threshold rule keeps no key below tkey
+            cut = max(cut, (unsigned long long)tkey << 32);
+            LYCHEE_STAMP(kTrResolve0 + 4);
+        }
+        LYCHEE_STAMP(kTrResolve0 + 6);
+        // padding after the kept tokens; the count must be k_eff (at most that
+        // under the threshold rule)
+        const uint32_t kept = min(total, ke);
+        for (int i = (int)kept + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
+        if (tid == 0 && (tkey ? total > ke : total != ke)) atomicOr(p.ws.err, 2u);
+        __syncthreads();
+        LYCHEE_STAMP(kTrResolve0 + 7);
+        return false;
     };
 
     for (int bg = head_of(lo); bg < BH && s_pref[bg] < hi; ++bg) {
@@ -1119,12 +1510,17 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         if (h1 <= lo || h1 == h0) continue;
         const int b = bg / p.Hkv, g = bg - b * p.Hkv;
         const bool retr = is_retr(bg);
-        const uint32_t cw = retr ? kCostRetrieval : kCostSparse;
+        const uint32_t cw = retr ? kCostRetrieval : p.cost_sparse;
         const uint32_t seg_lo = (max(lo, h0) - h0) / cw;     // first row (position) of this head
         const uint32_t seg_hi = (min(hi, h1) - h0) / cw;
         const int n = s_nctx[b];
         const uint32_t ks = (uint32_t)min(p.k, n);         // S entries of the head
         const uint32_t ke = s_ke[b];                          // tokens a retrieval head selects
+#ifdef LYCHEE_TRACE
+        if (tr_heads == 0) LYCHEE_STAMP(kTrHeadStart);
+        ++tr_heads;
+        tr_flags |= retr ? 1u : 2u;
+#endif
 
         // query slices: register h' holds query head g*G + (h' ^ xl), elements x*EPL..
         Frag<NDW> qf[G];
@@ -1281,9 +1677,11 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         const int nw = wl - wf + 1;
         if (!HYBRID) {
             stream_range(seg_lo, seg_hi, nullptr);
+            LYCHEE_STAMP(kTrStreamEnd);
         } else if (retr) {
             uint32_t* sc = p.ws.score + (size_t)bg * p.max_ctx;
             uint32_t* gh = p.ws.hist + (size_t)bg * kHistBins;
+            uint32_t w_count = 0, w_bound = 0;   // candidates appended, largest pass bound
             for (int i = tid; i < kHistBins; i += kAttendThreads) u.st.hist[i] = 0u;
             // equal passes of at most kKeyCap rows (no short tail pass)
             const uint32_t npass = (seg_hi - seg_lo + kKeyCap - 1) / kKeyCap;
@@ -1295,6 +1693,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 __syncthreads();
                 stream_range(c_lo, c_hi, nullptr);
                 __syncthreads();
+                LYCHEE_STAMP(kTrStreamEnd);
                 // every key to the score buffer (read only if the bound below fails,
                 // or by the rule-selection kernel)
                 for (uint32_t i = tid; i < len; i += kAttendThreads) coherent_store(&sc[c_lo + i], u.st.keys[i]);
@@ -1326,72 +1725,73 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                         hc[kHistPerThread - 4 - 4 * c] = v4.w;
                     }
                 }
-                if (tid == 0) s_lcnt = 0u;
                 block_crossing<kHistPerThread>(hc, kHistBins, need, s_wave, s_res);
                 const uint32_t Tw = s_res[0];
-                const uint32_t nkeep = s_res[3];                      // keys with digit >= Tw
-                // wavefront 0: the pass's bound to the head's bound word and a
-                // range of the candidate list for its keys from Tw up (it waits
-                // for that reply alone); wavefronts 1-3: the pass's counts from Tw
-                // up to the head's histogram (few bins, so few atomics on any one
-                // of them; other workgroups add to the same bins), then zeros
-                if (wave == 0) {
-                    if (tid == 0) {
-                        __hip_atomic_fetch_max(&p.ws.bmax[bg], Tw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        s_ctr = nkeep ? (uint32_t)counter_add64(&p.ws.selctr[bg], nkeep) : 0u;
-                    }
-                } else {
-                    for (int i = tid - 64; i < kHistBins; i += kAttendThreads - 64) {
-                        const uint32_t cnt = u.st.hist[i];
-                        if (cnt && (uint32_t)i >= Tw) atomicAdd(&gh[i], cnt);
-                        u.st.hist[i] = 0u;                           // the next pass starts from zero
-                    }
+                // the pass's counts from Tw up to the head's histogram (few bins,
+                // so few atomics on any one of them; other workgroups add to the
+                // same bins), then zeros for the next pass
+#pragma unroll
+                for (int c = 0; c < kHistPerThread; ++c) {
+                    const int i = tid + kAttendThreads * c;
+                    const uint32_t cnt = u.st.hist[i];
+                    if (cnt && (uint32_t)i >= Tw) atomicAdd(&gh[i], cnt);
+                    u.st.hist[i] = 0u;
                 }
-                // while the reservation travels: the kept positions to LDS (any
-                // order: the selector's result does not depend on it) ...
+                // Keys from Tw up, in position order, appended to this
+                // workgroup's region of the head's candidate list (it starts at
+                // the range's first row, and a pass keeps at most its rows):
+                // thread t flags positions 16t .. 16t + 15, a block scan ranks
+                // them, and the kept positions are staged in LDS for consecutive
+                // device-coherent stores.
                 {
                     const uint32_t kb = (uint32_t)digit_first_key(Tw);  // Tw <= kTopDigit: a real key
-                    for (uint32_t i = tid; i < len; i += kAttendThreads) {
-                        if (u.st.keys[i] >= kb) {
-                            const uint32_t at = atomicAdd(&s_lcnt, 1u);
-                            if (at < (uint32_t)kKeyCap) u.st.gbuf[at] = i;
-                        }
+                    uint32_t m16 = 0;
+                    const uint4* k4 = reinterpret_cast<const uint4*>(u.st.keys + 16 * tid);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint4 v = k4[c];
+                        const uint32_t i0 = 16u * (uint32_t)tid + 4u * (uint32_t)c;
+                        m16 |= (uint32_t)(i0 + 0u < len && v.x >= kb) << (4 * c + 0);
+                        m16 |= (uint32_t)(i0 + 1u < len && v.y >= kb) << (4 * c + 1);
+                        m16 |= (uint32_t)(i0 + 2u < len && v.z >= kb) << (4 * c + 2);
+                        m16 |= (uint32_t)(i0 + 3u < len && v.w >= kb) << (4 * c + 3);
                     }
-                }
-                __syncthreads();
-                // ... then out with consecutive device-coherent stores
-                {
-                    unsigned long long* cand = p.ws.cand + (size_t)bg * p.max_ctx;
-                    const uint32_t base = s_ctr, cnt = min(nkeep, (uint32_t)kKeyCap);
-                    for (uint32_t j = tid; j < cnt; j += kAttendThreads) {
+                    uint32_t kept;
+                    uint32_t at = block_exclusive_scan((uint32_t)__popc(m16), s_wave, &kept);
+                    while (m16) {
+                        const int e = __ffs(m16) - 1;
+                        m16 &= m16 - 1u;
+                        u.st.gbuf[at++] = 16u * (uint32_t)tid + (uint32_t)e;
+                    }
+                    __syncthreads();
+                    unsigned long long* cand = p.ws.cand + (size_t)bg * p.max_ctx + seg_lo + w_count;
+                    for (uint32_t j = tid; j < kept; j += kAttendThreads) {
                         const uint32_t off = u.st.gbuf[j];
-                        if (base + j < (uint32_t)p.max_ctx)
-                            coherent_store(&cand[base + j], pack_cand(u.st.keys[off], c_lo + off));
+                        coherent_store(&cand[j], pack_cand(u.st.keys[off], c_lo + off));
                     }
+                    w_count += kept;
+                    w_bound = max(w_bound, Tw);
                 }
                 __syncthreads();
             }
-            // Selection arrival, before the record: once its stores (candidates,
-            // scores, histogram and bound atomics) complete, this workgroup's
-            // part of the head's selection is in place.  Arrivals whose range
-            // ends in this head also count as free ones.  Roles in resolving
-            // the top-k (below): 1 the last arrival (with the number of helpers
-            // before it); 2 one of the first kResolveSlices free arrivals that
-            // is not last, a helper for slice number = free arrivals before it.
+            // Selection arrival, before the record: this workgroup's word (its
+            // candidates and largest bound) and, once every store above is
+            // complete, one count on the head's arrival counter; the last
+            // arrival resolves the head's top-k (fast_resolve, after its
+            // record and merges).
+            if (tid == 0 && !p.sel_keys_only) coherent_store(&p.ws.wmeta[w + bg], w_count | (w_bound << 20));
             wait_stores_complete();
             __syncthreads();
-            if (tid == 0 && p.sel_keys_only) s_sel[0] = 0u;   // no top-k to resolve
-            if (tid == 0 && !p.sel_keys_only) {
-                const bool ends_here = h1 >= hi;
-                const unsigned long long o64 =
-                    counter_add64(&p.ws.selctr[bg], kSelArrival | (ends_here ? kSelFreeArrival : 0ull));
-                const uint32_t before = (uint32_t)(o64 >> 32) & 0xFFFFu;   // arrivals before this one
-                const uint32_t free_before = (uint32_t)(o64 >> 48);
-                const bool last = before + 1u == (uint32_t)nw;
-                s_sel[0] = last ? 1u : (ends_here && free_before < (uint32_t)kResolveSlices ? 2u : 0u);
-                s_sel[1] = (uint32_t)o64;                // candidates of the whole head when last
-                s_sel[2] = last ? min(free_before, (uint32_t)kResolveSlices) : free_before;
+            if (tid == 0) {
+                uint32_t last = 0;
+                if (!p.sel_keys_only) {
+                    const uint32_t before = (uint32_t)counter_add64(&p.ws.selctr[bg], 1ull);
+                    last = before + 1u == (uint32_t)nw;
+                    if (last) counter_reset64(&p.ws.selctr[bg]);
+                }
+                s_sel[0] = last;
             }
+            LYCHEE_STAMP(kTrSelArrive);
         } else {
             // sparse head: stage the S entries of the range in LDS (one batched
             // load per chunk), forward them to S_out, then gather-stream
@@ -1446,6 +1846,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 }
                 stream_range(c_lo, c_hi, u.st.idx);
             }
+            LYCHEE_STAMP(kTrStreamEnd);
             // entries past min(k, n) (the -1 padding of a short context) belong
             // to the workgroup that finishes the head
             if (Sout && h1 <= hi) {
@@ -1513,6 +1914,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         const int nc = (nw + kCombineFanIn - 1) / kCombineFanIn;
         const int csize = min(kCombineFanIn, nw - c * kCombineFanIn);
         wait_stores_complete();
+        LYCHEE_STAMP(kTrRecordDone);
         __syncthreads();
         if (tid == 0) {
             uint32_t* ctr = p.ws.cnt1 + (size_t)bg * kLevel2Max + c;
@@ -1522,9 +1924,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             s_flag[0] = last;
         }
         __syncthreads();
+        LYCHEE_STAMP(kTrArrive);
         const uint32_t sel_role = (HYBRID && retr) ? s_sel[0] : 0u;
-        const uint32_t C_head = s_sel[1];
-        const uint32_t sel_aux = s_sel[2];           // helpers before the last arrival, or a helper's slice
         if (s_flag[0]) {
             const float* grp = p.ws.rec1 + (size_t)(wf + c * kCombineFanIn + bg) * RS;
             float* out_bg = p.out + ((size_t)b * Hq + (size_t)g * G) * D;
@@ -1545,62 +1946,33 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 __syncthreads();
                 if (s_flag[0]) merge_records<D, G>(p.ws.rec2 + (size_t)bg * kLevel2Max * RS, nc, nullptr, out_bg, u.st.ml);
             }
+            LYCHEE_STAMP(kTrMergeDone);
+#ifdef LYCHEE_TRACE
+            tr_flags |= 4u;
+#endif
         }
-        if (sel_role == 1u) {
-            // the last arrival votes on each slice that has a helper and takes
-            // the slices with none, or whose helper gave up or is still waiting
-            if (wave == 0) {
-                uint32_t old = 0;
-                if (lane < kResolveSlices && (uint32_t)lane < sel_aux)
-                    old = vote(bg * kResolveSlices + lane, 4u);
-                const unsigned long long take = __ballot(lane < kResolveSlices && (old == 0u || old == 2u));
-                if (lane == 0) s_sel[3] = (uint32_t)take;
+        if (sel_role == 1u) {        // the head's last selection arrival resolves its top-k
+            LYCHEE_STAMP(kTrResolveStart);
+#ifdef LYCHEE_TRACE
+            tr_flags |= 8u;
+#endif
+            if (fast_resolve(bg, n, ke, h0, wf, nw)) {
+#ifdef LYCHEE_TRACE
+                tr_flags |= 32u;
+#endif
+                resolve_topk(bg, n, ke, 0u, 0u, (uint32_t)kResolveSlices, true);
             }
-            __syncthreads();
-            const uint32_t take = s_sel[3];
-            for (uint32_t j0 = 0; j0 < (uint32_t)kResolveSlices;) {     // each run of taken slices at once
-                if (!((take >> j0) & 1u)) {
-                    ++j0;
-                    continue;
-                }
-                uint32_t j1 = j0 + 1u;
-                while (j1 < (uint32_t)kResolveSlices && ((take >> j1) & 1u)) ++j1;
-                resolve_topk(bg, n, ke, C_head, j0, j1);
-                j0 = j1;
-            }
-        } else if (sel_role == 2u) {   // the range ends in this head: wait and vote after the loop
-            pend_bg = bg;
-            pend_nw = (uint32_t)nw;
-            pend_n = n;
-            pend_ke = ke;
-            pend_slice = sel_aux;
+            LYCHEE_STAMP(kTrResolveEnd);
         }
 
         __syncthreads();
     }
 
-    if (HYBRID && pend_bg >= 0) {
-        if (tid == 0) {
-            // wait (bounded) for the last arrival, or for its vote
-            uint32_t ready = 0, C = 0;
-            for (int it = 0; it < kResolveWaitPolls; ++it) {
-                const unsigned long long s = coherent_load(&p.ws.selctr[pend_bg]);
-                const uint32_t votes = coherent_load(&p.ws.rclaim[pend_bg * kResolveSlices + pend_slice]);
-                if (((uint32_t)(s >> 32) & 0xFFFFu) == pend_nw) {
-                    ready = 1;
-                    C = (uint32_t)s;
-                    break;
-                }
-                if (votes != 0u) break;     // the last arrival voted first
-                __builtin_amdgcn_s_sleep(4);
-            }
-            const uint32_t old = vote(pend_bg * kResolveSlices + pend_slice, ready ? 1u : 2u);
-            s_flag[0] = ready && old == 0u;
-            s_res[2] = C;
-        }
-        __syncthreads();
-        if (s_flag[0]) resolve_topk(pend_bg, pend_n, pend_ke, s_res[2], pend_slice, pend_slice + 1u);
-    }
+#ifdef LYCHEE_TRACE
+    LYCHEE_TRACE_SET(kTrFlags, tr_flags);
+    LYCHEE_TRACE_SET(kTrHeads, tr_heads);
+#endif
+    LYCHEE_STAMP(kTrExit);
 }
 
 template <typename T, int D, int G, bool HYBRID>
@@ -1634,6 +2006,9 @@ hipError_t launch_d(const AttendParams& p, int D, int G, int cus, int per_cu, hi
 
 hipError_t launch_attend(const AttendParams& p, int dtype, int D, int G, bool hybrid, int cus, int per_cu,
                          hipStream_t stream) {
+#ifdef LYCHEE_ONE_VARIANT   // compile-time probe of one variant's resources (not a library build)
+    return hybrid ? launch_one<BF16, 128, 4, true>(p, cus, per_cu, stream) : hipErrorInvalidValue;
+#endif
     if (dtype == 1) return hybrid ? launch_d<BF16, true>(p, D, G, cus, per_cu, stream)
                                   : launch_d<BF16, false>(p, D, G, cus, per_cu, stream);
     if (dtype == 0) return hybrid ? launch_d<F32, true>(p, D, G, cus, per_cu, stream)

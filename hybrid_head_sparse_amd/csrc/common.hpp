@@ -27,7 +27,6 @@ constexpr int kLevel2Max = kMaxWG / kCombineFanIn + 2;
 // gives the sparse workgroups fewer rows and the retrieval workgroups more.
 constexpr uint32_t kCostRetrieval = 4;
 constexpr uint32_t kCostSparse = 8;
-constexpr uint32_t kMinCostPerWG = 64 * kCostSparse;   // never split the pool finer than this
 constexpr int kIdxChunk = 2048;       // sparse S positions staged in LDS per pass
 constexpr int kKeyCap = 4096;         // retrieval selection keys kept in LDS per pass
 
@@ -46,17 +45,15 @@ constexpr int kCandLds = 4096;                // threshold-digit candidates reso
 // candidates and wins (1102 -> 1076 us); 3.5 and 3 fall back often enough to
 // lose (1185 and 1295 us).
 constexpr uint32_t kSelMargin = 2;
-// Polls (about 1 us each) a helper spends waiting for the head's last arrival
-// before leaving its slice of the top-k to it.
-constexpr int kResolveWaitPolls = 64;
-// Slices of a retrieval head's context whose top-k winners are resolved by
-// separate workgroups (each reads every candidate, marks and writes its slice).
+// Slices of the context bitmap of the full-scan resolver (the fallback of the
+// candidate resolver: every key of the head re-read).
 constexpr int kResolveSlices = 8;
-// Increments of a head's selection counter: candidates in bits 0..31,
-// arrivals in bits 32..47, arrivals whose range ends in the head in 48..63.
-constexpr unsigned long long kSelArrival = 1ull << 32;
-constexpr unsigned long long kSelFreeArrival = 1ull << 48;
-static_assert(kMaxWG < (1 << 16) && kMaxCtx <= (1ll << 32), "selection counter fields");
+// The candidate resolver stages a head's candidates in LDS kFastBatch at a
+// time and resolves threshold-digit groups of at most kFastGroup keys.
+constexpr int kFastBatch = 8192;
+constexpr int kFastPer = kFastBatch / kAttendThreads;   // entries per thread of a batch
+constexpr int kFastGroup = 1024;
+static_assert(kMaxCtx <= (1 << 20), "a workgroup's candidate count fits 20 bits of its word");
 // Workgroups per retrieval head of the rule-selection kernel (Top-p and block
 // rules: each works on a slice of the head; the last to arrive cuts the set).
 constexpr int kRuleSplit = 16;
@@ -127,6 +124,9 @@ struct Workspace {
     float* rec1;                 // [(kMaxWG + BH) * RS]      level-1 partial records
     float* rec2;                 // [BH * kLevel2Max * RS]    level-2 partial records
     unsigned long long* cand;    // [BH * max_ctx]            selection candidates (key | index << 32)
+    uint32_t* wmeta;             // [kMaxWG + BH]             per (workgroup w, head bg) at w + bg: the
+                                 //                           candidates it appended | its largest pass
+                                 //                           bound << 20 (retrieval heads)
     uint32_t* score;             // [BH * max_ctx]            every selection key of a retrieval head
                                  //                           (read when a head's bounds fail, and by
                                  //                           the rule-selection kernel)
@@ -136,12 +136,8 @@ struct Workspace {
     // ---- zero-initialised region (restored to zero by every call) ----
     uint32_t* cnt1;              // [BH * kLevel2Max]         level-1 arrival counters
     uint32_t* cnt2;              // [BH]                      level-2 arrival counters
-    unsigned long long* selctr;  // [BH]                      candidates appended (bits 0..31) |
-                                 //                           workgroups done appending (32..47) |
-                                 //                           those whose range ends in the head (48..63)
-    uint32_t* bmax;              // [BH]                      largest candidate bound used for the head
-    uint32_t* rclaim;            // [BH * kResolveSlices]     votes of a helper and the last arrival on
-                                 //                           who resolves a slice of a head's top-k
+    unsigned long long* selctr;  // [BH]                      workgroups done appending their candidates
+    uint32_t* bmax;              // [BH]                      (full-scan resolver) largest bound used
     uint32_t* rdone;             // [BH]                      slices whose resolver has read the head's
                                  //                           histogram and counters
     uint32_t* hist;              // [BH * kHistBins]          first-digit counts from each pass's bound up
@@ -178,7 +174,6 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_cnt2 = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_sc = take(sizeof(unsigned long long) * (size_t)BH);
     size_t o_bmax = take(sizeof(uint32_t) * (size_t)BH);
-    size_t o_rclaim = take(sizeof(uint32_t) * (size_t)BH * kResolveSlices);
     size_t o_rdone = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_hist = take(sizeof(uint32_t) * (size_t)BH * kHistBins);
     size_t o_pctr = take(sizeof(uint32_t) * (size_t)BH);
@@ -187,6 +182,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_rec1 = take(sizeof(float) * (size_t)(kMaxWG + BH) * RS);
     size_t o_rec2 = take(sizeof(float) * (size_t)BH * kLevel2Max * RS);
     size_t o_cand = take(sizeof(unsigned long long) * (size_t)BH * max_ctx);
+    size_t o_wmeta = take(sizeof(uint32_t) * (size_t)(kMaxWG + BH));
     size_t o_score = take(sizeof(uint32_t) * (size_t)BH * max_ctx);
     size_t o_prec = take(sizeof(unsigned long long) * (size_t)BH * kRuleSplit * 4);
     const size_t CW = (size_t)(BH > 512 ? BH : 512);
@@ -200,6 +196,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.rec1 = (float*)(p + o_rec1);
         w.rec2 = (float*)(p + o_rec2);
         w.cand = (unsigned long long*)(p + o_cand);
+        w.wmeta = (uint32_t*)(p + o_wmeta);
         w.score = (uint32_t*)(p + o_score);
         w.prec = (unsigned long long*)(p + o_prec);
         w.crec_ml = with_correction ? (float*)(p + o_crml) : nullptr;
@@ -208,7 +205,6 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.cnt2 = (uint32_t*)(p + o_cnt2);
         w.selctr = (unsigned long long*)(p + o_sc);
         w.bmax = (uint32_t*)(p + o_bmax);
-        w.rclaim = (uint32_t*)(p + o_rclaim);
         w.rdone = (uint32_t*)(p + o_rdone);
         w.hist = (uint32_t*)(p + o_hist);
         w.pctr = (uint32_t*)(p + o_pctr);
@@ -240,6 +236,31 @@ struct AttendParams {
     // Retrieval heads only write every token's key to the score buffer and
     // leave S to a later kernel (the block rule): no top-k.
     uint32_t sel_keys_only;
+    // Phase timestamps (the LYCHEE_TRACE build only; null otherwise):
+    // kTraceSlots 64-bit words per workgroup and launch, at
+    // (trace_launch * gridDim.x + blockIdx.x) * kTraceSlots.
+    unsigned long long* trace;
+    uint32_t trace_launch;
+    uint32_t cost_sparse;   // pool cost of a gathered S row (a streamed row costs kCostRetrieval)
+};
+
+// Slots of a workgroup's phase-timestamp record (s_memrealtime, 100 MHz).
+enum TraceSlot {
+    kTrEntry = 0,        // first instruction
+    kTrPrologue,         // cost prefix and range boundaries ready
+    kTrHeadStart,        // first head of the range: before its query loads
+    kTrStreamEnd,        // last head's streaming (or gathering) done
+    kTrSelArrive,        // last retrieval head: selection arrival counted
+    kTrRecordDone,       // last head: partial record stored and complete
+    kTrArrive,           // last head: record arrival counted
+    kTrMergeDone,        // last merge this workgroup ran
+    kTrResolveStart,     // top-k resolve begun (last arrival or helper)
+    kTrResolveEnd,       // top-k resolve done
+    kTrExit,             // last instruction
+    kTrFlags,            // bit 0 retrieval head, 1 sparse head, 2 merger, 3 resolver, 4 helper
+    kTrHeads,            // heads the range touched
+    kTrResolve0 = 16,    // 16..27: phases inside the candidate resolver
+    kTraceSlots = 32
 };
 
 // Host launcher (defined next to the kernel).  dtype: 0 fp32, 1 bf16.  The

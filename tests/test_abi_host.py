@@ -15,6 +15,7 @@ import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lychee.h")
+TRACE_HEADER = os.path.join(ROOT, "include", "lychee_trace.h")
 
 
 @pytest.fixture(scope="module")
@@ -25,8 +26,8 @@ def lib():
     return hhs.load()
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(lychee_[a-z_]+)\s*\(", text)))
 
@@ -37,6 +38,22 @@ def test_every_declared_function_is_exported(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(hhs.EXPORTED)
+
+
+def test_trace_header_is_exported_by_the_trace_build_only(lib):
+    """include/lychee_trace.h declares what the trace build adds; the
+    product library does not carry it."""
+    from hybrid_head_sparse_amd import build
+    if not os.path.exists(build.TRACE_LIB):
+        build.build(verbose=False, trace=True)
+    tlib = ctypes.CDLL(build.TRACE_LIB)
+    extra = _declared_functions(TRACE_HEADER)
+    assert extra == ["lychee_set_trace"]
+    for name in extra:
+        assert hasattr(tlib, name), name
+        assert not hasattr(lib, name), name
+    for name in _declared_functions():
+        assert hasattr(tlib, name), name
 
 
 def _dims(**kw):
