@@ -443,7 +443,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 }
 
 // Block-wide exclusive prefix sum of one value per thread.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t inc = wave_inclusive_scan(v);
     __syncthreads();
@@ -475,7 +475,7 @@ __device__ __forceinline__ int32_t wave_inclusive_max(int32_t x) {
 
 // Block-wide exclusive max-scan of one value per thread (INT32_MIN for the
 // first thread); *total gets the block's maximum.
-__device__ int32_t block_exclusive_max(int32_t v, uint32_t* s_wave, int32_t* total) {
+__device__ __forceinline__ int32_t block_exclusive_max(int32_t v, uint32_t* s_wave, int32_t* total) {
     constexpr int32_t lo = -2147483647 - 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int32_t inc = wave_inclusive_max(v);
@@ -502,7 +502,7 @@ __device__ int32_t block_exclusive_max(int32_t v, uint32_t* s_wave, int32_t* tot
 // or above D); if the whole histogram holds fewer than `need`, D = 0 and the
 // counts above it and in all are returned.
 template <int PER>
-__device__ void block_crossing(const uint32_t (&cnt)[PER], int nbins, uint32_t need, uint32_t* s_wave,
+__device__ __forceinline__ void block_crossing(const uint32_t (&cnt)[PER], int nbins, uint32_t need, uint32_t* s_wave,
                                uint32_t* s_res) {
     uint32_t sum = 0;
 #pragma unroll
@@ -746,6 +746,54 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         w1 = n1;
     };
     const uint32_t lo = s_bound[w], hi = s_bound[w + 1];
+    // Resolve helpers.  A workgroup that holds gathered rows only is idle
+    // once its own work is done; the r-th retrieval head (head order, heads
+    // with rows) is paired with the r-th such workgroup, taken as the first
+    // workgroup of a sparse head that has at least two (so its range lies
+    // inside that head).  The pairing follows from the boundaries alone, so
+    // every workgroup derives the same one (wavefront-parallel ballots).
+    auto helper_cand = [&](int a) -> bool { return a < BH && !is_retr(a) && s_first[a + 1] >= s_first[a] + 2u; };
+    auto needs_help = [&](int a) -> bool { return a < BH && is_retr(a) && s_pref[a + 1] > s_pref[a]; };
+    auto kth_bit = [](unsigned long long m, int k) -> int {   // position of the k-th set bit (k from 0)
+        for (int t = 0; t < k; ++t) m &= m - 1ull;
+        return __ffsll((long long)m) - 1;
+    };
+    auto helper_of = [&](int X) -> int {       // X's helper workgroup, or -1
+        int r = 0;
+        for (int base = 0; base < X; base += 64) {
+            const int i = base + lane;
+            r += __popcll(__ballot(i < X && needs_help(i)));
+        }
+        for (int base = 0, seen = 0; base < BH; base += 64) {
+            const unsigned long long m = __ballot(helper_cand(base + lane));
+            const int c = __popcll(m);
+            if (seen + c > r) return (int)s_first[base + kth_bit(m, r - seen)];
+            seen += c;
+        }
+        return -1;
+    };
+    auto helped_by = [&](int ww) -> int {      // the head workgroup ww helps, or -1
+        int r = -1;
+        for (int base = 0, seen = 0; base < BH; base += 64) {
+            const int i = base + lane;
+            const bool c = helper_cand(i);
+            const unsigned long long m = __ballot(c);
+            const unsigned long long me = __ballot(c && s_first[i] == (uint32_t)ww);
+            if (me) {
+                r = seen + __popcll(m & ((1ull << (__ffsll((long long)me) - 1)) - 1ull));
+                break;
+            }
+            seen += __popcll(m);
+        }
+        if (r < 0) return -1;
+        for (int base = 0, seen = 0; base < BH; base += 64) {
+            const unsigned long long m = __ballot(needs_help(base + lane));
+            const int c = __popcll(m);
+            if (seen + c > r) return base + kth_bit(m, r - seen);
+            seen += c;
+        }
+        return -1;
+    };
     LYCHEE_STAMP(kTrPrologue);
 #ifdef LYCHEE_TRACE
     uint32_t tr_flags = 0, tr_heads = 0;
@@ -1258,20 +1306,29 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
             block_crossing<kHistPerThread>(hc, kHistBins, ke, s_wave, s_res);
         };
-        auto count_failing = [&](uint32_t Tc) -> uint32_t {
-            uint32_t f = 0;
-            for (int i = tid; i < nw; i += kAttendThreads) f += (s_wm[i] >> 20) > Tc ? 1u : 0u;
-            uint32_t nf;
-            (void)block_exclusive_scan(f, s_wave, &nf);
+        // the workgroups whose bound lies above Tc, listed in s_coff (free
+        // until the offsets are taken)
+        auto list_failing = [&](uint32_t Tc) -> uint32_t {
+            uint32_t nf = 0;
+            for (int i0 = 0; i0 < nw; i0 += kAttendThreads) {
+                const int i = i0 + tid;
+                const bool f = i < nw && (s_wm[i] >> 20) > Tc;
+                uint32_t tot;
+                const uint32_t pos = nf + block_exclusive_scan((uint32_t)f, s_wave, &tot);
+                if (f) s_coff[pos] = (uint32_t)i;
+                nf += tot;
+            }
+            __syncthreads();
             return nf;
         };
         crossing();
         uint32_t Td = s_res[0], c_above = s_res[1];
-        if (count_failing(Td)) {
+        const uint32_t nfail = list_failing(Td);
+        if (nfail) {
             // counts in [T, bound) of the workgroups whose bound lies above T
-            for (int i = 0; i < nw; ++i) {                       // (uniform loop)
+            for (uint32_t q = 0; q < nfail; ++q) {               // (uniform loop)
+                const int i = (int)s_coff[q];
                 const uint32_t bi = s_wm[i] >> 20;
-                if (bi <= Td) continue;
                 uint32_t r0, r1;
                 rows_of(i, r0, r1);
 #pragma unroll 8
@@ -1284,10 +1341,13 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             crossing();
             Td = s_res[0];
             c_above = s_res[1];
-            // their keys from the final T up replace their candidates
+            // their keys from the final T up replace their candidates (the
+            // added counts lie at digits >= T, so the final T is at least the
+            // first and the list holds every workgroup whose bound is above it)
             const uint32_t kb = (uint32_t)digit_first_key(Td);
             unsigned long long* cw = p.ws.cand + (size_t)hb * p.max_ctx;
-            for (int i = 0; i < nw; ++i) {                       // (uniform loop)
+            for (uint32_t q = 0; q < nfail; ++q) {               // (uniform loop)
+                const int i = (int)s_coff[q];
                 if ((s_wm[i] >> 20) <= Td) continue;
                 uint32_t r0, r1;
                 rows_of(i, r0, r1);
@@ -1310,6 +1370,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
             wait_stores_complete();
             __syncthreads();
+            LYCHEE_STAMP(kTrResolve0 + 2);
         }
         LYCHEE_STAMP(kTrResolve0 + 1);
         // 2. candidates: flat offsets of the workgroups' runs
@@ -1505,7 +1566,72 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         return false;
     };
 
-    for (int bg = head_of(lo); bg < BH && s_pref[bg] < hi; ++bg) {
+    // The heads of the range in order; a head whose top-k this workgroup
+    // resolves (as its last selection arrival, or as its helper once the
+    // range is done) waits in `pending` and is resolved at the top of the
+    // next pass, so the resolver has a single call site.
+    int pending = -1;
+    bool helped = false;
+    int next_bg = head_of(lo);
+    for (;;) {
+        if (pending >= 0) {
+            const int X = pending;
+            pending = -1;
+            const int b = X / p.Hkv;
+            const uint32_t h0 = s_pref[X], h1 = s_pref[X + 1];
+            int wf, wl;
+            wg_pair(h0, h1 - 1, wf, wl);
+            LYCHEE_STAMP(kTrResolveStart);
+#ifdef LYCHEE_TRACE
+            tr_flags |= 8u;
+#endif
+            if (fast_resolve(X, s_nctx[b], s_ke[b], h0, wf, wl - wf + 1)) {
+#ifdef LYCHEE_TRACE
+                tr_flags |= 32u;
+#endif
+                resolve_topk(X, s_nctx[b], s_ke[b], 0u, 0u, (uint32_t)kResolveSlices, true);
+            }
+            // the hand-off word back to idle for the next launch (both
+            // parties are done with it)
+            if (tid == 0 && coherent_load(&p.ws.hready[X]) != 0u) coherent_store(&p.ws.hready[X], 0u);
+            LYCHEE_STAMP(kTrResolveEnd);
+            __syncthreads();
+        }
+        if (!(next_bg < BH && s_pref[next_bg] < hi)) {
+            // range done: the helper duty, if any (a bounded wait for the
+            // head's last arrival; on time-out the helper withdraws and the
+            // last arrival resolves)
+            if (HYBRID && !helped && !p.sel_keys_only) {
+                helped = true;
+                const int X = helped_by(w);
+                if (X >= 0) {
+                    if (tid == 0) {
+                        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+                        uint32_t v;
+                        for (;;) {
+                            v = coherent_load(&p.ws.hready[X]);
+                            if (v == 1u) break;
+                            if (__builtin_amdgcn_s_memrealtime() - t0 > kHelperWaitTicks) {
+                                v = counter_cas(&p.ws.hready[X], 0u, 2u);   // withdraw, unless handed over meanwhile
+                                break;
+                            }
+                            __builtin_amdgcn_s_sleep(2);
+                        }
+                        s_flag[0] = v == 1u;
+                    }
+                    __syncthreads();
+                    if (s_flag[0]) {
+                        pending = X;
+#ifdef LYCHEE_TRACE
+                        tr_flags |= 64u;
+#endif
+                        continue;
+                    }
+                }
+            }
+            break;
+        }
+        const int bg = next_bg++;
         const uint32_t h0 = s_pref[bg], h1 = s_pref[bg + 1];
         if (h1 <= lo || h1 == h0) continue;
         const int b = bg / p.Hkv, g = bg - b * p.Hkv;
@@ -1776,9 +1902,12 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
             // Selection arrival, before the record: this workgroup's word (its
             // candidates and largest bound) and, once every store above is
-            // complete, one count on the head's arrival counter; the last
-            // arrival resolves the head's top-k (fast_resolve, after its
-            // record and merges).
+            // complete, one count on the head's arrival counter.  The last
+            // arrival hands the resolve to the head's helper (hready 0 -> 1;
+            // the helper polls it) or, with no helper or one that withdrew
+            // (hready 2), resolves the head's top-k itself after its record
+            // and merges.
+            const int hw = p.sel_keys_only ? -1 : helper_of(bg);
             if (tid == 0 && !p.sel_keys_only) coherent_store(&p.ws.wmeta[w + bg], w_count | (w_bound << 20));
             wait_stores_complete();
             __syncthreads();
@@ -1787,7 +1916,10 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 if (!p.sel_keys_only) {
                     const uint32_t before = (uint32_t)counter_add64(&p.ws.selctr[bg], 1ull);
                     last = before + 1u == (uint32_t)nw;
-                    if (last) counter_reset64(&p.ws.selctr[bg]);
+                    if (last) {
+                        counter_reset64(&p.ws.selctr[bg]);
+                        if (hw >= 0 && counter_cas(&p.ws.hready[bg], 0u, 1u) == 0u) last = 0;   // the helper's
+                    }
                 }
                 s_sel[0] = last;
             }
@@ -1951,19 +2083,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             tr_flags |= 4u;
 #endif
         }
-        if (sel_role == 1u) {        // the head's last selection arrival resolves its top-k
-            LYCHEE_STAMP(kTrResolveStart);
-#ifdef LYCHEE_TRACE
-            tr_flags |= 8u;
-#endif
-            if (fast_resolve(bg, n, ke, h0, wf, nw)) {
-#ifdef LYCHEE_TRACE
-                tr_flags |= 32u;
-#endif
-                resolve_topk(bg, n, ke, 0u, 0u, (uint32_t)kResolveSlices, true);
-            }
-            LYCHEE_STAMP(kTrResolveEnd);
-        }
+        if (sel_role == 1u) pending = bg;   // the head's last selection arrival resolves its top-k
 
         __syncthreads();
     }

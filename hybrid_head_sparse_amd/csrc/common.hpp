@@ -51,6 +51,9 @@ constexpr int kResolveSlices = 8;
 // The candidate resolver stages a head's candidates in LDS kFastBatch at a
 // time and resolves threshold-digit groups of at most kFastGroup keys.
 constexpr int kFastBatch = 8192;
+// A helper waits at most this long (s_memrealtime ticks, 100 MHz) for its
+// head's arrivals before it withdraws and leaves the resolve to the last one.
+constexpr unsigned long long kHelperWaitTicks = 10000;
 constexpr int kFastPer = kFastBatch / kAttendThreads;   // entries per thread of a batch
 constexpr int kFastGroup = 1024;
 static_assert(kMaxCtx <= (1 << 20), "a workgroup's candidate count fits 20 bits of its word");
@@ -111,6 +114,12 @@ __device__ __forceinline__ unsigned long long counter_add64(unsigned long long* 
 __device__ __forceinline__ void counter_reset64(unsigned long long* p) {
     __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Compare-and-swap at agent scope; returns the value found.
+__device__ __forceinline__ uint32_t counter_cas(uint32_t* p, uint32_t expect, uint32_t desired) {
+    __hip_atomic_compare_exchange_strong(p, &expect, desired, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return expect;
+}
 
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 maps as +0.
 __host__ __device__ inline uint32_t float_key(float f) {
@@ -142,6 +151,9 @@ struct Workspace {
                                  //                           histogram and counters
     uint32_t* hist;              // [BH * kHistBins]          first-digit counts from each pass's bound up
     uint32_t* pctr;              // [BH]                      rule selection: slices done
+    uint32_t* hready;            // [BH]                      helper hand-off of a retrieval head's
+                                 //                           resolve: 1 arrivals complete (the helper
+                                 //                           resolves), 2 the helper withdrew
     uint32_t* err;               // [4]
     void* zero_begin;
     size_t zero_bytes;
@@ -177,6 +189,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_rdone = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_hist = take(sizeof(uint32_t) * (size_t)BH * kHistBins);
     size_t o_pctr = take(sizeof(uint32_t) * (size_t)BH);
+    size_t o_hready = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_err = take(sizeof(uint32_t) * 4);
     const size_t z1 = off;
     size_t o_rec1 = take(sizeof(float) * (size_t)(kMaxWG + BH) * RS);
@@ -208,6 +221,7 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.rdone = (uint32_t*)(p + o_rdone);
         w.hist = (uint32_t*)(p + o_hist);
         w.pctr = (uint32_t*)(p + o_pctr);
+        w.hready = (uint32_t*)(p + o_hready);
         w.err = (uint32_t*)(p + o_err);
         w.zero_begin = p + z0;
     }
