@@ -55,16 +55,14 @@ namespace {
 // Phase timestamps of the LYCHEE_TRACE build (thread 0 of each workgroup);
 // compiled out otherwise.
 #ifdef LYCHEE_TRACE
+// tr_row: this workgroup's words, set once at kernel entry
 #define LYCHEE_STAMP(slot)                                                                                 \
     do {                                                                                                   \
-        if (p.trace && threadIdx.x == 0)                                                                   \
-            p.trace[((size_t)p.trace_launch * gridDim.x + blockIdx.x) * kTraceSlots + (slot)] =            \
-                __builtin_amdgcn_s_memrealtime();                                                          \
+        if (tr_row && threadIdx.x == 0) tr_row[(slot)] = __builtin_amdgcn_s_memrealtime();                \
     } while (0)
 #define LYCHEE_TRACE_SET(slot, v)                                                                          \
     do {                                                                                                   \
-        if (p.trace && threadIdx.x == 0)                                                                   \
-            p.trace[((size_t)p.trace_launch * gridDim.x + blockIdx.x) * kTraceSlots + (slot)] = (v);       \
+        if (tr_row && threadIdx.x == 0) tr_row[(slot)] = (v);                                              \
     } while (0)
 #else
 #define LYCHEE_STAMP(slot) \
@@ -596,6 +594,10 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     __shared__ uint32_t s_ceq;        // resolver: threshold-digit composites appended so far
     __shared__ unsigned long long s_cut;   // resolver: the smallest winning full_order of the threshold digit
 
+#ifdef LYCHEE_TRACE
+    unsigned long long* const tr_row =
+        p.trace ? p.trace + ((size_t)p.trace_launch * gridDim.x + blockIdx.x) * kTraceSlots : nullptr;
+#endif
     LYCHEE_STAMP(kTrEntry);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
@@ -605,37 +607,31 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     const int Hq = p.Hkv * G;
 
     // ---- prologue: contexts, pool cost per (b, g) and its exclusive prefix ----
+    // (thread t takes sequences and heads t, t + 256, ..: one pass when there
+    // are at most 256 of them)
     {
-        constexpr int PER = kMaxBH / kAttendThreads;   // 4 entries per thread
-        int nb[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) nb[i] = p.n_ctx[min(tid * PER + i, p.B - 1)];
         bool bad_n = false;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (tid * PER + i < p.B) {
-                // a context outside [1, max_ctx] breaks the contract: it is
-                // clamped to [0, max_ctx] (a sequence of 0 rows gets zeros and
-                // an empty set, written below) and latches error bit 16
-                int n = nb[i];
-                if (n < 1 || n > p.max_ctx) {
-                    bad_n = true;
-                    n = n < 0 ? 0 : (n > p.max_ctx ? p.max_ctx : n);
-                }
-                // min(k, n), or under the ratio rule min(k, ceil(theta n)) (at least one)
-                const double t = ceil(p.sel_ratio * (double)n);
-                const uint32_t kr = t < 1.0 ? 1u : (t > (double)n ? (uint32_t)n : (uint32_t)t);
-                s_nctx[tid * PER + i] = n;
-                s_ke[tid * PER + i] = min((uint32_t)min(p.k, n), kr);
+        for (int b = tid; b < p.B; b += kAttendThreads) {
+            // a context outside [1, max_ctx] breaks the contract: it is
+            // clamped to [0, max_ctx] (a sequence of 0 rows gets zeros and an
+            // empty set, written below) and latches error bit 16
+            int n = p.n_ctx[b];
+            if (n < 1 || n > p.max_ctx) {
+                bad_n = true;
+                n = n < 0 ? 0 : (n > p.max_ctx ? p.max_ctx : n);
             }
+            // min(k, n), or under the ratio rule min(k, ceil(theta n)) (at least one)
+            const double t = ceil(p.sel_ratio * (double)n);
+            const uint32_t kr = t < 1.0 ? 1u : (t > (double)n ? (uint32_t)n : (uint32_t)t);
+            s_nctx[b] = n;
+            s_ke[b] = min((uint32_t)min(p.k, n), kr);
         }
         if (bad_n && blockIdx.x == 0) atomicOr(p.ws.err, 16u);
         __syncthreads();
-        uint32_t u_[PER];
-        uint32_t tot = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int bg = tid * PER + i;
+        LYCHEE_STAMP(kTrPro0 + 0);
+        uint32_t run = 0;
+        for (int c0 = 0; c0 < BH; c0 += kAttendThreads) {   // (uniform loop)
+            const int bg = c0 + tid;
             uint32_t cost = 0;
             if (bg < BH) {
                 const int b = bg / p.Hkv, g = bg - b * p.Hkv;
@@ -643,19 +639,14 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 const bool retr = !HYBRID || ((p.role_bits >> g) & 1ull);
                 cost = retr ? kCostRetrieval * (uint32_t)n : p.cost_sparse * (uint32_t)min(p.k, n);
             }
-            u_[i] = cost;
-            tot += cost;
+            uint32_t tot;
+            const uint32_t ex = block_exclusive_scan(cost, s_wave, &tot);
+            if (bg < BH) s_pref[bg] = run + ex;
+            run += tot;
         }
-        uint32_t total;
-        uint32_t run = block_exclusive_scan(tot, s_wave, &total);
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int bg = tid * PER + i;
-            if (bg <= BH) s_pref[bg] = run;
-            run += u_[i];
-        }
-        if (tid == kAttendThreads - 1 && BH == kMaxBH) s_pref[kMaxBH] = run;
+        if (tid == 0) s_pref[BH] = run;
         __syncthreads();
+        LYCHEE_STAMP(kTrPro0 + 1);
     }
 
     const uint32_t U = s_pref[BH];
@@ -707,7 +698,10 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     // workgroup before it, which then spans heads (many small heads).  Every
     // workgroup tabulates all P+1 boundaries once, in parallel.
     for (int h = tid; h <= BH; h += kAttendThreads)
-        s_first[h] = U ? (uint32_t)(((unsigned long long)P * s_pref[h] + U / 2u) / U) : 0u;
+        // floor((P pref + floor(U/2)) / U) in fp64: the numerator (< 2^42) is
+        // exact and a quotient within 1/U of an integer stays apart from it
+        // after rounding, so the floor is exact (no 64-bit integer division)
+        s_first[h] = U ? (uint32_t)(((double)P * (double)s_pref[h] + (double)(U / 2u)) / (double)U) : 0u;
     __syncthreads();
     for (int ww = tid; ww <= P; ww += kAttendThreads) {
         uint32_t bnd;
@@ -725,11 +719,12 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             const uint32_t cwa = is_retr(a) ? kCostRetrieval : p.cost_sparse;
             const uint32_t rows = (h1 - h0) / cwa;
             const uint32_t i = (uint32_t)ww - s_first[a], nwh = s_first[a + 1] - s_first[a];   // nwh >= 1
-            bnd = h0 + cwa * (uint32_t)(((unsigned long long)i * rows) / nwh);
+            bnd = h0 + cwa * ((i * rows) / nwh);   // i * rows <= kMaxWG * kMaxCtx: 32-bit
         }
         s_bound[ww] = bnd;
     }
     __syncthreads();
+    LYCHEE_STAMP(kTrPro0 + 2);
     // Workgroups whose ranges hold cost positions c0 and c1: the number of
     // range starts s_bound[1..P-1] at or before each (the starts are
     // non-decreasing; an empty range shares its start with the next one, so
@@ -1324,7 +1319,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         crossing();
         uint32_t Td = s_res[0], c_above = s_res[1];
         const uint32_t nfail = list_failing(Td);
-        if (nfail) {
+        if (__builtin_expect(nfail != 0u, 0)) {
             // counts in [T, bound) of the workgroups whose bound lies above T
             for (uint32_t q = 0; q < nfail; ++q) {               // (uniform loop)
                 const int i = (int)s_coff[q];
@@ -1425,6 +1420,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     // all kFastPer loads in flight at once (straight-line code
                     // kept short: reads, loads, writes; rows past the batch
                     // load the head's first entry, unused)
+                    // (the keys of digit T flagged on the way: bit j of mm)
+                    uint32_t mm = 0;
                     {
                         uint32_t at[kFastPer];
 #pragma unroll
@@ -1435,25 +1432,16 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                             e[j] = coherent_load(&cand[kAttendThreads * j + tid < len ? at[j] : 0u]);
 #pragma unroll
                         for (int j = 0; j < kFastPer; ++j) {
-                            u.fr.key[kAttendThreads * j + tid] = (uint32_t)e[j];
+                            const uint32_t key = (uint32_t)e[j];
+                            u.fr.key[kAttendThreads * j + tid] = key;
                             u.fr.idx[kAttendThreads * j + tid] = (uint32_t)(e[j] >> 32);
+                            mm |= (uint32_t)(kAttendThreads * j + tid < len && key - klo <= khi - klo) << j;
                         }
                     }
                     LYCHEE_STAMP(kTrResolve0 + 10);
                     if (pass == 0) {
                         // keys of digit T (own entries only: no barrier needed
                         // before reading them back), placed by one block scan
-                        uint32_t mm = 0;
-#pragma unroll 1
-                        for (int j0 = 0; j0 < kFastPer; j0 += 8) {
-                            uint32_t kk[8];
-#pragma unroll
-                            for (int e2 = 0; e2 < 8; ++e2) kk[e2] = u.fr.key[kAttendThreads * (j0 + e2) + tid];
-#pragma unroll
-                            for (int e2 = 0; e2 < 8; ++e2)
-                                mm |= (uint32_t)(kAttendThreads * (j0 + e2) + tid < len && kk[e2] >= klo &&
-                                                 kk[e2] <= khi) << (j0 + e2);
-                        }
                         uint32_t gtot;
                         uint32_t q = s_ceq + block_exclusive_scan((uint32_t)__popc(mm), s_wave, &gtot);
                         while (mm) {
@@ -1470,51 +1458,48 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     LYCHEE_STAMP(kTrResolve0 + 8);
                 }
                 if (pass == 0) continue;
-                // winners of each (j, wavefront) step (lane j keeps step j's
-                // count), then their flat prefix
-                uint32_t mk = 0, cj = 0;
+                // One pass: wavefront v compacts the winners of its quarter
+                // of the batch (64 consecutive entries per step, ballot ranks,
+                // a running count) into its part of u.fr.map; the four counts
+                // then place the quarters, copied to S in order.
+                {
+                    constexpr uint32_t kQ = kFastBatch / kWaves;
+                    uint32_t* sbuf = u.fr.map + (uint32_t)wave * kQ;
+                    const uint32_t f0 = min((uint32_t)wave * kQ, len), f1 = min(f0 + kQ, len);
+                    uint32_t wcnt = 0;
 #pragma unroll 1
-                for (int j0 = 0; j0 < kFastPer; j0 += 8) {
-                    uint32_t kk[8], ii[8];
+                    for (uint32_t f = f0; f < f1; f += 64u * 8u) {
+                        uint32_t kk[8], ii[8];
 #pragma unroll
-                    for (int e2 = 0; e2 < 8; ++e2) {
-                        const uint32_t f = kAttendThreads * (j0 + e2) + tid;
-                        kk[e2] = u.fr.key[f];
-                        ii[e2] = u.fr.idx[f];
-                    }
+                        for (int e2 = 0; e2 < 8; ++e2) {
+                            const uint32_t fl = f + 64u * e2 + (uint32_t)lane;
+                            kk[e2] = u.fr.key[fl];
+                            ii[e2] = u.fr.idx[fl];
+                        }
 #pragma unroll
-                    for (int e2 = 0; e2 < 8; ++e2) {
-                        const uint32_t f = kAttendThreads * (j0 + e2) + tid;
-                        const bool wv = f < len && full_order(kk[e2], ii[e2]) >= cut;
-                        const uint32_t c = (uint32_t)__popcll(__ballot(wv));
-                        mk |= (uint32_t)wv << (j0 + e2);
-                        cj = lane == j0 + e2 ? c : cj;
+                        for (int e2 = 0; e2 < 8; ++e2) {
+                            const uint32_t fl = f + 64u * e2 + (uint32_t)lane;
+                            const bool wv = fl < f1 && full_order(kk[e2], ii[e2]) >= cut;
+                            const unsigned long long bw = __ballot(wv);
+                            if (wv) sbuf[wcnt + (uint32_t)__popcll(bw & lt_mask)] = ii[e2];
+                            wcnt += (uint32_t)__popcll(bw);
+                        }
                     }
+                    if (lane == 0) u.fr.jc[wave] = wcnt;
+                    __syncthreads();
+                    LYCHEE_STAMP(kTrResolve0 + 9);
+                    uint32_t base = 0, tot = 0;
+#pragma unroll
+                    for (int v = 0; v < kWaves; ++v) {
+                        const uint32_t c = u.fr.jc[v];
+                        base += v < wave ? c : 0u;
+                        tot += c;
+                    }
+                    for (uint32_t i = (uint32_t)lane; i < wcnt; i += 64u)
+                        srow[min(total + base + i, last)] = (int32_t)sbuf[i];
+                    total += tot;
+                    __syncthreads();
                 }
-                if (lane < kFastPer) u.fr.jc[lane * kWaves + wave] = cj;
-                __syncthreads();
-                LYCHEE_STAMP(kTrResolve0 + 9);
-                uint32_t tot;
-                const uint32_t pre = block_exclusive_scan(tid < kFastPer * kWaves ? u.fr.jc[tid] : 0u, s_wave, &tot);
-                if (tid < kFastPer * kWaves) u.fr.jc[tid] = pre;
-                __syncthreads();
-#pragma unroll 1
-                for (int j0 = 0; j0 < kFastPer; j0 += 8) {
-                    uint32_t base[8], ii[8];
-#pragma unroll
-                    for (int e2 = 0; e2 < 8; ++e2) {
-                        base[e2] = u.fr.jc[(j0 + e2) * kWaves + wave];
-                        ii[e2] = u.fr.idx[kAttendThreads * (j0 + e2) + tid];
-                    }
-#pragma unroll
-                    for (int e2 = 0; e2 < 8; ++e2) {
-                        const bool wv = (mk >> (j0 + e2)) & 1u;
-                        const unsigned long long bw = __ballot(wv);
-                        if (wv) srow[min(total + base[e2] + (uint32_t)__popcll(bw & lt_mask), last)] = (int32_t)ii[e2];
-                    }
-                }
-                total += tot;
-                __syncthreads();
             }
             if (pass == 1) break;
             LYCHEE_STAMP(kTrResolve0 + 3);
@@ -1533,21 +1518,31 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             } else if (r_left == g) {                              // all of digit T
                 cut = (unsigned long long)klo << 32;
             } else {
-                // rank every composite against all (at most kFastGroup / 256 = 4
-                // per thread), 8 composites read per round trip
-                for (uint32_t q0 = tid; q0 < g; q0 += kAttendThreads) {
+                // rank every value against all: lane l ranks values l, l + 64,
+                // .. and wavefront v counts over the v-th quarter of the
+                // values (8 read per round trip); the four partial counts
+                // meet in u.fr.map (free between the gathers)
+                uint32_t* rank = u.fr.map;
+                for (uint32_t q0 = tid; q0 < g; q0 += kAttendThreads) rank[q0] = 0u;
+                __syncthreads();
+                const uint32_t qs = (g + kWaves - 1u) / kWaves;
+                const uint32_t qa = min(g, (uint32_t)wave * qs), qb = min(g, qa + qs);
+                for (uint32_t q0 = (uint32_t)lane; q0 < g; q0 += 64u) {
                     const unsigned long long mine = u.fr.comp[q0];
-                    uint32_t above = 0, q = 0;
-                    for (; q + 8u <= g; q += 8u) {
+                    uint32_t above = 0, q = qa;
+                    for (; q + 8u <= qb; q += 8u) {
                         unsigned long long c8[8];
 #pragma unroll
                         for (int e2 = 0; e2 < 8; ++e2) c8[e2] = u.fr.comp[q + e2];
 #pragma unroll
                         for (int e2 = 0; e2 < 8; ++e2) above += c8[e2] > mine;
                     }
-                    for (; q < g; ++q) above += u.fr.comp[q] > mine;
-                    if (above == r_left - 1u) s_cut = mine;
+                    for (; q < qb; ++q) above += u.fr.comp[q] > mine;
+                    if (above) atomicAdd(&rank[q0], above);
                 }
+                __syncthreads();
+                for (uint32_t q0 = tid; q0 < g; q0 += kAttendThreads)
+                    if (rank[q0] == r_left - 1u) s_cut = u.fr.comp[q0];
                 __syncthreads();
                 cut = s_cut;
             }
@@ -1573,8 +1568,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     int pending = -1;
     bool helped = false;
     int next_bg = head_of(lo);
+    LYCHEE_STAMP(kTrPro0 + 3);
     for (;;) {
-        if (pending >= 0) {
+        if (__builtin_expect(pending >= 0, 0)) {   // (out of the way of the streaming path)
             const int X = pending;
             pending = -1;
             const int b = X / p.Hkv;
@@ -1585,7 +1581,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #ifdef LYCHEE_TRACE
             tr_flags |= 8u;
 #endif
-            if (fast_resolve(X, s_nctx[b], s_ke[b], h0, wf, wl - wf + 1)) {
+            if (__builtin_expect(fast_resolve(X, s_nctx[b], s_ke[b], h0, wf, wl - wf + 1), 0)) {
 #ifdef LYCHEE_TRACE
                 tr_flags |= 32u;
 #endif

@@ -26,7 +26,7 @@ constexpr int kLevel2Max = kMaxWG / kCombineFanIn + 2;
 // 7 and 9 (and against retrieval costs 3, 5, 6 and 8): a dearer sparse row
 // gives the sparse workgroups fewer rows and the retrieval workgroups more.
 constexpr uint32_t kCostRetrieval = 4;
-constexpr uint32_t kCostSparse = 8;
+constexpr uint32_t kCostSparse = 6;
 constexpr int kIdxChunk = 2048;       // sparse S positions staged in LDS per pass
 constexpr int kKeyCap = 4096;         // retrieval selection keys kept in LDS per pass
 
@@ -55,8 +55,10 @@ constexpr int kFastBatch = 8192;
 // head's arrivals before it withdraws and leaves the resolve to the last one.
 constexpr unsigned long long kHelperWaitTicks = 10000;
 constexpr int kFastPer = kFastBatch / kAttendThreads;   // entries per thread of a batch
+static_assert((kFastBatch / (kAttendThreads / 64)) % 512 == 0, "a wavefront's quarter of a batch is whole 8-step reads");
 constexpr int kFastGroup = 1024;
 static_assert(kMaxCtx <= (1 << 20), "a workgroup's candidate count fits 20 bits of its word");
+static_assert((unsigned long long)kMaxWG * kMaxCtx < (1ull << 32), "workgroup boundaries in 32-bit arithmetic");
 // Workgroups per retrieval head of the rule-selection kernel (Top-p and block
 // rules: each works on a slice of the head; the last to arrive cuts the set).
 constexpr int kRuleSplit = 16;
@@ -274,6 +276,7 @@ enum TraceSlot {
     kTrFlags,            // bit 0 retrieval head, 1 sparse head, 2 merger, 3 resolver, 4 helper
     kTrHeads,            // heads the range touched
     kTrResolve0 = 16,    // 16..27: phases inside the candidate resolver
+    kTrPro0 = 28,        // 28..31: phases inside the prologue
     kTraceSlots = 32
 };
 

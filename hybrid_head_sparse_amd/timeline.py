@@ -37,6 +37,8 @@ SLOTS = 32
 RES0 = 16               # resolver phase stamps: RES0 + 0..11
 RES_PHASES = ("hist+words", "crossing", "recount", "staged+group", "cut", "offsets", "emitted", "padded",
               "staged", "counted", "gathered")
+PRO0 = 28               # prologue phase stamps: PRO0 + 0..3
+PRO_PHASES = ("contexts", "cost prefix", "boundaries", "loop entry")
 TICK_US = 0.01          # s_memrealtime: 100 MHz
 
 
@@ -133,6 +135,16 @@ def report(tr, grid: int, roles, spans):
         "\n".join(kind_lines) + "\n"
     text += "\nCandidate resolver phases (median us from its start to the end of each phase):\n\n" + \
         resolver_table(tr, kinds)
+    pro = ["| " + " | ".join(PRO_PHASES) + " | prologue done |", "|" + "---|" * (len(PRO_PHASES) + 1)]
+    vals = [[] for _ in range(len(PRO_PHASES) + 1)]
+    for r in rows:
+        t = tr[r["layer"]].astype(np.int64)
+        live = t[:, ENTRY] > 0
+        for j, slot in enumerate([PRO0 + i for i in range(len(PRO_PHASES))] + [PROLOGUE]):
+            ok = live & (t[:, slot] > 0)
+            vals[j] += ((t[ok, slot] - t[ok, ENTRY]) * TICK_US).tolist()
+    pro.append("| " + " | ".join(f"{statistics.median(v):.2f}" if v else "-" for v in vals) + " |")
+    text += "\nPrologue phases (median us from each workgroup's entry, all layers):\n\n" + "\n".join(pro) + "\n"
     text += f"\nSum of layer spans {sum(r['exit'] for r in rows):.1f} us"
     if spans:
         text += f"; eager steps {', '.join(f'{s:.1f}' for s in spans)} us"
