@@ -1414,7 +1414,14 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                         const uint32_t ci = s_coff[i];
                         const uint32_t f0 = max(ci, b0), f1 = max(f0, min(s_coff[i + 1], b0 + len));
                         const uint32_t r = (max(s_bound[wf + i], h0) - h0) / kCostRetrieval + (f0 - ci);
-                        for (uint32_t f = f0; f < f1; ++f) u.fr.map[f - b0] = r + (f - f0);
+                        uint32_t f = f0;
+                        for (; f + 4u <= f1; f += 4u) {              // (four independent writes a step)
+                            u.fr.map[f - b0] = r + (f - f0);
+                            u.fr.map[f + 1u - b0] = r + (f + 1u - f0);
+                            u.fr.map[f + 2u - b0] = r + (f + 2u - f0);
+                            u.fr.map[f + 3u - b0] = r + (f + 3u - f0);
+                        }
+                        for (; f < f1; ++f) u.fr.map[f - b0] = r + (f - f0);
                     }
                     __syncthreads();
                     // all kFastPer loads in flight at once (straight-line code
@@ -1972,6 +1979,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     }
                     run_max = max(run_max, cmax);
                 }
+                LYCHEE_STAMP(kTrSStaged);
                 stream_range(c_lo, c_hi, u.st.idx);
             }
             LYCHEE_STAMP(kTrStreamEnd);

@@ -275,7 +275,8 @@ enum TraceSlot {
     kTrExit,             // last instruction
     kTrFlags,            // bit 0 retrieval head, 1 sparse head, 2 merger, 3 resolver, 4 helper
     kTrHeads,            // heads the range touched
-    kTrResolve0 = 16,    // 16..27: phases inside the candidate resolver
+    kTrResolve0 = 16,    // 16..26: phases inside the candidate resolver
+    kTrSStaged = 27,     // a sparse head's S entries staged (the gather starts)
     kTrPro0 = 28,        // 28..31: phases inside the prologue
     kTraceSlots = 32
 };

@@ -87,6 +87,28 @@ def _kernel_stats(d: str) -> list[dict]:
         return list(csv.DictReader(f))
 
 
+def write_stats(trace: str, wl: str, cmds: str) -> None:
+    """profiles/attend_<wl>_kernel_stats.md from a --kernel-trace --stats run."""
+    rows = []
+    for r in _kernel_stats(trace):
+        name = r.get("Name") or r.get("KERNEL_NAME") or ""
+        if not any(k in name for k in ("attend_kernel", "rule", "correction", "merge")):
+            continue
+        rows.append((name, int(r["Calls"]), float(r["TotalDurationNs"]), float(r["AverageNs"]),
+                     float(r["MinNs"]), float(r["MaxNs"])))
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"attend_{wl}_kernel_stats.md"), "w") as f:
+        f.write(f"# rocprofv3 kernel statistics: attention kernels, {wl}\n\n")
+        f.write("Commands (from the repository root on one MI355X):\n\n```\n" + cmds + "\n```\n\n")
+        f.write("| kernel | calls | total ms | average us | min us | max us |\n|---|---|---|---|---|---|\n")
+        for name, calls, tot, avg, mn, mx in rows:
+            f.write(f"| `{name}` | {calls} | {tot / 1e6:.3f} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |\n")
+        f.write("\nThe hybrid kernel (`..., true>`) runs every layer of the step (layer 0 all retrieval, the\n"
+                "others mixed) in the eager, graph and event-timed passes of the benchmark; the dense kernel\n"
+                "(`..., false>`) is the all-retrieval comparison.  The hybrid average over a step's layers is\n"
+                "what the benchmark reports as `roofline.avg_launch_us` (its step time over the layers).\n")
+
+
 def summarize(a) -> None:
     is_copy = lambda name: ("copy" in name.lower() or "elementwise" in name.lower()) and "attend" not in name
     is_hyb = lambda name: HYBRID_KERNEL in name
@@ -100,28 +122,10 @@ def summarize(a) -> None:
     write = _counter_per_dispatch(a.write, "WRITE_SIZE", is_hyb)
     fetch_b = statistics.mean(fetch) * 1024.0 * f_scale
     write_b = statistics.mean(write) * 1024.0 * w_scale
-    stats = _kernel_stats(a.trace)
     cmds = open(a.commands).read().strip()
     sha = kernel_code_digest()
     wl = a.workload
-
-    rows = []
-    for r in stats:
-        name = r.get("Name") or r.get("KERNEL_NAME") or ""
-        if "attend_kernel" not in name:
-            continue
-        rows.append((name, int(r["Calls"]), float(r["TotalDurationNs"]), float(r["AverageNs"]),
-                     float(r["MinNs"]), float(r["MaxNs"])))
-    os.makedirs(PROFILES, exist_ok=True)
-    with open(os.path.join(PROFILES, f"attend_{wl}_kernel_stats.md"), "w") as f:
-        f.write(f"# rocprofv3 kernel statistics: attention kernels, {wl}\n\n")
-        f.write("Commands (from the repository root on one MI355X):\n\n```\n" + cmds + "\n```\n\n")
-        f.write("| kernel | calls | total ms | average us | min us | max us |\n|---|---|---|---|---|---|\n")
-        for name, calls, tot, avg, mn, mx in rows:
-            f.write(f"| `{name}` | {calls} | {tot / 1e6:.3f} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |\n")
-        f.write("\nThe hybrid kernel's calls cover every layer of the step (one all-retrieval layer 0 and the\n"
-                "mixed layers) in the eager, graph and event-timed passes of the benchmark; its average is\n"
-                "comparable with the benchmark's `roofline.avg_launch_us`.\n")
+    write_stats(a.trace, wl, cmds)
     res = {
         "workload": wl,
         "kernel": HYBRID_KERNEL,
@@ -160,9 +164,15 @@ def main(argv=None) -> None:
     for k in ("trace", "fetch", "write", "copy_fetch", "copy_write", "commands"):
         s.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     s.add_argument("--copy-mib", type=int, default=1024)
+    t = sub.add_parser("stats")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--trace", required=True)
+    t.add_argument("--commands", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         run_copy(a.mib)
+    elif a.cmd == "stats":
+        write_stats(a.trace, a.workload, open(a.commands).read().strip())
     else:
         summarize(a)
 

@@ -34,10 +34,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SLOTS = 32
 (ENTRY, PROLOGUE, HEAD, STREAM, SELARR, RECORD, ARRIVE, MERGED, RSTART, REND, EXIT, FLAGS, HEADS) = range(13)
-RES0 = 16               # resolver phase stamps: RES0 + 0..11
+RES0 = 16               # resolver phase stamps: RES0 + 0..10
 RES_PHASES = ("hist+words", "crossing", "recount", "staged+group", "cut", "offsets", "emitted", "padded",
-              "staged", "counted", "gathered")
+              "staged", "compacted", "gathered")
 PRO0 = 28               # prologue phase stamps: PRO0 + 0..3
+SSTAGED = 27            # a sparse head's S entries staged
 PRO_PHASES = ("contexts", "cost prefix", "boundaries", "loop entry")
 TICK_US = 0.01          # s_memrealtime: 100 MHz
 
@@ -135,6 +136,18 @@ def report(tr, grid: int, roles, spans):
         "\n".join(kind_lines) + "\n"
     text += "\nCandidate resolver phases (median us from its start to the end of each phase):\n\n" + \
         resolver_table(tr, kinds)
+    sp = ["| retrieval heads | head start | S staged | stream end |", "|---|---|---|---|"]
+    for R in sorted(kinds):
+        hs, st, se = [], [], []
+        for r in kinds[R]:
+            t = tr[r["layer"]].astype(np.int64)
+            ok = (t[:, ENTRY] > 0) & (t[:, SSTAGED] > 0) & ((t[:, FLAGS] & 3) == 2)
+            hs += ((t[ok, HEAD] - t[ok, ENTRY]) * TICK_US).tolist()
+            st += ((t[ok, SSTAGED] - t[ok, ENTRY]) * TICK_US).tolist()
+            se += ((t[ok, STREAM] - t[ok, ENTRY]) * TICK_US).tolist()
+        if st:
+            sp.append(f"| {R} | {statistics.median(hs):.2f} | {statistics.median(st):.2f} | {statistics.median(se):.2f} |")
+    text += "\nGathered-rows workgroups (median us from entry):\n\n" + "\n".join(sp) + "\n"
     pro = ["| " + " | ".join(PRO_PHASES) + " | prologue done |", "|" + "---|" * (len(PRO_PHASES) + 1)]
     vals = [[] for _ in range(len(PRO_PHASES) + 1)]
     for r in rows:

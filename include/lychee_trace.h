@@ -26,8 +26,9 @@ extern "C" {
  * flags (1 retrieval head, 2 sparse head, 4 merger, 8 resolver as last
  * arrival, 32 full-scan resolve), word 12 the heads the range touched,
  * words 13-15 the candidate resolver's sizes (units | T << 32, threshold
- * group | count above T << 32, k_eff | workgroups << 32) and words 16-27
- * stamps of its phases (read by hybrid_head_sparse_amd/timeline.py).  The buffer must hold (launch + 1) * grid * 256
+ * group | count above T << 32, k_eff | workgroups << 32), words 16-26
+ * stamps of its phases, word 27 a sparse head's S entries staged and words
+ * 28-31 phases of the prologue (read by hybrid_head_sparse_amd/timeline.py).  The buffer must hold (launch + 1) * grid * 256
  * bytes. */
 lychee_status lychee_set_trace(lychee_handle* h, void* buffer, uint32_t launch);
 
