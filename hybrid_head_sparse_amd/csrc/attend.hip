@@ -748,7 +748,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     // inside that head).  The pairing follows from the boundaries alone, so
     // every workgroup derives the same one (wavefront-parallel ballots).
     auto helper_cand = [&](int a) -> bool { return a < BH && !is_retr(a) && s_first[a + 1] >= s_first[a] + 2u; };
-    auto needs_help = [&](int a) -> bool { return a < BH && is_retr(a) && s_pref[a + 1] > s_pref[a]; };
+    auto has_rows = [&](int a) -> bool { return a < BH && s_pref[a + 1] > s_pref[a]; };
+    auto needs_help = [&](int a) -> bool { return has_rows(a) && is_retr(a); };
     auto kth_bit = [](unsigned long long m, int k) -> int {   // position of the k-th set bit (k from 0)
         for (int t = 0; t < k; ++t) m &= m - 1ull;
         return __ffsll((long long)m) - 1;
@@ -759,7 +760,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             const int i = base + lane;
             r += __popcll(__ballot(i < X && needs_help(i)));
         }
-        for (int base = 0, seen = 0; base < BH; base += 64) {
+        int seen = 0;
+        for (int base = 0; base < BH; base += 64) {
             const unsigned long long m = __ballot(helper_cand(base + lane));
             const int c = __popcll(m);
             if (seen + c > r) return (int)s_first[base + kth_bit(m, r - seen)];
@@ -768,8 +770,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         return -1;
     };
     auto helped_by = [&](int ww) -> int {      // the head workgroup ww helps, or -1
-        int r = -1;
-        for (int base = 0, seen = 0; base < BH; base += 64) {
+        int r = -1, seen = 0;
+        for (int base = 0; base < BH; base += 64) {
             const int i = base + lane;
             const bool c = helper_cand(i);
             const unsigned long long m = __ballot(c);
@@ -1409,19 +1411,25 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             for (uint32_t bb = 0; bb < nbatch; ++bb) {
                 const uint32_t b0 = bb * (uint32_t)kFastBatch, len = min((uint32_t)kFastBatch, C - b0);
                 if (pass == 0 || nbatch > 1u) {
-                    // source row of every entry: thread t writes workgroup t's run
-                    for (int i = tid; i < nw; i += kAttendThreads) {
-                        const uint32_t ci = s_coff[i];
-                        const uint32_t f0 = max(ci, b0), f1 = max(f0, min(s_coff[i + 1], b0 + len));
-                        const uint32_t r = (max(s_bound[wf + i], h0) - h0) / kCostRetrieval + (f0 - ci);
-                        uint32_t f = f0;
-                        for (; f + 4u <= f1; f += 4u) {              // (four independent writes a step)
-                            u.fr.map[f - b0] = r + (f - f0);
-                            u.fr.map[f + 1u - b0] = r + (f + 1u - f0);
-                            u.fr.map[f + 2u - b0] = r + (f + 2u - f0);
-                            u.fr.map[f + 3u - b0] = r + (f + 3u - f0);
+                    // source row of every entry: tpp threads write each
+                    // workgroup's run (more threads per run when there are
+                    // fewer runs), four entries a step each
+                    {
+                        const int tpp = nw >= kAttendThreads / 2 ? 1 : (nw >= kAttendThreads / 4 ? 2 : (nw >= kAttendThreads / 8 ? 4 : 8));
+                        const int sub = tid & (tpp - 1);
+                        for (int i = tid / tpp; i < nw; i += kAttendThreads / tpp) {
+                            const uint32_t ci = s_coff[i];
+                            const uint32_t f0 = max(ci, b0), f1 = max(f0, min(s_coff[i + 1], b0 + len));
+                            const uint32_t r = (max(s_bound[wf + i], h0) - h0) / kCostRetrieval + (f0 - ci);
+                            uint32_t f = f0 + (uint32_t)sub;
+                            for (; f + 3u * (uint32_t)tpp < f1; f += 4u * (uint32_t)tpp) {
+                                u.fr.map[f - b0] = r + (f - f0);
+                                u.fr.map[f + (uint32_t)tpp - b0] = r + (f + (uint32_t)tpp - f0);
+                                u.fr.map[f + 2u * (uint32_t)tpp - b0] = r + (f + 2u * (uint32_t)tpp - f0);
+                                u.fr.map[f + 3u * (uint32_t)tpp - b0] = r + (f + 3u * (uint32_t)tpp - f0);
+                            }
+                            for (; f < f1; f += (uint32_t)tpp) u.fr.map[f - b0] = r + (f - f0);
                         }
-                        for (; f < f1; ++f) u.fr.map[f - b0] = r + (f - f0);
                     }
                     __syncthreads();
                     // all kFastPer loads in flight at once (straight-line code
@@ -1594,9 +1602,13 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #endif
                 resolve_topk(X, s_nctx[b], s_ke[b], 0u, 0u, (uint32_t)kResolveSlices, true);
             }
-            // the hand-off word back to idle for the next launch (both
-            // parties are done with it)
-            if (tid == 0 && coherent_load(&p.ws.hready[X]) != 0u) coherent_store(&p.ws.hready[X], 0u);
+            // the hand-off word back to idle for the next launch where this
+            // workgroup is the last party to touch it (1: it is the helper;
+            // 5: the helper withdrew; 4 is restored by the helper)
+            if (tid == 0) {
+                const uint32_t v = coherent_load(&p.ws.hready[X]);
+                if (v == 1u || v == 5u) coherent_store(&p.ws.hready[X], 0u);
+            }
             LYCHEE_STAMP(kTrResolveEnd);
             __syncthreads();
         }
@@ -1609,16 +1621,23 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 const int X = helped_by(w);
                 if (X >= 0) {
                     if (tid == 0) {
-                        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-                        uint32_t v;
-                        for (;;) {
-                            v = coherent_load(&p.ws.hready[X]);
-                            if (v == 1u) break;
-                            if (__builtin_amdgcn_s_memrealtime() - t0 > kHelperWaitTicks) {
-                                v = counter_cas(&p.ws.hready[X], 0u, 2u);   // withdraw, unless handed over meanwhile
-                                break;
+                        // waiting (0 -> 3; 1 if already handed over, 6 offered:
+                        // take it, 4 taken by the last arrival)
+                        uint32_t v = counter_cas(&p.ws.hready[X], 0u, 3u);
+                        if (v == 6u) v = counter_cas(&p.ws.hready[X], 6u, 1u) == 6u ? 1u : 4u;
+                        if (v == 4u) {
+                            coherent_store(&p.ws.hready[X], 0u);               // the last arrival resolves
+                        } else if (v != 1u) {
+                            const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+                            for (;;) {
+                                v = coherent_load(&p.ws.hready[X]);
+                                if (v == 1u) break;
+                                if (__builtin_amdgcn_s_memrealtime() - t0 > kHelperWaitTicks) {
+                                    v = counter_cas(&p.ws.hready[X], 3u, 5u) == 3u ? 5u : 1u;   // withdraw, unless
+                                    break;                                                      // handed over meanwhile
+                                }
+                                __builtin_amdgcn_s_sleep(2);
                             }
-                            __builtin_amdgcn_s_sleep(2);
                         }
                         s_flag[0] = v == 1u;
                     }
@@ -1906,12 +1925,16 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // Selection arrival, before the record: this workgroup's word (its
             // candidates and largest bound) and, once every store above is
             // complete, one count on the head's arrival counter.  The last
-            // arrival hands the resolve to the head's helper (hready 0 -> 1;
-            // the helper polls it) or, with no helper or one that withdrew
-            // (hready 2), resolves the head's top-k itself after its record
-            // and merges.
-            const int hw = p.sel_keys_only ? -1 : helper_of(bg);
+            // arrival hands the resolve to the head's helper if the helper is
+            // already waiting (hready 3 -> 1); otherwise it offers it (0 -> 6)
+            // and, after its record and merges, takes it back unless the
+            // helper took it meanwhile (6 -> 4 against the helper's 6 -> 1).
+            // States of hready: 0 idle, 3 helper waiting, 6 offered, 1 the
+            // helper's (it restores 0 after the resolve), 4 the last arrival's
+            // (the helper restores 0 when it comes), 5 helper withdrew (the
+            // last arrival resolves and restores 0).
             if (tid == 0 && !p.sel_keys_only) coherent_store(&p.ws.wmeta[w + bg], w_count | (w_bound << 20));
+            const int hw = p.sel_keys_only ? -1 : helper_of(bg);   // (while the stores travel)
             wait_stores_complete();
             __syncthreads();
             if (tid == 0) {
@@ -1921,7 +1944,20 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     last = before + 1u == (uint32_t)nw;
                     if (last) {
                         counter_reset64(&p.ws.selctr[bg]);
-                        if (hw >= 0 && counter_cas(&p.ws.hready[bg], 0u, 1u) == 0u) last = 0;   // the helper's
+                        if (hw >= 0) {
+                            // 3 -> 1 if the helper waits, else 0 -> 6; at most three
+                            // rounds (the helper moves 0 -> 3 once and 3 -> 5 once)
+                            uint32_t expect = 3u;
+                            for (int round = 0; round < 4; ++round) {
+                                const uint32_t v = counter_cas(&p.ws.hready[bg], expect, expect == 3u ? 1u : 6u);
+                                if (v == expect) {
+                                    last = expect == 3u ? 0u : 2u;   // handed over / offered
+                                    break;
+                                }
+                                if (v == 5u) break;         // the helper withdrew: resolve here
+                                expect = v;                 // 0 or 3: try that
+                            }
+                        }
                     }
                 }
                 s_sel[0] = last;
@@ -2088,6 +2124,11 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #endif
         }
         if (sel_role == 1u) pending = bg;   // the head's last selection arrival resolves its top-k
+        if (sel_role == 2u) {               // offered to the helper: take it back unless taken
+            if (tid == 0) s_flag[1] = counter_cas(&p.ws.hready[bg], 6u, 4u) == 6u;
+            __syncthreads();
+            if (s_flag[1]) pending = bg;
+        }
 
         __syncthreads();
     }
