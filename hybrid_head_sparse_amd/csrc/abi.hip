@@ -287,7 +287,11 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
     ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
     const int G = d.n_q_heads / d.n_kv_heads;
     ap.sel_ratio = rule == LYCHEE_SELECT_RATIO ? param : 1.0;
-    ap.sel_keys_only = hybrid && rule == LYCHEE_SELECT_BLOCK ? 1u : 0u;
+    ap.sel_block = 0u;
+    if (hybrid && rule == LYCHEE_SELECT_BLOCK)
+        while ((1 << ap.sel_block) < (int)param) ++ap.sel_block;          // param: 16 .. 256, a power of two
+    ap.sel_zpart = hybrid && rule == LYCHEE_SELECT_TOPP ? 1u : 0u;
+    ap.bkey_stride = block_key_stride(d.max_ctx);
     // The kernel's selection key is the fp32 sum of the G query heads' raw
     // dot products, i.e. G sqrt(d) times the pooled score: tau maps there.
     ap.trace = h->trace;
@@ -307,8 +311,10 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
         tp.S = S_out;
         tp.score = h->ws.score;
         tp.comp = h->ws.cand;
-        tp.rec = h->ws.prec;
-        tp.ctr = h->ws.pctr;
+        tp.bkey = h->ws.bkey;
+        tp.zpart = h->ws.zpart;
+        tp.bkey_stride = block_key_stride(d.max_ctx);
+        tp.nslots = attend_grid(h->cus, h->per_cu) + d.batch * d.n_kv_heads;
         tp.n_ctx = n_ctx;
         tp.err = h->ws.err;
         tp.role_bits = bits;

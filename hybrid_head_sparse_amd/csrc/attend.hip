@@ -593,6 +593,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     __shared__ int s_rel;
     __shared__ uint32_t s_ceq;        // resolver: threshold-digit composites appended so far
     __shared__ unsigned long long s_cut;   // resolver: the smallest winning full_order of the threshold digit
+    __shared__ uint32_t s_zk[kWaves];      // Top-p normaliser: per-wavefront largest key, then sum
+    __shared__ double s_zd[kWaves];
 
 #ifdef LYCHEE_TRACE
     unsigned long long* const tr_row =
@@ -1616,7 +1618,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // range done: the helper duty, if any (a bounded wait for the
             // head's last arrival; on time-out the helper withdraws and the
             // last arrival resolves)
-            if (HYBRID && !helped && !p.sel_keys_only) {
+            if (HYBRID && !helped && !p.sel_block) {
                 helped = true;
                 const int X = helped_by(w);
                 if (X >= 0) {
@@ -1830,6 +1832,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             uint32_t* sc = p.ws.score + (size_t)bg * p.max_ctx;
             uint32_t* gh = p.ws.hist + (size_t)bg * kHistBins;
             uint32_t w_count = 0, w_bound = 0;   // candidates appended, largest pass bound
+            float zm = -INFINITY;                // Top-p: largest pooled sum of the range so far
+            double zs = 0.0;                     // and the sum of 2^((f - zm) c) over it
             for (int i = tid; i < kHistBins; i += kAttendThreads) u.st.hist[i] = 0u;
             // equal passes of at most kKeyCap rows (no short tail pass)
             const uint32_t npass = (seg_hi - seg_lo + kKeyCap - 1) / kKeyCap;
@@ -1842,13 +1846,96 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 stream_range(c_lo, c_hi, nullptr);
                 __syncthreads();
                 LYCHEE_STAMP(kTrStreamEnd);
-                // every key to the score buffer (read only if the bound below fails,
-                // or by the rule-selection kernel)
-                for (uint32_t i = tid; i < len; i += kAttendThreads) coherent_store(&sc[c_lo + i], u.st.keys[i]);
-                if (p.sel_keys_only) {     // a later kernel selects from the keys alone
+                if (p.sel_block) {
+                    // The block rule: the largest key of each block of the pass
+                    // (blocks of 2^sel_block >= 16 tokens, numbered from token
+                    // 0), folded into the head's block words by atomic max.
+                    // Thread t takes positions 16t .. 16t + 15, so at most two
+                    // blocks; a block split between threads, passes or
+                    // workgroups gets one atomic from each part.  No top-k:
+                    // the rule-selection kernel reads the block words.
+                    const uint32_t i0 = 16u * (uint32_t)tid;
+                    if (i0 < len) {
+                        uint32_t* bk = p.ws.bkey + (size_t)bg * (size_t)p.bkey_stride;
+                        const uint4* k4 = reinterpret_cast<const uint4*>(u.st.keys + i0);
+                        uint32_t blk = (c_lo + i0) >> p.sel_block, bmx = 0u;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const uint4 v = k4[c];
+                            const uint32_t kv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const uint32_t i = i0 + 4u * (uint32_t)c + (uint32_t)e;
+                                if (i < len) {
+                                    const uint32_t bi = (c_lo + i) >> p.sel_block;
+                                    if (bi != blk) {
+                                        atomicMax(&bk[blk], bmx);
+                                        blk = bi;
+                                        bmx = 0u;
+                                    }
+                                    bmx = max(bmx, kv[e]);
+                                }
+                            }
+                        }
+                        atomicMax(&bk[blk], bmx);
+                    }
                     for (int i = tid; i < kHistBins; i += kAttendThreads) u.st.hist[i] = 0u;
                     __syncthreads();
                     continue;
+                }
+                // every key to the score buffer (read only if the bound below fails,
+                // or by the rule-selection kernel)
+                for (uint32_t i = tid; i < len; i += kAttendThreads) coherent_store(&sc[c_lo + i], u.st.keys[i]);
+                if (p.sel_zpart) {
+                    // The Top-p rule: this pass's part of the normaliser, with
+                    // f the pooled sum a key encodes and c = scale_log2 / G:
+                    // m = the pass's largest f, z = sum of 2^((f - m) c) (fp32
+                    // terms, fp32 per thread, double across threads in a
+                    // fixed order), merged into the range's running pair.
+                    const uint32_t i0 = 16u * (uint32_t)tid;
+                    uint32_t kv[16];
+                    uint32_t kmax = 0u;
+                    {
+                        const uint4* k4 = reinterpret_cast<const uint4*>(u.st.keys + i0);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const uint4 v = k4[c];
+                            kv[4 * c + 0] = v.x; kv[4 * c + 1] = v.y; kv[4 * c + 2] = v.z; kv[4 * c + 3] = v.w;
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        kv[e] = i0 + (uint32_t)e < len ? kv[e] : 0u;      // 0: below every key
+                        kmax = max(kmax, kv[e]);
+                    }
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+                    if (lane == 0) s_zk[wave] = kmax;
+                    __syncthreads();
+                    kmax = s_zk[0];
+#pragma unroll
+                    for (int wv = 1; wv < kWaves; ++wv) kmax = max(kmax, s_zk[wv]);
+                    const float c = p.scale_log2 * (1.0f / (float)G);
+                    const float mp = key_float(kmax);
+                    float zt = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) zt += kv[e] ? exp2f((key_float(kv[e]) - mp) * c) : 0.0f;
+                    double zd = (double)zt;
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) zd += __shfl_xor(zd, o);
+                    if (lane == 0) s_zd[wave] = zd;
+                    __syncthreads();
+                    double zp = s_zd[0];
+#pragma unroll
+                    for (int wv = 1; wv < kWaves; ++wv) zp += s_zd[wv];
+                    if (zm == -INFINITY) {
+                        zm = mp;
+                        zs = zp;
+                    } else {
+                        const float M = fmaxf(zm, mp);
+                        zs = zs * (double)exp2f((zm - M) * c) + zp * (double)exp2f((mp - M) * c);
+                        zm = M;
+                    }
                 }
                 // this pass's bound: its own crossing at its share s of k_eff plus
                 // a margin, the smaller of kSelMargin - 1 shares and 4 standard
@@ -1933,13 +2020,18 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // helper's (it restores 0 after the resolve), 4 the last arrival's
             // (the helper restores 0 when it comes), 5 helper withdrew (the
             // last arrival resolves and restores 0).
-            if (tid == 0 && !p.sel_keys_only) coherent_store(&p.ws.wmeta[w + bg], w_count | (w_bound << 20));
-            const int hw = p.sel_keys_only ? -1 : helper_of(bg);   // (while the stores travel)
+            if (tid == 0 && p.sel_zpart && zm != -INFINITY) {   // the range's normaliser part (next kernel)
+                const unsigned long long zb = __builtin_bit_cast(unsigned long long, zs);
+                *reinterpret_cast<uint4*>(p.ws.zpart + 4 * (size_t)(w + bg)) =
+                    make_uint4((uint32_t)bg + 1u, __builtin_bit_cast(uint32_t, zm), (uint32_t)zb, (uint32_t)(zb >> 32));
+            }
+            if (tid == 0 && !p.sel_block) coherent_store(&p.ws.wmeta[w + bg], w_count | (w_bound << 20));
+            const int hw = p.sel_block ? -1 : helper_of(bg);   // (while the stores travel)
             wait_stores_complete();
             __syncthreads();
             if (tid == 0) {
                 uint32_t last = 0;
-                if (!p.sel_keys_only) {
+                if (!p.sel_block) {
                     const uint32_t before = (uint32_t)counter_add64(&p.ws.selctr[bg], 1ull);
                     last = before + 1u == (uint32_t)nw;
                     if (last) {
@@ -2142,9 +2234,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 
 template <typename T, int D, int G, bool HYBRID>
 hipError_t launch_one(const AttendParams& p, int cus, int per_cu, hipStream_t stream) {
-    int grid = cus * per_cu;
-    if (grid > kMaxWG) grid = kMaxWG;
-    if (grid < 1) grid = 1;
+    const int grid = attend_grid(cus, per_cu);
     hipLaunchKernelGGL((attend_kernel<T, D, G, HYBRID>), dim3(grid), dim3(kAttendThreads), 0, stream, p);
     return hipGetLastError();
 }

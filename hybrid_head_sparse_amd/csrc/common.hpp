@@ -59,9 +59,9 @@ static_assert((kFastBatch / (kAttendThreads / 64)) % 512 == 0, "a wavefront's qu
 constexpr int kFastGroup = 1024;
 static_assert(kMaxCtx <= (1 << 20), "a workgroup's candidate count fits 20 bits of its word");
 static_assert((unsigned long long)kMaxWG * kMaxCtx < (1ull << 32), "workgroup boundaries in 32-bit arithmetic");
-// Workgroups per retrieval head of the rule-selection kernel (Top-p and block
-// rules: each works on a slice of the head; the last to arrive cuts the set).
-constexpr int kRuleSplit = 16;
+// Top-p normaliser partials of one attention launch: one slot per (workgroup
+// w, head bg) pair at w + bg.
+constexpr int kZSlots = kMaxWG + kMaxBH;
 
 // Cross-workgroup hand-off without cache-wide maintenance.  Data one
 // workgroup leaves for another inside the same launch is written with
@@ -129,6 +129,11 @@ __host__ __device__ inline uint32_t float_key(float f) {
     if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// Inverse of float_key.
+__host__ __device__ inline float key_float(uint32_t key) {
+    const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+    return __builtin_bit_cast(float, u);
+}
 
 // ---------------------------------------------------------------- workspace
 struct Workspace {
@@ -141,7 +146,6 @@ struct Workspace {
     uint32_t* score;             // [BH * max_ctx]            every selection key of a retrieval head
                                  //                           (read when a head's bounds fail, and by
                                  //                           the rule-selection kernel)
-    unsigned long long* prec;    // [BH * kRuleSplit * 4]     rule selection: per-slice partials
     float* crec_ml;              // [CW * 32 G * 2]           correction attention: chunk partials
     float* crec_o;               // [CW * 32 G * D]           (CW = max(512, BH) workgroups)
     // ---- zero-initialised region (restored to zero by every call) ----
@@ -152,7 +156,13 @@ struct Workspace {
     uint32_t* rdone;             // [BH]                      slices whose resolver has read the head's
                                  //                           histogram and counters
     uint32_t* hist;              // [BH * kHistBins]          first-digit counts from each pass's bound up
-    uint32_t* pctr;              // [BH]                      rule selection: slices done
+    uint32_t* bkey;              // [BH * ceil(max_ctx / 16)] block rule: the largest selection key of
+                                 //                           each block (atomic max; read and restored to
+                                 //                           zero by the rule-selection kernel)
+    uint32_t* zpart;             // [(kMaxWG + BH) * 4]       Top-p: per (workgroup w, head bg) at w + bg:
+                                 //                           bg + 1 (0 = empty), the largest pooled sum m
+                                 //                           and the sum of 2^((f - m) c) as a double
+                                 //                           (tags restored to 0 by the rule kernel)
     uint32_t* hready;            // [BH]                      helper hand-off of a retrieval head's
                                  //                           resolve: 1 arrivals complete (the helper
                                  //                           resolves), 2 the helper withdrew
@@ -161,6 +171,9 @@ struct Workspace {
     size_t zero_bytes;
     size_t total_bytes;
 };
+
+// Block words per head of the block rule: one per 16 tokens (the smallest block).
+inline int block_key_stride(int max_ctx) { return (max_ctx + 15) / 16; }
 
 // Record = m[G], l[G], o[G][D] (floats): running max (log2 domain), sum of
 // weights, unnormalised weighted value sum.
@@ -190,7 +203,8 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_bmax = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_rdone = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_hist = take(sizeof(uint32_t) * (size_t)BH * kHistBins);
-    size_t o_pctr = take(sizeof(uint32_t) * (size_t)BH);
+    size_t o_bkey = take(sizeof(uint32_t) * (size_t)BH * (size_t)block_key_stride(max_ctx));
+    size_t o_zpart = take(sizeof(uint32_t) * 4 * (size_t)(kMaxWG + BH));
     size_t o_hready = take(sizeof(uint32_t) * (size_t)BH);
     size_t o_err = take(sizeof(uint32_t) * 4);
     const size_t z1 = off;
@@ -199,7 +213,6 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
     size_t o_cand = take(sizeof(unsigned long long) * (size_t)BH * max_ctx);
     size_t o_wmeta = take(sizeof(uint32_t) * (size_t)(kMaxWG + BH));
     size_t o_score = take(sizeof(uint32_t) * (size_t)BH * max_ctx);
-    size_t o_prec = take(sizeof(unsigned long long) * (size_t)BH * kRuleSplit * 4);
     const size_t CW = (size_t)(BH > 512 ? BH : 512);
     size_t o_crml = with_correction ? take(sizeof(float) * CW * 32 * G * 2) : 0;
     size_t o_cro = with_correction ? take(sizeof(float) * CW * 32 * G * D) : 0;
@@ -213,7 +226,6 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.cand = (unsigned long long*)(p + o_cand);
         w.wmeta = (uint32_t*)(p + o_wmeta);
         w.score = (uint32_t*)(p + o_score);
-        w.prec = (unsigned long long*)(p + o_prec);
         w.crec_ml = with_correction ? (float*)(p + o_crml) : nullptr;
         w.crec_o = with_correction ? (float*)(p + o_cro) : nullptr;
         w.cnt1 = (uint32_t*)(p + o_cnt1);
@@ -222,7 +234,8 @@ inline Workspace carve_workspace(void* base, int B, int Hq, int Hkv, int D, int 
         w.bmax = (uint32_t*)(p + o_bmax);
         w.rdone = (uint32_t*)(p + o_rdone);
         w.hist = (uint32_t*)(p + o_hist);
-        w.pctr = (uint32_t*)(p + o_pctr);
+        w.bkey = (uint32_t*)(p + o_bkey);
+        w.zpart = (uint32_t*)(p + o_zpart);
         w.hready = (uint32_t*)(p + o_hready);
         w.err = (uint32_t*)(p + o_err);
         w.zero_begin = p + z0;
@@ -249,9 +262,14 @@ struct AttendParams {
     // kept.  S is padded with -1.
     double sel_ratio;
     uint32_t sel_tkey;
-    // Retrieval heads only write every token's key to the score buffer and
-    // leave S to a later kernel (the block rule): no top-k.
-    uint32_t sel_keys_only;
+    // Block rule (sel_block = log2 of the block size, 0 otherwise): retrieval
+    // heads fold each block's largest selection key into ws.bkey and leave S
+    // to the rule-selection kernel (no top-k, no score buffer).
+    uint32_t sel_block;
+    // Top-p rule: retrieval heads also publish their part of the normaliser
+    // (ws.zpart) for the rule-selection kernel.
+    uint32_t sel_zpart;
+    int32_t bkey_stride;    // block words per head in ws.bkey
     // Phase timestamps (the LYCHEE_TRACE build only; null otherwise):
     // kTraceSlots 64-bit words per workgroup and launch, at
     // (trace_launch * gridDim.x + blockIdx.x) * kTraceSlots.
@@ -280,6 +298,13 @@ enum TraceSlot {
     kTrPro0 = 28,        // 28..31: phases inside the prologue
     kTraceSlots = 32
 };
+
+// Persistent grid of the attention kernel: `cus` times `per_cu` workgroups,
+// at most kMaxWG.
+inline int attend_grid(int cus, int per_cu) {
+    const int g = cus * per_cu;
+    return g > kMaxWG ? kMaxWG : (g < 1 ? 1 : g);
+}
 
 // Host launcher (defined next to the kernel).  dtype: 0 fp32, 1 bf16.  The
 // persistent grid is `cus` times `per_cu` workgroups (at most kMaxWG).

@@ -182,3 +182,21 @@ def test_block_rule_every_block_and_short_context():
 def test_block_rule_at_128k_context():
     w = synth.Workload("select_block_128k", 36, 1, 2, 32, 8, 128, 131072, 4096, "bf16", 4, hh_frac=0.01)
     _two_layers(w, "block", 64)
+
+
+# A 2^18-token context: layer 0 gives each workgroup 8192 rows, so it makes
+# two passes (the Top-p normaliser parts and the block maxima are merged
+# across passes), and 16-token blocks give 16384 block words per head, more
+# than the rule kernel holds in registers (its scratch path).
+LONG = synth.Workload("select_256k", 37, 1, 2, 32, 8, 128, 262144, 4096, "bf16", 4, qk_scaled=False,
+                      hh_frac=0.01)
+
+
+def test_topp_rule_two_passes_per_workgroup():
+    S0, _ = _two_layers(LONG, "topp", 0.05)
+    kept = (S0 != -1).sum(axis=2)
+    assert kept.min() >= 1 and kept.max() <= LONG.k
+
+
+def test_block_rule_scratch_path_and_two_passes():
+    _two_layers(LONG.replace(name="select_256k_block", seed=38), "block", 16)
