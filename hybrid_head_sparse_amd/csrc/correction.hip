@@ -41,10 +41,19 @@ namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;               // head dim of the MFMA path
 constexpr int kTile = 32;             // keys per tile
 constexpr int kVtStride = kTile + 4;  // bf16 per transposed V row in LDS (padded)
+constexpr int kKStride = kD + 8;      // bf16 per K row in LDS (padded by 16 bytes)
+
+// the value of lane l ^ 32 (gfx950 permlane32 swap: no LDS round trip)
+__device__ __forceinline__ float lane_xor32(float v) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 // row of accumulator register r for lane half h
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
@@ -63,9 +72,14 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
     const int c0 = (int)(((long long)n * chunk) / p.nchunks);
     const int c1 = (int)(((long long)n * (chunk + 1)) / p.nchunks);
     const size_t kv_row0 = (size_t)bg * p.max_ctx;
+    const int last = max(c1 - 1, 0);   // loads clamp to the chunk's last row (row 0 for an empty chunk)
     const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.kc);
     const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.vc);
 
+    // K of a tile, row-major with rows padded to kKStride (so the A-operand
+    // reads of 8 consecutive lanes, 8 keys at one offset, fall on distinct
+    // bank groups); V of a tile transposed (d-major).  Both double-buffered.
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kD * kVtStride];
     __shared__ float s_alpha[G][32];
 
@@ -84,39 +98,51 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
     for (int t4 = 0; t4 < 4; ++t4) acc_o[t4] = v16f{};
     float m_run = -INFINITY, l_part = 0.0f;
 
-    // the V tile starting at key k0: 16-byte pieces (8 columns of one key),
-    // loaded a tile ahead into registers, then stored transposed into
-    // s_vt[buf] at the end of the current tile.  With an even number of pieces
-    // per thread, a thread takes pairs of consecutive keys (pair j: keys 2 kp,
-    // 2 kp + 1 with kp = (tid + 64 G j) / 16) and writes both keys of a column
-    // as one 32-bit word; otherwise piece j is key (tid + 64 G j) / 16 alone.
+    // A tile's K and V are loaded cooperatively, once per workgroup, as
+    // 16-byte pieces (8 columns of one key): kPieces per thread and operand.
+    // K piece j of a thread is key (tid + 64 G j) / 16, columns 8 ((tid + 64 G
+    // j) % 16): whole rows per 16 lanes, stored as they come.  V is stored
+    // transposed, so consecutive lanes take consecutive keys of one column
+    // block (their 32-bit LDS words then fall on distinct banks).  With an
+    // even number of pieces per thread, a thread takes a pair of keys (pair
+    // index i = tid + 64 G (j / 2): keys 2 (i % 16) and 2 (i % 16) + 1, columns
+    // 8 (i / 16)) and writes both keys of a column as one 32-bit word;
+    // otherwise piece j (i = tid + 64 G j) is key i % 32, columns 8 (i / 32).
     constexpr int kPieces = kTile * kD / 8 / (64 * G);
     constexpr bool kPairs = kPieces % 2 == 0;
     auto piece_key = [&](int j) -> int {
-        if constexpr (kPairs) return 2 * ((threadIdx.x + 64 * G * (j >> 1)) >> 4) + (j & 1);
-        else return (threadIdx.x + 64 * G * j) >> 4;
+        if constexpr (kPairs) return 2 * ((threadIdx.x + 64 * G * (j >> 1)) & 15) + (j & 1);
+        else return (threadIdx.x + 64 * G * j) & 31;
     };
     auto piece_d0 = [&](int j) -> int {
-        if constexpr (kPairs) return ((threadIdx.x + 64 * G * (j >> 1)) & 15) * 8;
-        else return ((threadIdx.x + 64 * G * j) & 15) * 8;
+        if constexpr (kPairs) return ((threadIdx.x + 64 * G * (j >> 1)) >> 4) * 8;
+        else return ((threadIdx.x + 64 * G * j) >> 5) * 8;
     };
     // Every load is issued on every path (rows past the chunk are clamped to
-    // its last row, V pieces there are zeroed after the load): the compiler's
-    // wait counts are then exact, and a tile waits for its own operands only,
-    // not for the loads issued ahead of it.
-    auto load_v = [&](int k0, uint4* vr) {
+    // its last row, V pieces there are zeroed after the load; K there only
+    // meets masked scores): the wait counts are then exact.
+    auto load_kv = [&](int k0, u32x4 (&kr)[kPieces], uint4 (&vr)[kPieces]) {
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j) {
+            const int idx = threadIdx.x + 64 * G * j;
+            const int key = min(k0 + (idx >> 4), last);
+            kr[j] = *reinterpret_cast<const u32x4*>(kc + (kv_row0 + (size_t)key) * kD + (idx & 15) * 8);
+        }
 #pragma unroll
         for (int j = 0; j < kPieces; ++j) {
             const int key = piece_key(j), d0 = piece_d0(j);
-            vr[j] = *reinterpret_cast<const uint4*>(vc + (kv_row0 + (size_t)min(k0 + key, c1 - 1)) * kD + d0);
+            vr[j] = *reinterpret_cast<const uint4*>(vc + (kv_row0 + (size_t)min(k0 + key, last)) * kD + d0);
         }
     };
-    auto zero_v_tail = [&](int k0, uint4* vr) {       // V rows past the chunk contribute 0
+    auto store_kv = [&](int k0, const u32x4 (&kr)[kPieces], uint4 (&vr)[kPieces], int buf) {
 #pragma unroll
-        for (int j = 0; j < kPieces; ++j)
+        for (int j = 0; j < kPieces; ++j) {
+            const int idx = threadIdx.x + 64 * G * j;
+            *reinterpret_cast<u32x4*>(&s_k[buf][(idx >> 4) * kKStride + (idx & 15) * 8]) = kr[j];
+        }
+#pragma unroll
+        for (int j = 0; j < kPieces; ++j)       // V rows past the chunk contribute 0
             if (k0 + piece_key(j) >= c1) vr[j] = make_uint4(0u, 0u, 0u, 0u);
-    };
-    auto store_v = [&](const uint4* vr, int buf) {
         if constexpr (kPairs) {
 #pragma unroll
             for (int j = 0; j < kPieces; j += 2) {
@@ -144,39 +170,51 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
             }
         }
     };
-    auto load_k = [&](int k0, uint4* kr) {
-        const int key = min(k0 + c32, c1 - 1);
-        const uint4* src = reinterpret_cast<const uint4*>(kc + (kv_row0 + (size_t)key) * kD + 64 * h);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) kr[c] = src[c];
-    };
 
-    // Two register sets per operand, alternating: at tile it, K of tiles it and
-    // it + 1 and V of tile it + 1 are in registers (V of tile it is in LDS);
-    // the loads of tile it + 2 are issued during tile it, so each has about
-    // two tiles of work to arrive.
+    // Two register sets of pieces, alternating: at tile it, tile it's K and V
+    // are in LDS buffer it & 1, tile it + 1's pieces are in one set, and tile
+    // it + 2's loads go to the other (free since its tile went to LDS at the
+    // end of tile it - 1), so each load has about two tiles of work to arrive.
+    // The first loads are issued on every path (a chunk without rows reads row
+    // 0 and uses nothing): with no branch before the loop, the wait counts at
+    // its top need not cover the query loads of a path that skips them.
     const int ntiles = c1 > c0 ? (c1 - c0 + kTile - 1) / kTile : 0;
-    uint4 kA[8], kB[8], vA[kPieces], vB[kPieces];
-    if (ntiles > 0) {
-        load_k(c0, kA);
-        load_v(c0, vA);
-        load_k(c0 + kTile, kB);
-        load_v(c0 + kTile, vB);
-        zero_v_tail(c0, vA);
-        store_v(vA, 0);
-    }
+    u32x4 kA[kPieces], kB[kPieces];
+    uint4 vA[kPieces], vB[kPieces];
+    load_kv(c0, kA, vA);
+    load_kv(c0 + kTile, kB, vB);
+    store_kv(c0, kA, vA, 0);
     __syncthreads();
-    // tile it with K in kx, its V in LDS, the next tile's V in vy; vx is free
-    auto tile = [&](int it, uint4 (&kx)[8], uint4 (&vx)[kPieces], uint4 (&vy)[kPieces]) {
+    // tile it: its K and V in LDS, the next tile's pieces in (kn, vn); (kf, vf) free
+    auto tile = [&](int it, u32x4 (&kn)[kPieces], uint4 (&vn)[kPieces], u32x4 (&kf)[kPieces],
+                    uint4 (&vf)[kPieces]) {
         const int k0 = c0 + it * kTile;
         const int buf = it & 1;
-        load_v(k0 + 2 * kTile, vx);
-        // S^T = K Q^T
-        v16f s = v16f{};
+        load_kv(k0 + 2 * kTile, kf, vf);
+        // S^T = K Q^T (A operand: key c32, columns 64 h + 8 c .. + 7)
+        v8bf ka[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kx[c]), qop[c], s, 0, 0, 0);
-        load_k(k0 + 2 * kTile, kx);   // this set's K registers are free again
+            ka[c] = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(&s_k[buf][c32 * kKStride + 64 * h + 8 * c]));
+        // the B operands of O += P V (keys 16 s + 4 h + 0..3 and 16 s + 8 + 4 h
+        // + 0..3 of one d column of V^T), read here so that their latency
+        // passes during the S MFMAs and the softmax rather than before each
+        // P V MFMA
+        v8bf bv[4][2];
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint16_t* col = &s_vt[buf][(32 * t4 + c32) * kVtStride + 16 * ks + 4 * h];
+                const uint2 lo = *reinterpret_cast<const uint2*>(col);
+                const uint2 hi = *reinterpret_cast<const uint2*>(col + 8);
+                bv[t4][ks] = __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        v16f s = v16f{};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qop[c], s, 0, 0, 0);
         // causal mask and the tile max of this lane's query
         float z[16];
         float mt = -INFINITY;
@@ -197,7 +235,7 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
                 mt = fmaxf(mt, z[r]);
             }
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = fmaxf(mt, lane_xor32(mt));
         const float m_new = fmaxf(m_run, mt);
         // lazy rescale (when the max grows by more than 2^8, or from empty)
         const bool grow = m_new > m_run + 8.0f || (m_run == -INFINITY && m_new != -INFINITY);
@@ -236,35 +274,26 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
             }
         }
         l_part += ls;
-        // O += P V (B operand of step s: keys 16 s + 4 h + 0..3 and 16 s + 8 + 4 h
-        // + 0..3 of one d column of V^T)
+        // O += P V
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
+        for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const uint16_t* col = &s_vt[buf][(32 * t4 + c32) * kVtStride + 16 * ks + 4 * h];
-                const uint2 lo = *reinterpret_cast<const uint2*>(col);
-                const uint2 hi = *reinterpret_cast<const uint2*>(col + 8);
-                const v8bf bv = __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                acc_o[t4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bv, acc_o[t4], 0, 0, 0);
-            }
-        }
-        if (it + 1 < ntiles) {
-            zero_v_tail(k0 + kTile, vy);
-            store_v(vy, buf ^ 1);     // (buf ^ 1 was last read before the previous barrier)
-        }
+            for (int ks = 0; ks < 2; ++ks)
+                acc_o[t4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], bv[t4][ks], acc_o[t4], 0, 0, 0);
+        // the next tile to the other buffer (last read before the previous barrier)
+        if (it + 1 < ntiles) store_kv(k0 + kTile, kn, vn, buf ^ 1);
         __syncthreads();                 // buf ^ 1 complete; buf is restaged only after the next barrier
     };
     int it = 0;
     for (; it + 1 < ntiles; it += 2) {
-        tile(it, kA, vA, vB);
-        tile(it + 1, kB, vB, vA);
+        tile(it, kB, vB, kA, vA);
+        tile(it + 1, kA, vA, kB, vB);
     }
-    if (it < ntiles) tile(it, kA, vA, vB);
+    if (it < ntiles) tile(it, kB, vB, kA, vA);
 
     // partials of this chunk: per query row (w, q): m (log2), l, unnormalised O
     const size_t rec = (size_t)blockIdx.x * (32 * G);
-    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    const float l_tot = l_part + lane_xor32(l_part);
     if (h == 0) {
         p.rec_ml[(rec + (size_t)w * 32 + c32) * 2 + 0] = m_run;
         p.rec_ml[(rec + (size_t)w * 32 + c32) * 2 + 1] = l_tot;
