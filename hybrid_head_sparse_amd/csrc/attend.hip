@@ -1802,21 +1802,31 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 
         // Two-deep software pipeline over the tiles of [r_lo, r_hi): wave w
         // owns tiles starting at r_lo + w*KPW, stepping by STRIDE.
+        // The bounds are wavefront-uniform by construction; saying so keeps the
+        // loop's exits scalar, so no path reaches the loop top with lanes off
+        // and tile B's loads still in flight (the wait there would have to
+        // drain every load, tile A's prefetch included).
         auto stream_range = [&](uint32_t r_lo, uint32_t r_hi, const int32_t* sidx) {
+            r_lo = __builtin_amdgcn_readfirstlane(r_lo);
+            r_hi = __builtin_amdgcn_readfirstlane(r_hi);
             uint32_t tb = r_lo + (uint32_t)wave * KPW;
             if (tb >= r_hi) return;
             Frag<NDW> kA[NK], vA[NK], kB[NK], vB[NK];
             int tokA = 0, tokB = 0;
             bool vmA = false, vmB = false;
             load_tile(tb, r_lo, r_hi, sidx, kA, vA, tokA, vmA);
+            // One exit, at the bottom: an exit between the two halves would
+            // reach the loop top (as the structurizer lays it out) with tile
+            // B's loads in flight, and the wait there would drain tile A's
+            // prefetch on every iteration.  Tile A's loads of the last round
+            // may lie past the range (clamped rows, never computed).
             for (;;) {
                 const uint32_t t1 = tb + STRIDE;
                 load_tile(t1, r_lo, r_hi, sidx, kB, vB, tokB, vmB);
                 compute_tile(kA, vA, tokA, vmA);
-                if (t1 >= r_hi) break;
                 const uint32_t t2 = t1 + STRIDE;
                 load_tile(t2, r_lo, r_hi, sidx, kA, vA, tokA, vmA);
-                compute_tile(kB, vB, tokB, vmB);
+                if (t1 < r_hi) compute_tile(kB, vB, tokB, vmB);
                 if (t2 >= r_hi) break;
                 tb = t2;
             }
