@@ -73,8 +73,10 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
     const int c1 = (int)(((long long)n * (chunk + 1)) / p.nchunks);
     const size_t kv_row0 = (size_t)bg * p.max_ctx;
     const int last = max(c1 - 1, 0);   // loads clamp to the chunk's last row (row 0 for an empty chunk)
-    const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.kc);
-    const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.vc);
+    // this head's rows (a wavefront-uniform base; per-lane offsets stay 32-bit:
+    // a head's slot is max_ctx * 256 bytes)
+    const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.kc) + kv_row0 * kD;
+    const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.vc) + kv_row0 * kD;
 
     // K of a tile, row-major with rows padded to kKStride (so the A-operand
     // reads of 8 consecutive lanes, 8 keys at one offset, fall on distinct
@@ -126,12 +128,12 @@ __global__ void __launch_bounds__(64 * G, G >= 4 ? 2 : 1) correction_partial_ker
         for (int j = 0; j < kPieces; ++j) {
             const int idx = threadIdx.x + 64 * G * j;
             const int key = min(k0 + (idx >> 4), last);
-            kr[j] = *reinterpret_cast<const u32x4*>(kc + (kv_row0 + (size_t)key) * kD + (idx & 15) * 8);
+            kr[j] = *reinterpret_cast<const u32x4*>(kc + ((uint32_t)key * kD + (uint32_t)(idx & 15) * 8u));
         }
 #pragma unroll
         for (int j = 0; j < kPieces; ++j) {
             const int key = piece_key(j), d0 = piece_d0(j);
-            vr[j] = *reinterpret_cast<const uint4*>(vc + (kv_row0 + (size_t)min(k0 + key, last)) * kD + d0);
+            vr[j] = *reinterpret_cast<const uint4*>(vc + ((uint32_t)min(k0 + key, last) * kD + (uint32_t)d0));
         }
     };
     auto store_kv = [&](int k0, const u32x4 (&kr)[kPieces], uint4 (&vr)[kPieces], int buf) {
