@@ -11,8 +11,9 @@
 // instruction).  A workgroup takes one (sequence, KV head) and one chunk of
 // its context; wavefront w is query head g G + w and holds that head's T
 // queries (padded to 32) as the 32 columns of its tiles.  Per tile of 32 keys:
-//   S^T = K Q^T          (8 MFMAs over d = 128; K straight from memory,
-//                         each lane a contiguous 128 bytes of one key row)
+//   S^T = K Q^T          (8 MFMAs over d = 128; the A operands, 16 bytes of
+//                         one key row per lane and MFMA, read from the tile's
+//                         K in LDS)
 //   causal mask, online softmax in the log2 domain (each lane holds 16 keys
 //   of one query; one exchange with the other half-wave gives the tile max;
 //   a tile that every query sees whole skips the mask, and its exponent is
@@ -21,7 +22,11 @@
 //   O += P V             (8 MFMAs: the 16 probabilities a lane holds are,
 //                         converted to bf16, its A operands for the tile's
 //                         two 16-key steps; V is staged transposed in LDS,
-//                         double-buffered, so a B operand is two 8-byte reads)
+//                         so a B operand is two 8-byte reads)
+// The workgroup loads each tile's K and V once (16-byte pieces, two tiles
+// ahead) and stages them in double-buffered LDS: K row-major with padded rows,
+// V transposed.  Every wavefront reads its operands of both MFMA groups at the
+// top of the tile.
 // A contraction may take its index in any order common to both operands: over
 // d, lane half h takes d in [64 h, 64 h + 64); over the keys of a 16-key step
 // s, element i of lane half h is key 16 s + 8 (i / 4) + 4 h + i % 4, which is
