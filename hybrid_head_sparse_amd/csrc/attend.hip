@@ -48,6 +48,7 @@
 // Cross-workgroup hand-off uses device-coherent stores/loads and relaxed
 // counters (see common.hpp): no L2-wide write-back or invalidate.
 #include "common.hpp"
+#include "rules.hpp"
 
 namespace lychee {
 namespace {
@@ -536,7 +537,7 @@ __device__ __forceinline__ void block_crossing(const uint32_t (&cnt)[PER], int n
     __syncthreads();
 }
 
-template <typename T, int D, int G, bool HYBRID>
+template <typename T, int D, int G, bool HYBRID, bool BLOCK>
 __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendParams p) {
     using Ge = Geo<T, D, G>;
     constexpr int EPL = Ge::EPL, NDW = Ge::NDW, NK = Ge::NK, KPW = Ge::KPW, RS = Ge::RS;
@@ -575,10 +576,17 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         alignas(16) unsigned long long comp[HYBRID ? kFastGroup : 1];   // the threshold digit's composites
         uint32_t jc[HYBRID ? kFastPer * kWaves : 1];   // winners per (step, wavefront), then their prefix
     };
+    struct BlockLds {                         // the block rule's resolve (block_resolve)
+        uint32_t h12[HYBRID ? kHistBins : 1];     // first-digit histogram of the block words
+        uint32_t w[HYBRID ? kMaxCtx / 16 : 1];    // the head's block words (blocks of >= 16 tokens)
+        uint32_t list[HYBRID ? kMaxSelBlocks : 1];   // the kept blocks, ascending (at most floor(k / bs))
+        alignas(16) unsigned long long comp[HYBRID ? kFastGroup : 1];   // the threshold digit's composites
+    };
     union Lds {
         StreamLds st;
         SelectLds se;
         FastLds fr;
+        BlockLds bl;
     };
     __shared__ __attribute__((aligned(16))) Lds u;
     __shared__ uint32_t s_pref[kMaxBH + 1];
@@ -1578,6 +1586,162 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         return false;
     };
 
+    // The block rule (blocks of bs = 2^sel_block tokens, a block scored by the
+    // largest selection key of its tokens): the floor(k / bs) highest blocks,
+    // ties to the lower block, their tokens listed ascending in S (a short last
+    // block is the highest kept one, so its missing tokens fall at the end).
+    // Every pass folded its blocks' largest keys into the head's block words;
+    // the head's last selection arrival (or its helper) reads them here,
+    // restores them to zero, and cuts on full_order(word, block):
+    // 1. the words to LDS and their first digits to a histogram; the crossing
+    //    at floor(k / bs) gives the threshold digit T and the count above it;
+    // 2. the cut within digit T: by counting ranks when T holds at most
+    //    kFastGroup blocks, else by 12-bit radix passes over the composites of
+    //    T (a composite prefix: a digit is an aligned key range);
+    // 3. one block scan lists the kept blocks ascending; S is written from
+    //    the list.
+    auto block_resolve = [&](int hb, int n) __attribute__((always_inline)) {
+        int32_t* srow = p.S_out + (size_t)hb * p.k;
+        uint32_t* bk = p.ws.bkey + (size_t)hb * (size_t)p.bkey_stride;
+        const uint32_t bsh = p.sel_block;
+        const uint32_t nb = ((uint32_t)n + (1u << bsh) - 1u) >> bsh;
+        const uint32_t m = min((uint32_t)p.k >> bsh, nb);               // blocks kept
+        __syncthreads();
+        for (int i = tid; i < kHistBins; i += kAttendThreads) u.bl.h12[i] = 0u;
+        if (tid == 0) s_ceq = 0u;
+        __syncthreads();
+        for (uint32_t base = 0; base < nb; base += kAttendThreads * 8u) {
+            uint32_t wv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {                                  // every load in flight at once
+                const uint32_t i = base + (uint32_t)(kAttendThreads * e + tid);
+                wv[e] = i < nb ? coherent_load(&bk[i]) : 0u;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t i = base + (uint32_t)(kAttendThreads * e + tid);
+                if (i < nb) {
+                    coherent_store(&bk[i], 0u);                            // below every key, for the next call
+                    u.bl.w[i] = wv[e];
+                    atomicAdd(&u.bl.h12[key_digit(wv[e])], 1u);
+                }
+            }
+        }
+        __syncthreads();
+        unsigned long long cut = 0ull;                                     // kept: full_order >= cut
+        if (m < nb) {
+            {
+                uint32_t hc[kHistPerThread];
+#pragma unroll
+                for (int i = 0; i < kHistPerThread; ++i) hc[i] = u.bl.h12[kHistBins - 1 - (kHistPerThread * tid + i)];
+                block_crossing<kHistPerThread>(hc, kHistBins, m, s_wave, s_res);
+            }
+            const uint32_t Td = s_res[0], above = s_res[1], g = s_res[3] - s_res[1];
+            const uint32_t klo = (uint32_t)digit_first_key(Td);
+            const uint32_t khi = (uint32_t)(digit_first_key(Td + 1u) - 1ull);
+            const uint32_t r_left = m - above;                             // blocks of digit T kept (>= 1)
+            __syncthreads();                                               // s_res is rewritten below
+            if (r_left == g) {
+                cut = (unsigned long long)klo << 32;                       // every block of digit T
+            } else if (g <= (uint32_t)kFastGroup) {
+                for (uint32_t i = tid; i < nb; i += kAttendThreads) {
+                    const uint32_t wv = u.bl.w[i];
+                    if (wv >= klo && wv <= khi) u.bl.comp[atomicAdd(&s_ceq, 1u)] = full_order(wv, i);
+                }
+                __syncthreads();
+                // the r_left-th largest of the group: r_left - 1 of its
+                // composites lie above it (composites are distinct)
+                for (uint32_t q = tid; q < g; q += kAttendThreads) {
+                    const unsigned long long mine = u.bl.comp[q];
+                    uint32_t gt = 0, j = 0;
+                    for (; j + 8u <= g; j += 8u) {
+                        unsigned long long c8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) c8[e] = u.bl.comp[j + e];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) gt += c8[e] > mine ? 1u : 0u;
+                    }
+                    for (; j < g; ++j) gt += u.bl.comp[j] > mine ? 1u : 0u;
+                    if (gt == r_left - 1u) s_cut = mine;
+                }
+                __syncthreads();
+                cut = s_cut;
+            } else {
+                // many blocks share digit T (e.g. identical keys): 12-bit radix
+                // passes over its composites, which share the bits above `shift`
+                const uint32_t x = klo ^ khi;
+                int shift = 32 + (x ? 32 - __clz(x) : 0);
+                unsigned long long prefix = ((unsigned long long)klo << 32) >> shift;
+                uint32_t need = r_left;
+                while (shift > 0) {
+                    const int bits = shift >= 12 ? 12 : shift;
+                    const int nshift = shift - bits;
+                    const uint32_t nbin = 1u << bits;
+                    for (int i = tid; i < kHistBins; i += kAttendThreads) u.bl.h12[i] = 0u;
+                    __syncthreads();
+                    for (uint32_t i = tid; i < nb; i += kAttendThreads) {
+                        const unsigned long long c = full_order(u.bl.w[i], i);
+                        if ((c >> shift) == prefix) atomicAdd(&u.bl.h12[(uint32_t)(c >> nshift) & (nbin - 1u)], 1u);
+                    }
+                    __syncthreads();
+                    uint32_t hc[kHistPerThread];
+#pragma unroll
+                    for (int i = 0; i < kHistPerThread; ++i) {
+                        const uint32_t rank = (uint32_t)(kHistPerThread * tid + i);
+                        hc[i] = rank < nbin ? u.bl.h12[nbin - 1u - rank] : 0u;
+                    }
+                    block_crossing<kHistPerThread>(hc, (int)nbin, need, s_wave, s_res);
+                    const uint32_t d = s_res[0], ab = s_res[1], gs = s_res[3] - s_res[1];
+                    __syncthreads();
+                    prefix = (prefix << bits) | d;
+                    need -= ab;
+                    shift = nshift;
+                    if (gs == 1u && shift > 0) {                           // the bin holds the cut alone
+                        for (uint32_t i = tid; i < nb; i += kAttendThreads) {
+                            const unsigned long long c = full_order(u.bl.w[i], i);
+                            if ((c >> shift) == prefix) s_cut = c;
+                        }
+                        __syncthreads();
+                        prefix = s_cut;
+                        shift = 0;
+                    }
+                }
+                cut = prefix;
+            }
+        }
+        // the kept blocks, ascending: thread t takes blocks [per t, per t + per)
+        const uint32_t per = (nb + kAttendThreads - 1u) / kAttendThreads;
+        const uint32_t e0 = (uint32_t)tid * per;
+        uint32_t mine = 0;
+        for (uint32_t e = 0; e < per; ++e) {
+            const uint32_t i = e0 + e;
+            mine += (i < nb && full_order(u.bl.w[i], i) >= cut) ? 1u : 0u;
+        }
+        uint32_t tot;
+        uint32_t at = block_exclusive_scan(mine, s_wave, &tot);
+        for (uint32_t e = 0; e < per; ++e) {
+            const uint32_t i = e0 + e;
+            if (i < nb && full_order(u.bl.w[i], i) >= cut) {
+                if (at < (uint32_t)kMaxSelBlocks) u.bl.list[at] = i;
+                ++at;
+            }
+        }
+        __syncthreads();
+        const uint32_t kept = min(min(tot, m), (uint32_t)kMaxSelBlocks);
+        const uint32_t bmask = (1u << bsh) - 1u;
+        for (uint32_t i = tid; i < (uint32_t)p.k; i += kAttendThreads) {
+            const uint32_t r = i >> bsh;
+            int32_t v = -1;
+            if (r < kept) {
+                const uint32_t tok = (u.bl.list[r] << bsh) + (i & bmask);
+                v = tok < (uint32_t)n ? (int32_t)tok : -1;
+            }
+            srow[i] = v;
+        }
+        if (tid == 0 && tot != m) atomicOr(p.ws.err, 2u);
+        __syncthreads();
+    };
+
     // The heads of the range in order; a head whose top-k this workgroup
     // resolves (as its last selection arrival, or as its helper once the
     // range is done) waits in `pending` and is resolved at the top of the
@@ -1598,7 +1762,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #ifdef LYCHEE_TRACE
             tr_flags |= 8u;
 #endif
-            if (__builtin_expect(fast_resolve(X, s_nctx[b], s_ke[b], h0, wf, wl - wf + 1), 0)) {
+            if constexpr (BLOCK) {
+                block_resolve(X, s_nctx[b]);
+            } else if (__builtin_expect(fast_resolve(X, s_nctx[b], s_ke[b], h0, wf, wl - wf + 1), 0)) {
 #ifdef LYCHEE_TRACE
                 tr_flags |= 32u;
 #endif
@@ -1618,7 +1784,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // range done: the helper duty, if any (a bounded wait for the
             // head's last arrival; on time-out the helper withdraws and the
             // last arrival resolves)
-            if (HYBRID && !helped && !p.sel_block) {
+            if (HYBRID && !helped) {
                 helped = true;
                 const int X = helped_by(w);
                 if (X >= 0) {
@@ -1856,7 +2022,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 stream_range(c_lo, c_hi, nullptr);
                 __syncthreads();
                 LYCHEE_STAMP(kTrStreamEnd);
-                if (p.sel_block) {
+                if (BLOCK) {
                     // The block rule: the largest key of each block of the pass
                     // (blocks of 2^sel_block >= 16 tokens, numbered from token
                     // 0), folded into the head's block words by atomic max.
@@ -2035,13 +2201,13 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                 *reinterpret_cast<uint4*>(p.ws.zpart + 4 * (size_t)(w + bg)) =
                     make_uint4((uint32_t)bg + 1u, __builtin_bit_cast(uint32_t, zm), (uint32_t)zb, (uint32_t)(zb >> 32));
             }
-            if (tid == 0 && !p.sel_block) coherent_store(&p.ws.wmeta[w + bg], w_count | (w_bound << 20));
-            const int hw = p.sel_block ? -1 : helper_of(bg);   // (while the stores travel)
+            if (tid == 0 && !BLOCK) coherent_store(&p.ws.wmeta[w + bg], w_count | (w_bound << 20));
+            const int hw = helper_of(bg);   // (while the stores travel)
             wait_stores_complete();
             __syncthreads();
             if (tid == 0) {
                 uint32_t last = 0;
-                if (!p.sel_block) {
+                {
                     const uint32_t before = (uint32_t)counter_add64(&p.ws.selctr[bg], 1ull);
                     last = before + 1u == (uint32_t)nw;
                     if (last) {
@@ -2242,29 +2408,38 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     LYCHEE_STAMP(kTrExit);
 }
 
-template <typename T, int D, int G, bool HYBRID>
+template <typename T, int D, int G, bool HYBRID, bool BLOCK>
 hipError_t launch_one(const AttendParams& p, int cus, int per_cu, hipStream_t stream) {
     const int grid = attend_grid(cus, per_cu);
-    hipLaunchKernelGGL((attend_kernel<T, D, G, HYBRID>), dim3(grid), dim3(kAttendThreads), 0, stream, p);
+    hipLaunchKernelGGL((attend_kernel<T, D, G, HYBRID, BLOCK>), dim3(grid), dim3(kAttendThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename T, int D, bool HYBRID>
+template <typename T, int D, bool HYBRID, bool BLOCK>
 hipError_t launch_g(const AttendParams& p, int G, int cus, int per_cu, hipStream_t stream) {
     switch (G) {
-        case 1: return launch_one<T, D, 1, HYBRID>(p, cus, per_cu, stream);
-        case 2: return launch_one<T, D, 2, HYBRID>(p, cus, per_cu, stream);
-        case 4: return launch_one<T, D, 4, HYBRID>(p, cus, per_cu, stream);
-        case 8: return launch_one<T, D, 8, HYBRID>(p, cus, per_cu, stream);
+        case 1: return launch_one<T, D, 1, HYBRID, BLOCK>(p, cus, per_cu, stream);
+        case 2: return launch_one<T, D, 2, HYBRID, BLOCK>(p, cus, per_cu, stream);
+        case 4: return launch_one<T, D, 4, HYBRID, BLOCK>(p, cus, per_cu, stream);
+        case 8: return launch_one<T, D, 8, HYBRID, BLOCK>(p, cus, per_cu, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T, bool HYBRID>
+template <typename T, bool HYBRID, bool BLOCK>
 hipError_t launch_d(const AttendParams& p, int D, int G, int cus, int per_cu, hipStream_t stream) {
-    if (D == 64) return launch_g<T, 64, HYBRID>(p, G, cus, per_cu, stream);
-    if (D == 128) return launch_g<T, 128, HYBRID>(p, G, cus, per_cu, stream);
+    if (D == 64) return launch_g<T, 64, HYBRID, BLOCK>(p, G, cus, per_cu, stream);
+    if (D == 128) return launch_g<T, 128, HYBRID, BLOCK>(p, G, cus, per_cu, stream);
     return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_t(const AttendParams& p, int D, int G, bool hybrid, int cus, int per_cu, hipStream_t stream) {
+    if (!hybrid) return launch_d<T, false, false>(p, D, G, cus, per_cu, stream);
+    // the block rule has its own build of the kernel: its resolver stays out of
+    // the token top-k build's code and register allocation
+    return p.sel_block ? launch_d<T, true, true>(p, D, G, cus, per_cu, stream)
+                       : launch_d<T, true, false>(p, D, G, cus, per_cu, stream);
 }
 
 }  // namespace
@@ -2272,12 +2447,10 @@ hipError_t launch_d(const AttendParams& p, int D, int G, int cus, int per_cu, hi
 hipError_t launch_attend(const AttendParams& p, int dtype, int D, int G, bool hybrid, int cus, int per_cu,
                          hipStream_t stream) {
 #ifdef LYCHEE_ONE_VARIANT   // compile-time probe of one variant's resources (not a library build)
-    return hybrid ? launch_one<BF16, 128, 4, true>(p, cus, per_cu, stream) : hipErrorInvalidValue;
+    return hybrid ? launch_one<BF16, 128, 4, true, false>(p, cus, per_cu, stream) : hipErrorInvalidValue;
 #endif
-    if (dtype == 1) return hybrid ? launch_d<BF16, true>(p, D, G, cus, per_cu, stream)
-                                  : launch_d<BF16, false>(p, D, G, cus, per_cu, stream);
-    if (dtype == 0) return hybrid ? launch_d<F32, true>(p, D, G, cus, per_cu, stream)
-                                  : launch_d<F32, false>(p, D, G, cus, per_cu, stream);
+    if (dtype == 1) return launch_t<BF16>(p, D, G, hybrid, cus, per_cu, stream);
+    if (dtype == 0) return launch_t<F32>(p, D, G, hybrid, cus, per_cu, stream);
     return hipErrorInvalidValue;
 }
 
