@@ -312,9 +312,7 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
         tp.S = S_out;
         tp.score = h->ws.score;
         tp.comp = h->ws.cand;
-        tp.bkey = h->ws.bkey;
         tp.zpart = h->ws.zpart;
-        tp.bkey_stride = block_key_stride(d.max_ctx);
         tp.nslots = attend_grid(h->cus, h->per_cu) + d.batch * d.n_kv_heads;
         tp.n_ctx = n_ctx;
         tp.err = h->ws.err;
@@ -323,10 +321,8 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
         tp.Hkv = d.n_kv_heads;
         tp.max_ctx = d.max_ctx;
         tp.k = k;
-        tp.mode = rule == LYCHEE_SELECT_TOPP ? kRuleTopP : kRuleBlock;
-        tp.block = rule == LYCHEE_SELECT_BLOCK ? (int32_t)param : 0;
         tp.c_log2 = (float)(1.4426950408889634 / ((double)G * std::sqrt((double)d.head_dim)));
-        tp.P = rule == LYCHEE_SELECT_TOPP ? (unsigned long long)(param * 0x1p52) : 0ull;
+        tp.P = (unsigned long long)(param * 0x1p52);
         e = launch_rule_select(tp, h->stream);
         if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "rule selection launch failed: %s", hipGetErrorString(e));
     }

@@ -158,7 +158,7 @@ struct Workspace {
     uint32_t* hist;              // [BH * kHistBins]          first-digit counts from each pass's bound up
     uint32_t* bkey;              // [BH * ceil(max_ctx / 16)] block rule: the largest selection key of
                                  //                           each block (atomic max; read and restored to
-                                 //                           zero by the rule-selection kernel)
+                                 //                           zero by the head's block resolve)
     uint32_t* zpart;             // [(kMaxWG + BH) * 4]       Top-p: per (workgroup w, head bg) at w + bg:
                                  //                           bg + 1 (0 = empty), the largest pooled sum m
                                  //                           and the sum of 2^((f - m) c) as a double
@@ -262,9 +262,10 @@ struct AttendParams {
     // kept.  S is padded with -1.
     double sel_ratio;
     uint32_t sel_tkey;
-    // Block rule (sel_block = log2 of the block size, 0 otherwise): retrieval
-    // heads fold each block's largest selection key into ws.bkey and leave S
-    // to the rule-selection kernel (no top-k, no score buffer).
+    // Block rule (sel_block = log2 of the block size, 0 otherwise; the
+    // kernel's BLOCK build): retrieval heads fold each block's largest
+    // selection key into ws.bkey (no token top-k, no score buffer), and the
+    // head's last selection arrival or its helper cuts the blocks.
     uint32_t sel_block;
     // Top-p rule: retrieval heads also publish their part of the normaliser
     // (ws.zpart) for the rule-selection kernel.

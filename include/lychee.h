@@ -143,8 +143,8 @@ lychee_status lychee_decode_layer(lychee_handle* h,
  *              bs = param tokens (16, 32, 64, 128 or 256; the last block may
  *              be shorter), a block scored by the largest s_j of its tokens,
  *              the floor(k / bs) highest blocks kept (at most 4096 blocks;
- *              k >= bs), their tokens listed ascending.  Runs the second
- *              kernel too.
+ *              k >= bs), their tokens listed ascending.  Cut inside the
+ *              attention kernel (no second kernel).
  * Ties go to the lower index (token or block) under every rule. */
 enum {
     LYCHEE_SELECT_TOPK = 0,
@@ -162,7 +162,7 @@ enum {
  * unused for TOPK).  Returns LYCHEE_ERR_INVALID_ARG for an unknown rule, theta
  * or p outside (0, 1], a NaN tau or a block size or k the block rule does not
  * take, after which nothing is enqueued.  With profile events set, `stop`
- * follows the second kernel of TOPP and BLOCK. */
+ * follows the second kernel of TOPP. */
 lychee_status lychee_decode_layer_select(lychee_handle* h,
                                          const void* q, const void* k_cache, const void* v_cache,
                                          const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out,
