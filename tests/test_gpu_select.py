@@ -186,8 +186,9 @@ def test_block_rule_at_128k_context():
 
 # A 2^18-token context: layer 0 gives each workgroup 8192 rows, so it makes
 # two passes (the Top-p normaliser parts and the block maxima are merged
-# across passes), and 16-token blocks give 16384 block words per head, more
-# than the rule kernel holds in registers (its scratch path).
+# across passes), and 16-token blocks give 16384 block words per head, the
+# most the block resolve holds in LDS; the Top-p kernel holds more than 16
+# of a head's 4096 entries per thread outside its registers.
 LONG = synth.Workload("select_256k", 37, 1, 2, 32, 8, 128, 262144, 4096, "bf16", 4, qk_scaled=False,
                       hh_frac=0.01)
 
@@ -198,5 +199,31 @@ def test_topp_rule_two_passes_per_workgroup():
     assert kept.min() >= 1 and kept.max() <= LONG.k
 
 
-def test_block_rule_scratch_path_and_two_passes():
+def test_block_rule_16384_blocks_and_two_passes():
     _two_layers(LONG.replace(name="select_256k_block", seed=38), "block", 16)
+
+
+@pytest.mark.parametrize("n", [9001, 40000])
+def test_block_rule_tied_block_maxima(n):
+    """Every key ties, so every block's largest key ties: the floor(k / bs)
+    lowest blocks are kept (reading R17: ties go to the lower block).  In
+    16-token blocks, 9001 tokens give 563 blocks, cut by counting ranks within
+    the threshold digit; 40000 give 2500, more than that count takes, cut by
+    radix passes over the digit's composites."""
+    import torch
+    k, bs = 1024, 16
+    w = synth.Workload(f"block_ties_{n}", 39, 1, 1, 8, 2, 128, n, k, "bf16", 0, ctx_list=(n,))
+    x = synth.layer_inputs(w, 0)
+    x["k"][:] = x["k"][:, :, :1, :]
+    handle = make_handle(w)
+    lens = synth.n_ctx(w)
+    n_ctx_dev = torch.from_numpy(lens).cuda()
+    role = np.ones(2, np.uint8)
+    log(f"[block ties] n={n} k={k} bs={bs}")
+    out, S, _ = run_layer(handle, x, role, None, n_ctx_dev, k, rule="block", param=bs)
+    m = min(k // bs, -(-n // bs))
+    for g in range(2):
+        np.testing.assert_array_equal(S[0, g, :m * bs], np.arange(m * bs))
+        assert np.all(S[0, g, m * bs:] == -1)
+    compare_layer(out, S, x, role, None, lens, k, "bf16", rule="block", param=bs)
+    handle.check_device_errors()
