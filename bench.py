@@ -274,8 +274,7 @@ def main():
     step_bytes = sum(hyb_bytes)
     att_mean = [statistics.mean(v) for v in att_ms]
     # The roofline's launch time: the graph-timed step (HIP events on the
-    # replay stream) over its launches -- one attention kernel per layer, plus
-    # the rule kernel of the Top-p and block rules, which is counted in.  The
+    # replay stream) over its launches -- one attention kernel per layer.  The
     # per-launch event times of eager calls add the launch overhead of an
     # eager call and are reported beside it.
     att_all_bytes = sum(hyb_bytes)                    # per step, over all attention launches

@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblychee.so")
 TRACE_BUILD = os.path.join(HERE, "_build_trace")
 TRACE_LIB = os.path.join(HERE, "liblychee_trace.so")
-SOURCES = ["attend.hip", "rules.hip", "correction.hip", "abi.hip"]
+SOURCES = ["attend.hip", "correction.hip", "abi.hip"]
 ARCH = os.environ.get("LYCHEE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -12,7 +12,6 @@
 
 #include "../../include/lychee.h"
 #include "common.hpp"
-#include "rules.hpp"
 #include "correction.hpp"
 
 using namespace lychee;
@@ -291,6 +290,7 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
     if (hybrid && rule == LYCHEE_SELECT_BLOCK)
         while ((1 << ap.sel_block) < (int)param) ++ap.sel_block;          // param: 16 .. 256, a power of two
     ap.sel_zpart = hybrid && rule == LYCHEE_SELECT_TOPP ? 1u : 0u;
+    ap.topp_P = rule == LYCHEE_SELECT_TOPP ? (unsigned long long)(param * 0x1p52) : 0ull;
     ap.bkey_stride = block_key_stride(d.max_ctx);
     // The kernel's selection key is the fp32 sum of the G query heads' raw
     // dot products, i.e. G sqrt(d) times the pooled score: tau maps there.
@@ -304,28 +304,6 @@ static lychee_status run_layer(lychee_handle* h, const void* q, const void* kc, 
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
     hipError_t e = launch_attend(ap, d.dtype, d.head_dim, G, hybrid, h->cus, h->per_cu, h->stream);
     if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-    if (hybrid && bits != 0 && rule == LYCHEE_SELECT_TOPP) {
-        // the attention kernel wrote the top-min(k, n) sets and the normaliser
-        // parts: cut the sets to their Top-p prefix (the block rule is cut in
-        // the attention kernel itself)
-        RuleParams tp{};
-        tp.S = S_out;
-        tp.score = h->ws.score;
-        tp.comp = h->ws.cand;
-        tp.zpart = h->ws.zpart;
-        tp.nslots = attend_grid(h->cus, h->per_cu) + d.batch * d.n_kv_heads;
-        tp.n_ctx = n_ctx;
-        tp.err = h->ws.err;
-        tp.role_bits = bits;
-        tp.B = d.batch;
-        tp.Hkv = d.n_kv_heads;
-        tp.max_ctx = d.max_ctx;
-        tp.k = k;
-        tp.c_log2 = (float)(1.4426950408889634 / ((double)G * std::sqrt((double)d.head_dim)));
-        tp.P = (unsigned long long)(param * 0x1p52);
-        e = launch_rule_select(tp, h->stream);
-        if (e != hipSuccess) return fail(LYCHEE_ERR_HIP, "rule selection launch failed: %s", hipGetErrorString(e));
-    }
     if (h->ev_stop && hipEventRecord(h->ev_stop, h->stream) != hipSuccess)
         return fail(LYCHEE_ERR_HIP, "hipEventRecord failed");
     return ok();

@@ -48,7 +48,6 @@
 // Cross-workgroup hand-off uses device-coherent stores/loads and relaxed
 // counters (see common.hpp): no L2-wide write-back or invalidate.
 #include "common.hpp"
-#include "rules.hpp"
 
 namespace lychee {
 namespace {
@@ -408,6 +407,8 @@ __device__ __forceinline__ unsigned long long digit_first_key(uint32_t d) {
 }
 constexpr int kWords = kMaxCtx / 32;                     // context bitmap words
 constexpr int kHistPerThread = kHistBins / kAttendThreads;
+constexpr int kToppBins = 256;                           // Top-p cut: 8-bit radix digits
+constexpr int kToppSlots = 16;                           // Top-p cut: set entries a thread holds in registers
 constexpr int kCandPerThread = kCandLds / kAttendThreads;
 
 __device__ __forceinline__ unsigned long long pack_cand(uint32_t key, uint32_t idx) {
@@ -537,7 +538,7 @@ __device__ __forceinline__ void block_crossing(const uint32_t (&cnt)[PER], int n
     __syncthreads();
 }
 
-template <typename T, int D, int G, bool HYBRID, bool BLOCK>
+template <typename T, int D, int G, bool HYBRID, bool BLOCK, bool TOPP>
 __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendParams p) {
     using Ge = Geo<T, D, G>;
     constexpr int EPL = Ge::EPL, NDW = Ge::NDW, NK = Ge::NK, KPW = Ge::KPW, RS = Ge::RS;
@@ -582,11 +583,22 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         uint32_t list[HYBRID ? kMaxSelBlocks : 1];   // the kept blocks, ascending (at most floor(k / bs))
         alignas(16) unsigned long long comp[HYBRID ? kFastGroup : 1];   // the threshold digit's composites
     };
+    struct ToppLds {                          // the Top-p cut (topp_cut)
+        unsigned long long hist[HYBRID ? kToppBins : 1];   // a digit's share-weighted counts
+        uint32_t hcnt[HYBRID ? kToppBins : 1];             // and plain counts
+        unsigned long long lo[kWaves], hi[kWaves], tot[kWaves];
+        double zd[kWaves];
+        float fm[kWaves];
+        uint32_t cnt[kWaves];
+        unsigned long long above, cutv;
+        uint32_t digit, found, single;
+    };
     union Lds {
         StreamLds st;
         SelectLds se;
         FastLds fr;
         BlockLds bl;
+        ToppLds tp;
     };
     __shared__ __attribute__((aligned(16))) Lds u;
     __shared__ uint32_t s_pref[kMaxBH + 1];
@@ -671,6 +683,12 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         return;
     }
 
+    // A resolver's S entry: device-coherent in the Top-p build, whose cut
+    // reads the row back from its coherence point.
+    auto put_s = [&](int32_t* row, uint32_t i, int32_t v) {
+        if constexpr (TOPP) coherent_store(&row[i], v);
+        else row[i] = v;
+    };
     auto is_retr = [&](int hb) -> bool { return !HYBRID || ((p.role_bits >> (hb % p.Hkv)) & 1ull); };
     // Heads of a sequence with no context (out of contract, flagged in the
     // prologue) own no rows: workgroup bg % P writes their zero output and
@@ -895,9 +913,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         __syncthreads();
         if (ke == (uint32_t)n && p.sel_tkey == 0u) {      // every token (the threshold rule still filters)
             release_head();
-            for (uint32_t i = rlo + tid; i < min(rlo + rlen, (uint32_t)n); i += kAttendThreads) srow[i] = (int32_t)i;
+            for (uint32_t i = rlo + tid; i < min(rlo + rlen, (uint32_t)n); i += kAttendThreads) put_s(srow, i, (int32_t)i);
             if (whi == Wn)
-                for (int i = n + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
+                for (int i = n + tid; i < p.k; i += kAttendThreads) put_s(srow, i, -1);
         } else {
             constexpr int RC = 32;     // candidate slots per thread in the first load (8192 per head; fewer registers)
             constexpr int kB = 16;     // batch of later candidates
@@ -1196,7 +1214,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     while (bw) {
                         const int bit = __ffs(bw) - 1;
                         bw &= bw - 1u;
-                        srow[min(at, last)] = (int32_t)(rlo + (uint32_t)((i + q) * 32 + bit));   // at < ke unless the counts disagree (flagged below)
+                        put_s(srow, min(at, last), (int32_t)(rlo + (uint32_t)((i + q) * 32 + bit)));   // at < ke unless the counts disagree (flagged below)
                         ++at;
                     }
                 }
@@ -1204,7 +1222,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             if (whi == Wn) {           // the slice holding the end of the context
                 // (the threshold rule keeps the winners at or above its floor)
                 const uint32_t kept = p.sel_tkey ? min(below_total + total, ke) : ke;
-                for (int i = (int)kept + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
+                for (int i = (int)kept + tid; i < p.k; i += kAttendThreads) put_s(srow, i, -1);
                 if (tid == 0 && (p.sel_tkey ? below_total + total > ke : below_total + total != ke))
                     atomicOr(p.ws.err, 2u);
             }
@@ -1292,8 +1310,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
         }
         if (ke == (uint32_t)n && p.sel_tkey == 0u) {          // every token
-            for (uint32_t i = tid; i < (uint32_t)n; i += kAttendThreads) srow[i] = (int32_t)i;
-            for (int i = n + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
+            for (uint32_t i = tid; i < (uint32_t)n; i += kAttendThreads) put_s(srow, i, (int32_t)i);
+            for (int i = n + tid; i < p.k; i += kAttendThreads) put_s(srow, i, -1);
             __syncthreads();
             return false;
         }
@@ -1521,7 +1539,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                         tot += c;
                     }
                     for (uint32_t i = (uint32_t)lane; i < wcnt; i += 64u)
-                        srow[min(total + base + i, last)] = (int32_t)sbuf[i];
+                        put_s(srow, min(total + base + i, last), (int32_t)sbuf[i]);
                     total += tot;
                     __syncthreads();
                 }
@@ -1579,7 +1597,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         // padding after the kept tokens; the count must be k_eff (at most that
         // under the threshold rule)
         const uint32_t kept = min(total, ke);
-        for (int i = (int)kept + tid; i < p.k; i += kAttendThreads) srow[i] = -1;
+        for (int i = (int)kept + tid; i < p.k; i += kAttendThreads) put_s(srow, i, -1);
         if (tid == 0 && (tkey ? total > ke : total != ke)) atomicOr(p.ws.err, 2u);
         __syncthreads();
         LYCHEE_STAMP(kTrResolve0 + 7);
@@ -1742,6 +1760,248 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         __syncthreads();
     };
 
+    // Top-p (the Top-p reading of the digest's ablation of selection
+    // methods): the shortest prefix of the ranking (pooled score descending,
+    // index ascending) of the head's top-min(k, n) set whose share of the
+    // softmax of the pooled scores over the whole context reaches p.  Run by
+    // the workgroup that resolved the set, right after it:
+    // 1. the set (read back from S) and its keys (from the score buffer),
+    //    composites key << 18 | inverted index (larger = earlier in the
+    //    ranking); the normaliser parts of the head's workgroups, merged in
+    //    slot order into Z (slot tags restored to zero);
+    // 2. shares exp(.)/Z as 52-bit fixed point (integer sums do not depend
+    //    on order); a set holding less than p stays as it is;
+    // 3. an MSD radix of 8-bit digits from the highest bit where the
+    //    composites differ, share-weighted, until a digit's group holds one
+    //    composite: the cut;
+    // 4. the kept tokens compacted to the front of the row (ascending) by one
+    //    block scan, -1 after them.
+    auto topp_cut = [&](int hb, int n, int wf, int nw) __attribute__((always_inline)) {
+        int32_t* srow = p.S_out + (size_t)hb * p.k;
+        const uint32_t* sc = p.ws.score + (size_t)hb * p.max_ctx;
+        unsigned long long* cp = p.ws.cand + (size_t)hb * p.max_ctx;   // free once the set is resolved
+        const uint32_t ke = (uint32_t)min(p.k, max(n, 0));
+        const float cl = p.scale_log2 * (1.0f / (float)G);             // key units -> log2 of a share
+        wait_stores_complete();                                        // the row's coherent stores
+        __syncthreads();
+        const uint32_t per = (ke + kAttendThreads - 1u) / kAttendThreads;
+        const uint32_t e0 = (uint32_t)tid * per;
+        unsigned long long cr[kToppSlots];
+        unsigned long long clo = ~0ull, chi = 0ull;
+        bool bad = false;
+        uint32_t iv[kToppSlots];
+#pragma unroll
+        for (int e = 0; e < kToppSlots; ++e) {
+            const uint32_t i = e0 + (uint32_t)e;
+            iv[e] = ((uint32_t)e < per && i < ke) ? (uint32_t)coherent_load(&srow[i]) : 0u;
+        }
+        constexpr int kZPer = kMaxWG / kAttendThreads;                 // part slots per thread
+        uint32_t zt[kZPer], zm_[kZPer], zlo[kZPer], zhi[kZPer];
+#pragma unroll
+        for (int e = 0; e < kZPer; ++e) {
+            const int i = tid + kAttendThreads * e;
+            const uint32_t* zw = p.ws.zpart + 4 * (size_t)(wf + hb + i);
+            zt[e] = zm_[e] = zlo[e] = zhi[e] = 0u;
+            if (i < nw) {
+                zt[e] = coherent_load(&zw[0]);
+                zm_[e] = coherent_load(&zw[1]);
+                zlo[e] = coherent_load(&zw[2]);
+                zhi[e] = coherent_load(&zw[3]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < kToppSlots; ++e) {
+            const uint32_t i = e0 + (uint32_t)e;
+            cr[e] = 0ull;
+            if ((uint32_t)e < per && i < ke) {
+                bad |= iv[e] >= (uint32_t)n;
+                const uint32_t jj = iv[e] < (uint32_t)n ? iv[e] : 0u;
+                cr[e] = ((unsigned long long)coherent_load(&sc[jj]) << kIdxBits) | (unsigned long long)(kIdxMask - jj);
+                clo = cr[e] < clo ? cr[e] : clo;
+                chi = cr[e] > chi ? cr[e] : chi;
+            }
+        }
+        for (uint32_t e = kToppSlots; e < per; ++e) {                  // (more than kToppSlots per thread)
+            const uint32_t i = e0 + e;
+            if (i < ke) {
+                const uint32_t j = (uint32_t)coherent_load(&srow[i]);
+                bad |= j >= (uint32_t)n;
+                const uint32_t jj = j < (uint32_t)n ? j : 0u;
+                const unsigned long long c = ((unsigned long long)coherent_load(&sc[jj]) << kIdxBits) |
+                                             (unsigned long long)(kIdxMask - jj);
+                cp[i] = c;                                             // (read back by this thread only)
+                clo = c < clo ? c : clo;
+                chi = c > chi ? c : chi;
+            }
+        }
+        if (bad) atomicOr(p.ws.err, 2u);
+        // the composites' range and the largest pooled sum over the parts
+        float fmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kZPer; ++e)
+            if (zt[e] == (uint32_t)hb + 1u) fmax = fmaxf(fmax, __builtin_bit_cast(float, zm_[e]));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            fmax = fmaxf(fmax, __shfl_xor(fmax, o));
+            const unsigned long long ylo = __shfl_xor(clo, o), yhi = __shfl_xor(chi, o);
+            clo = ylo < clo ? ylo : clo;
+            chi = yhi > chi ? yhi : chi;
+        }
+        if (lane == 0) {
+            u.tp.lo[wave] = clo;
+            u.tp.hi[wave] = chi;
+            u.tp.fm[wave] = fmax;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) {
+            clo = u.tp.lo[wv] < clo ? u.tp.lo[wv] : clo;
+            chi = u.tp.hi[wv] > chi ? u.tp.hi[wv] : chi;
+            fmax = fmaxf(fmax, u.tp.fm[wv]);
+        }
+        // Z = sum of z_w 2^((m_w - fmax) c), the parts in slot order
+        double z = 0.0;
+        {
+            double zs = 0.0;
+#pragma unroll
+            for (int e = 0; e < kZPer; ++e) {
+                if (zt[e] == (uint32_t)hb + 1u) {
+                    const double zw = __builtin_bit_cast(double, ((unsigned long long)zhi[e] << 32) | zlo[e]);
+                    zs += zw * (double)exp2f((__builtin_bit_cast(float, zm_[e]) - fmax) * cl);
+                    coherent_store(&p.ws.zpart[4 * (size_t)(wf + hb + tid + kAttendThreads * e)], 0u);   // free again
+                }
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) zs += __shfl_xor(zs, o);
+            if (lane == 0) u.tp.zd[wave] = zs;
+            __syncthreads();
+#pragma unroll
+            for (int wv = 0; wv < kWaves; ++wv) z += u.tp.zd[wv];
+        }
+        const double inv_z = 1.0 / z;
+        auto weight = [&](unsigned long long c) -> unsigned long long {
+            const float f = key_float((uint32_t)(c >> kIdxBits));
+            return (unsigned long long)((double)exp2f((f - fmax) * cl) * inv_z * 0x1p52);
+        };
+        const unsigned long long target = p.topp_P;
+        unsigned long long wr[kToppSlots];
+#pragma unroll
+        for (int e = 0; e < kToppSlots; ++e) wr[e] = ((uint32_t)e < per && e0 + (uint32_t)e < ke) ? weight(cr[e]) : 0ull;
+        auto for_each_elem = [&](auto&& f) {
+#pragma unroll
+            for (int e = 0; e < kToppSlots; ++e)
+                if ((uint32_t)e < per && e0 + (uint32_t)e < ke) f(cr[e], wr[e]);
+            for (uint32_t e = kToppSlots; e < per; ++e)
+                if (e0 + e < ke) {
+                    const unsigned long long c = cp[e0 + e];
+                    f(c, weight(c));
+                }
+        };
+        // the set's whole share: below p, no prefix reaches p and the row stays
+        bool cut = true;
+        {
+            unsigned long long tot = 0;
+            for_each_elem([&](unsigned long long, unsigned long long wt) { tot += wt; });
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+            if (lane == 0) u.tp.tot[wave] = tot;
+            __syncthreads();
+            tot = 0;
+#pragma unroll
+            for (int wv = 0; wv < kWaves; ++wv) tot += u.tp.tot[wv];
+            cut = ke > 0u && tot >= target;
+        }
+        int shift = clo == chi ? 0 : 64 - __clzll((long long)(clo ^ chi));
+        unsigned long long prefix = chi >> shift, above = 0;
+        while (cut && shift > 0) {
+            const int bits = shift >= 8 ? 8 : shift;
+            const int nshift = shift - bits;
+            const uint32_t nbin = 1u << bits;
+            for (int i = tid; i < kToppBins; i += kAttendThreads) {
+                u.tp.hist[i] = 0ull;
+                u.tp.hcnt[i] = 0u;
+            }
+            __syncthreads();
+            for_each_elem([&](unsigned long long c, unsigned long long wt) {
+                if ((c >> shift) == prefix) {
+                    const uint32_t dg = (uint32_t)(c >> nshift) & (nbin - 1u);
+                    atomicAdd(&u.tp.hist[dg], wt);
+                    atomicAdd(&u.tp.hcnt[dg], 1u);
+                }
+            });
+            __syncthreads();
+            if (wave == 0) {
+                // crossing: lane l holds digits nbin-1-4l .. nbin-4-4l (descending
+                // rank 4l .. 4l+3); a wavefront scan gives each its running share
+                unsigned long long h[4], ls = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t t = 4u * (uint32_t)lane + (uint32_t)r;
+                    h[r] = t < nbin ? u.tp.hist[nbin - 1u - t] : 0ull;
+                    ls += h[r];
+                }
+                unsigned long long inc = ls;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const unsigned long long y = __shfl_up(inc, o);
+                    if (lane >= o) inc += y;
+                }
+                unsigned long long run = above + inc - ls, before = 0;
+                int found = -1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (found < 0 && run + h[r] >= target) {
+                        found = 4 * lane + r;
+                        before = run;
+                    }
+                    run += h[r];
+                }
+                const unsigned long long m = __ballot(found >= 0);
+                if (m == 0ull) {
+                    if (lane == 0) u.tp.found = 0u;
+                } else if (lane == __ffsll((long long)m) - 1) {
+                    const uint32_t dg = nbin - 1u - (uint32_t)found;
+                    u.tp.found = 1u;
+                    u.tp.digit = dg;
+                    u.tp.above = before;
+                    u.tp.single = u.tp.hcnt[dg] == 1u;
+                }
+            }
+            __syncthreads();
+            if (!u.tp.found) {                         // (the whole-share test above rules this out)
+                cut = false;
+                break;
+            }
+            prefix = (prefix << bits) | u.tp.digit;
+            above = u.tp.above;
+            shift = nshift;
+            const bool single = u.tp.single;
+            __syncthreads();                           // the digit's words are rewritten by the next pass
+            if (single && shift > 0) {
+                // the digit's group is one composite: it is the cut
+                for_each_elem([&](unsigned long long c, unsigned long long) {
+                    if ((c >> shift) == prefix) u.tp.cutv = c;
+                });
+                __syncthreads();
+                prefix = u.tp.cutv;
+                shift = 0;
+            }
+        }
+        if (cut) {
+            // the kept tokens (composites >= prefix) in their ascending order,
+            // compacted to the front of the row
+            uint32_t mine = 0;
+            for_each_elem([&](unsigned long long c, unsigned long long) { mine += c >= prefix ? 1u : 0u; });
+            uint32_t total;
+            uint32_t at = block_exclusive_scan(mine, s_wave, &total);
+            for_each_elem([&](unsigned long long c, unsigned long long) {
+                if (c >= prefix) srow[at++] = (int32_t)(kIdxMask - (uint32_t)(c & kIdxMask));
+            });
+            for (uint32_t i = total + (uint32_t)tid; i < ke; i += kAttendThreads) srow[i] = -1;
+        }
+        __syncthreads();
+    };
+
     // The heads of the range in order; a head whose top-k this workgroup
     // resolves (as its last selection arrival, or as its helper once the
     // range is done) waits in `pending` and is resolved at the top of the
@@ -1770,6 +2030,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #endif
                 resolve_topk(X, s_nctx[b], s_ke[b], 0u, 0u, (uint32_t)kResolveSlices, true);
             }
+            if constexpr (TOPP) topp_cut(X, s_nctx[b], wf, wl - wf + 1);
             // the hand-off word back to idle for the next launch where this
             // workgroup is the last party to touch it (1: it is the helper;
             // 5: the helper withdrew; 4 is restored by the helper)
@@ -2028,8 +2289,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     // 0), folded into the head's block words by atomic max.
                     // Thread t takes positions 16t .. 16t + 15, so at most two
                     // blocks; a block split between threads, passes or
-                    // workgroups gets one atomic from each part.  No top-k:
-                    // the rule-selection kernel reads the block words.
+                    // workgroups gets one atomic from each part.  No token
+                    // top-k: the head's block resolve reads the block words.
                     const uint32_t i0 = 16u * (uint32_t)tid;
                     if (i0 < len) {
                         uint32_t* bk = p.ws.bkey + (size_t)bg * (size_t)p.bkey_stride;
@@ -2060,9 +2321,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     continue;
                 }
                 // every key to the score buffer (read only if the bound below fails,
-                // or by the rule-selection kernel)
+                // or by the Top-p cut)
                 for (uint32_t i = tid; i < len; i += kAttendThreads) coherent_store(&sc[c_lo + i], u.st.keys[i]);
-                if (p.sel_zpart) {
+                if (TOPP) {
                     // The Top-p rule: this pass's part of the normaliser, with
                     // f the pooled sum a key encodes and c = scale_log2 / G:
                     // m = the pass's largest f, z = sum of 2^((f - m) c) (fp32
@@ -2196,10 +2457,13 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             // helper's (it restores 0 after the resolve), 4 the last arrival's
             // (the helper restores 0 when it comes), 5 helper withdrew (the
             // last arrival resolves and restores 0).
-            if (tid == 0 && p.sel_zpart && zm != -INFINITY) {   // the range's normaliser part (next kernel)
-                const unsigned long long zb = __builtin_bit_cast(unsigned long long, zs);
-                *reinterpret_cast<uint4*>(p.ws.zpart + 4 * (size_t)(w + bg)) =
-                    make_uint4((uint32_t)bg + 1u, __builtin_bit_cast(uint32_t, zm), (uint32_t)zb, (uint32_t)(zb >> 32));
+            if (TOPP && tid == 0 && zm != -INFINITY) {   // the range's normaliser part (device-coherent:
+                const unsigned long long zb = __builtin_bit_cast(unsigned long long, zs);   // the resolver reads it)
+                uint32_t* zw = p.ws.zpart + 4 * (size_t)(w + bg);
+                coherent_store(&zw[1], __builtin_bit_cast(uint32_t, zm));
+                coherent_store(&zw[2], (uint32_t)zb);
+                coherent_store(&zw[3], (uint32_t)(zb >> 32));
+                coherent_store(&zw[0], (uint32_t)bg + 1u);
             }
             if (tid == 0 && !BLOCK) coherent_store(&p.ws.wmeta[w + bg], w_count | (w_bound << 20));
             const int hw = helper_of(bg);   // (while the stores travel)
@@ -2408,38 +2672,39 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     LYCHEE_STAMP(kTrExit);
 }
 
-template <typename T, int D, int G, bool HYBRID, bool BLOCK>
+template <typename T, int D, int G, bool HYBRID, bool BLOCK, bool TOPP>
 hipError_t launch_one(const AttendParams& p, int cus, int per_cu, hipStream_t stream) {
     const int grid = attend_grid(cus, per_cu);
-    hipLaunchKernelGGL((attend_kernel<T, D, G, HYBRID, BLOCK>), dim3(grid), dim3(kAttendThreads), 0, stream, p);
+    hipLaunchKernelGGL((attend_kernel<T, D, G, HYBRID, BLOCK, TOPP>), dim3(grid), dim3(kAttendThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename T, int D, bool HYBRID, bool BLOCK>
+template <typename T, int D, bool HYBRID, bool BLOCK, bool TOPP>
 hipError_t launch_g(const AttendParams& p, int G, int cus, int per_cu, hipStream_t stream) {
     switch (G) {
-        case 1: return launch_one<T, D, 1, HYBRID, BLOCK>(p, cus, per_cu, stream);
-        case 2: return launch_one<T, D, 2, HYBRID, BLOCK>(p, cus, per_cu, stream);
-        case 4: return launch_one<T, D, 4, HYBRID, BLOCK>(p, cus, per_cu, stream);
-        case 8: return launch_one<T, D, 8, HYBRID, BLOCK>(p, cus, per_cu, stream);
+        case 1: return launch_one<T, D, 1, HYBRID, BLOCK, TOPP>(p, cus, per_cu, stream);
+        case 2: return launch_one<T, D, 2, HYBRID, BLOCK, TOPP>(p, cus, per_cu, stream);
+        case 4: return launch_one<T, D, 4, HYBRID, BLOCK, TOPP>(p, cus, per_cu, stream);
+        case 8: return launch_one<T, D, 8, HYBRID, BLOCK, TOPP>(p, cus, per_cu, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T, bool HYBRID, bool BLOCK>
+template <typename T, bool HYBRID, bool BLOCK, bool TOPP>
 hipError_t launch_d(const AttendParams& p, int D, int G, int cus, int per_cu, hipStream_t stream) {
-    if (D == 64) return launch_g<T, 64, HYBRID, BLOCK>(p, G, cus, per_cu, stream);
-    if (D == 128) return launch_g<T, 128, HYBRID, BLOCK>(p, G, cus, per_cu, stream);
+    if (D == 64) return launch_g<T, 64, HYBRID, BLOCK, TOPP>(p, G, cus, per_cu, stream);
+    if (D == 128) return launch_g<T, 128, HYBRID, BLOCK, TOPP>(p, G, cus, per_cu, stream);
     return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t launch_t(const AttendParams& p, int D, int G, bool hybrid, int cus, int per_cu, hipStream_t stream) {
-    if (!hybrid) return launch_d<T, false, false>(p, D, G, cus, per_cu, stream);
-    // the block rule has its own build of the kernel: its resolver stays out of
+    if (!hybrid) return launch_d<T, false, false, false>(p, D, G, cus, per_cu, stream);
+    // the block and Top-p rules have builds of their own: their cuts stay out of
     // the token top-k build's code and register allocation
-    return p.sel_block ? launch_d<T, true, true>(p, D, G, cus, per_cu, stream)
-                       : launch_d<T, true, false>(p, D, G, cus, per_cu, stream);
+    if (p.sel_block) return launch_d<T, true, true, false>(p, D, G, cus, per_cu, stream);
+    if (p.sel_zpart) return launch_d<T, true, false, true>(p, D, G, cus, per_cu, stream);
+    return launch_d<T, true, false, false>(p, D, G, cus, per_cu, stream);
 }
 
 }  // namespace
@@ -2447,7 +2712,7 @@ hipError_t launch_t(const AttendParams& p, int D, int G, bool hybrid, int cus, i
 hipError_t launch_attend(const AttendParams& p, int dtype, int D, int G, bool hybrid, int cus, int per_cu,
                          hipStream_t stream) {
 #ifdef LYCHEE_ONE_VARIANT   // compile-time probe of one variant's resources (not a library build)
-    return hybrid ? launch_one<BF16, 128, 4, true, false>(p, cus, per_cu, stream) : hipErrorInvalidValue;
+    return hybrid ? launch_one<BF16, 128, 4, true, false, false>(p, cus, per_cu, stream) : hipErrorInvalidValue;
 #endif
     if (dtype == 1) return launch_t<BF16>(p, D, G, hybrid, cus, per_cu, stream);
     if (dtype == 0) return launch_t<F32>(p, D, G, hybrid, cus, per_cu, stream);

@@ -10,6 +10,7 @@ namespace lychee {
 
 // ---------------------------------------------------------------- limits
 constexpr int kMaxWG = 2048;          // persistent attention workgroups per launch
+constexpr int kMaxSelBlocks = 4096;   // floor(k / bs) limit of the block rule (blocks listed in LDS)
 constexpr int kMaxBH = 1024;          // batch * n_kv_heads
 constexpr int kMaxKvHeads = 64;       // role mask travels as one 64-bit word
 constexpr int kMaxCtx = 1 << 18;      // token index fits 18 bits (select bitmap in LDS)
@@ -145,7 +146,7 @@ struct Workspace {
                                  //                           bound << 20 (retrieval heads)
     uint32_t* score;             // [BH * max_ctx]            every selection key of a retrieval head
                                  //                           (read when a head's bounds fail, and by
-                                 //                           the rule-selection kernel)
+                                 //                           the Top-p cut)
     float* crec_ml;              // [CW * 32 G * 2]           correction attention: chunk partials
     float* crec_o;               // [CW * 32 G * D]           (CW = max(512, BH) workgroups)
     // ---- zero-initialised region (restored to zero by every call) ----
@@ -162,7 +163,7 @@ struct Workspace {
     uint32_t* zpart;             // [(kMaxWG + BH) * 4]       Top-p: per (workgroup w, head bg) at w + bg:
                                  //                           bg + 1 (0 = empty), the largest pooled sum m
                                  //                           and the sum of 2^((f - m) c) as a double
-                                 //                           (tags restored to 0 by the rule kernel)
+                                 //                           (tags restored to 0 by the Top-p cut)
     uint32_t* hready;            // [BH]                      helper hand-off of a retrieval head's
                                  //                           resolve: 1 arrivals complete (the helper
                                  //                           resolves), 2 the helper withdrew
@@ -267,9 +268,12 @@ struct AttendParams {
     // selection key into ws.bkey (no token top-k, no score buffer), and the
     // head's last selection arrival or its helper cuts the blocks.
     uint32_t sel_block;
-    // Top-p rule: retrieval heads also publish their part of the normaliser
-    // (ws.zpart) for the rule-selection kernel.
+    // Top-p rule (the kernel's TOPP build): retrieval heads also publish their
+    // part of the normaliser (ws.zpart), and the head's last selection arrival
+    // or its helper cuts the top-k set to its Top-p prefix; topp_P is p as
+    // 52-bit fixed point.
     uint32_t sel_zpart;
+    unsigned long long topp_P;
     int32_t bkey_stride;    // block words per head in ws.bkey
     // Phase timestamps (the LYCHEE_TRACE build only; null otherwise):
     // kTraceSlots 64-bit words per workgroup and launch, at

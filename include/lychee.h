@@ -136,8 +136,8 @@ lychee_status lychee_decode_layer(lychee_handle* h,
  *              over all n tokens reaches p = param in (0, 1], at most
  *              min(k, n) tokens.  Shares are fp32 exponentials over an fp64
  *              normaliser, summed as 52-bit fixed point, so a cut within that
- *              rounding of p may land one token either side.  Runs a second
- *              kernel after the attention kernel.
+ *              rounding of p may land one token either side.  Cut inside the
+ *              attention kernel, after the top-min(k, n) set.
  *   BLOCK      block-granular selection (the digest's kernel works on blocks
  *              of 64 tokens and states no rule for a block's score): blocks of
  *              bs = param tokens (16, 32, 64, 128 or 256; the last block may
@@ -161,8 +161,7 @@ enum {
  * (theta for RATIO, tau for THRESHOLD, p for TOPP, the block size for BLOCK,
  * unused for TOPK).  Returns LYCHEE_ERR_INVALID_ARG for an unknown rule, theta
  * or p outside (0, 1], a NaN tau or a block size or k the block rule does not
- * take, after which nothing is enqueued.  With profile events set, `stop`
- * follows the second kernel of TOPP. */
+ * take, after which nothing is enqueued. */
 lychee_status lychee_decode_layer_select(lychee_handle* h,
                                          const void* q, const void* k_cache, const void* v_cache,
                                          const uint8_t* role_mask, const int32_t* S_in, int32_t* S_out,

@@ -220,8 +220,8 @@ def _raw(t):
 
 def test_loop_kernels_replay_from_a_graph():
     """Append, correction, and a hybrid layer under the Top-p and the block
-    rule (each with the rule-selection kernel after the attention kernel) and
-    under the Ratio and Threshold rules (in the attention kernel), captured once into a HIP graph: three replays, with the cache and n_ctx
+    rule (each cut in its own build of the attention kernel) and under the
+    Ratio and Threshold rules, captured once into a HIP graph: three replays, with the cache and n_ctx
     restored eagerly between them, each reproduce the eager run bitwise, and
     the eager layers meet the parity bar against the oracle."""
     import torch
