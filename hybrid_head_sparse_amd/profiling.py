@@ -30,8 +30,8 @@ ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 ATTEND_SRC = os.path.join(HERE, "csrc", "attend.hip")
 KERNEL_SOURCES = (ATTEND_SRC, os.path.join(HERE, "csrc", "common.hpp"))
-HYBRID_KERNEL = "attend_kernel<lychee::(anonymous namespace)::BF16, 128, 4, true, false>"
-DENSE_KERNEL = "attend_kernel<lychee::(anonymous namespace)::BF16, 128, 4, false, false>"
+HYBRID_KERNEL = "attend_kernel<lychee::(anonymous namespace)::BF16, 128, 4, true, false, false>"
+DENSE_KERNEL = "attend_kernel<lychee::(anonymous namespace)::BF16, 128, 4, false, false, false>"
 
 
 def kernel_code_digest(texts=None) -> str:
@@ -103,9 +103,10 @@ def write_stats(trace: str, wl: str, cmds: str) -> None:
         f.write("| kernel | calls | total ms | average us | min us | max us |\n|---|---|---|---|---|---|\n")
         for name, calls, tot, avg, mn, mx in rows:
             f.write(f"| `{name}` | {calls} | {tot / 1e6:.3f} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |\n")
-        f.write("\nThe hybrid kernel (`..., true, false>`) runs every layer of the step (layer 0 all retrieval, the\n"
-                "others mixed) in the eager, graph and event-timed passes of the benchmark; the dense kernel\n"
-                "(`..., false, false>`) is the all-retrieval comparison; `..., true, true>` is the block rule's build.  The hybrid average over a step's layers is\n"
+        f.write("\nThe hybrid kernel's token top-k build (`..., true, false, false>`) runs every layer of the step\n"
+                "(layer 0 all retrieval, the others mixed) in the eager, graph and event-timed passes of the\n"
+                "benchmark; the dense build (`..., false, false, false>`) is the all-retrieval comparison (the\n"
+                "block and Top-p rules have builds of their own).  The hybrid average over a step's layers is\n"
                 "what the benchmark reports as `roofline.avg_launch_us` (its step time over the layers).\n")
 
 
