@@ -10,13 +10,14 @@
 //
 // Work pooling.  All (head, row) work -- a row is one streamed key of a
 // retrieval head or one gathered S row of a sparse head -- is laid on one cost
-// axis (a gathered row weighs twice a streamed one) and cut into equal
-// contiguous ranges, one per persistent workgroup, as the digest's kernel
-// description asks (equal-size splits spread over all thread blocks).  Each
-// range yields one partial (m, l, o) record per head it touches; the last
-// workgroup of each group of 32 merges the group's records by the
-// log-sum-exp rule and the last group merger writes the output (partials +
-// LSE combine, fused into the same launch).
+// axis (a gathered row weighs 1.5 streamed ones by default) and dealt to the
+// persistent workgroups head by head, in proportion to cost, as the digest's
+// kernel description asks (the work spread evenly over all thread blocks); a
+// head's rows are split evenly among its workgroups.  Each range yields one
+// partial (m, l, o) record per head it touches; the last workgroup of each
+// group of 32 merges the group's records by the log-sum-exp rule and the last
+// group merger writes the output (partials + LSE combine, fused into the same
+// launch).
 //
 // Selection without a second pass over the scores.  While streaming, every
 // retrieval workgroup keeps the order-preserving 32-bit keys of its pooled
@@ -24,16 +25,18 @@
 // live).  When a pass is done it takes its own bound: the digit where its
 // histogram reaches its share of k plus a margin.  It adds its counts from
 // that bound up to the head's global histogram and appends its keys from the
-// bound up to the head's candidate list.  The resolver reads the final
-// histogram: if no pass's bound exceeds the head's threshold digit T, the
-// histogram is exact from T up and the candidates hold every key from T up
-// (otherwise it re-reads every key).  It keeps the candidates above T,
-// resolves the ones in digit T by the rest of the key and then the token
-// index (larger key first, lower index first: a strict total order, so the
-// result is exact and unique), marks the winners in an LDS bitmap of the
-// context and writes them in ascending order.  The resolve runs on the head's
-// first arrival whose range ends in the head (it waits, bounded, for the last
-// one) or on the last arrival, whichever votes first.
+// bound up, in position order, to its own region of the head's candidate
+// list.  The head's last selection arrival hands the resolve to a paired idle
+// workgroup (or does it itself): from the final histogram it takes the
+// threshold digit T; if a workgroup's bound lies above T its rows are
+// recounted and its candidates replaced (every key re-read as a last
+// resort); the candidates above T win, and those in digit T are ranked by
+// the rest of the key and then the token index (larger key first, lower index
+// first: a strict total order, so the result is exact and unique); the
+// winners are written to S in ascending order.  The Ratio and Threshold rules
+// change the count and the floor of this cut; the block and Top-p rules have
+// builds of their own (block maxima instead of the token top-k; the top-k set
+// cut to its Top-p prefix after the resolve).
 //
 // CDNA4 mapping of the streaming loop: a key row is spread over 16 lanes (one
 // DPP row), each lane issuing one 8-32 byte load per row; the G query heads of
