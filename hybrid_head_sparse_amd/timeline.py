@@ -171,6 +171,9 @@ def main(argv=None) -> int:
     ap.add_argument("--out", default=None)
     ap.add_argument("--raw", default=None, help="also save the raw stamps of the last repetition (.npy)")
     ap.add_argument("--from-raw", default=None, help="report on saved stamps (.npy) instead of running")
+    ap.add_argument("--rule", default="topk", choices=["topk", "ratio", "threshold", "topp", "block"],
+                    help="selection rule of the retrieval heads (as bench.py --rule)")
+    ap.add_argument("--param", type=float, default=0.0, help="the rule's parameter (as bench.py --param)")
     a = ap.parse_args(argv)
     sys.path.insert(0, ROOT)
     import numpy as np
@@ -213,7 +216,8 @@ def main(argv=None) -> int:
         for l in range(w.layers):
             h.set_trace(buf, l)
             x = dev[l]
-            h.decode_layer(x["q"], x["k"], x["v"], roles[l], S[l - 1] if l else None, S[l], outs[l], n_ctx, k)
+            h.decode_layer(x["q"], x["k"], x["v"], roles[l], S[l - 1] if l else None, S[l], outs[l], n_ctx, k,
+                           rule=a.rule, param=a.param)
         ev1.record()
         torch.cuda.synchronize()
         spans.append(ev0.elapsed_time(ev1) * 1e3)
