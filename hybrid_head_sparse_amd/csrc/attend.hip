@@ -1793,25 +1793,27 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         unsigned long long clo = ~0ull, chi = 0ull;
         bool bad = false;
         uint32_t iv[kToppSlots];
+        // Every load is issued on every path (indices clamped, results masked):
+        // loads under per-slot branches each get a wait of their own, which
+        // serialises the rounds.  ke >= 1 and nw >= 1 here.
 #pragma unroll
-        for (int e = 0; e < kToppSlots; ++e) {
-            const uint32_t i = e0 + (uint32_t)e;
-            iv[e] = ((uint32_t)e < per && i < ke) ? (uint32_t)coherent_load(&srow[i]) : 0u;
-        }
+        for (int e = 0; e < kToppSlots; ++e)
+            iv[e] = (uint32_t)coherent_load(&srow[min(e0 + (uint32_t)e, ke - 1u)]);
         constexpr int kZPer = kMaxWG / kAttendThreads;                 // part slots per thread
         uint32_t zt[kZPer], zm_[kZPer], zlo[kZPer], zhi[kZPer];
 #pragma unroll
         for (int e = 0; e < kZPer; ++e) {
             const int i = tid + kAttendThreads * e;
-            const uint32_t* zw = p.ws.zpart + 4 * (size_t)(wf + hb + i);
-            zt[e] = zm_[e] = zlo[e] = zhi[e] = 0u;
-            if (i < nw) {
-                zt[e] = coherent_load(&zw[0]);
-                zm_[e] = coherent_load(&zw[1]);
-                zlo[e] = coherent_load(&zw[2]);
-                zhi[e] = coherent_load(&zw[3]);
-            }
+            const uint32_t* zw = p.ws.zpart + 4 * (size_t)(wf + hb + min(i, nw - 1));
+            zt[e] = coherent_load(&zw[0]);
+            zm_[e] = coherent_load(&zw[1]);
+            zlo[e] = coherent_load(&zw[2]);
+            zhi[e] = coherent_load(&zw[3]);
+            if (i >= nw) zt[e] = 0u;                                   // not this head's part
         }
+        uint32_t kk[kToppSlots];
+#pragma unroll
+        for (int e = 0; e < kToppSlots; ++e) kk[e] = coherent_load(&sc[iv[e] < (uint32_t)n ? iv[e] : 0u]);
 #pragma unroll
         for (int e = 0; e < kToppSlots; ++e) {
             const uint32_t i = e0 + (uint32_t)e;
@@ -1819,7 +1821,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             if ((uint32_t)e < per && i < ke) {
                 bad |= iv[e] >= (uint32_t)n;
                 const uint32_t jj = iv[e] < (uint32_t)n ? iv[e] : 0u;
-                cr[e] = ((unsigned long long)coherent_load(&sc[jj]) << kIdxBits) | (unsigned long long)(kIdxMask - jj);
+                cr[e] = ((unsigned long long)kk[e] << kIdxBits) | (unsigned long long)(kIdxMask - jj);
                 clo = cr[e] < clo ? cr[e] : clo;
                 chi = cr[e] > chi ? cr[e] : chi;
             }
