@@ -776,11 +776,19 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     // once its own work is done; the r-th retrieval head (head order, heads
     // with rows) is paired with the r-th such workgroup, taken as the first
     // workgroup of a sparse head that has at least two (so its range lies
-    // inside that head).  The pairing follows from the boundaries alone, so
-    // every workgroup derives the same one (wavefront-parallel ballots).
+    // inside that head).  A retrieval head left without one (more retrieval
+    // heads than such workgroups, as in a layer of retrieval heads only) is
+    // helped by its own first workgroup when it spans at least two: that
+    // workgroup is idle once its range is recorded, and it takes the resolve
+    // while the head's last selection arrival records and merges (if it is
+    // that arrival itself, it offers the resolve to itself and takes it
+    // back, as when no helper comes).  The pairing follows from the
+    // boundaries alone, so every workgroup derives the same one
+    // (wavefront-parallel ballots).
     auto helper_cand = [&](int a) -> bool { return a < BH && !is_retr(a) && s_first[a + 1] >= s_first[a] + 2u; };
     auto has_rows = [&](int a) -> bool { return a < BH && s_pref[a + 1] > s_pref[a]; };
     auto needs_help = [&](int a) -> bool { return has_rows(a) && is_retr(a); };
+    auto own_helper = [&](int a) -> bool { return s_first[a + 1] >= s_first[a] + 2u; };   // a < BH
     auto kth_bit = [](unsigned long long m, int k) -> int {   // position of the k-th set bit (k from 0)
         for (int t = 0; t < k; ++t) m &= m - 1ull;
         return __ffsll((long long)m) - 1;
@@ -798,7 +806,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             if (seen + c > r) return (int)s_first[base + kth_bit(m, r - seen)];
             seen += c;
         }
-        return -1;
+        return own_helper(X) ? (int)s_first[X] : -1;
     };
     auto helped_by = [&](int ww) -> int {      // the head workgroup ww helps, or -1
         int r = -1, seen = 0;
@@ -813,7 +821,25 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
             seen += __popcll(m);
         }
-        if (r < 0) return -1;
+        if (r < 0) {
+            // the first workgroup of a retrieval head that no gathered-rows
+            // workgroup helps: its rank among those heads is at least the
+            // number of gathered-rows helpers
+            int ncand = 0;
+            for (int base = 0; base < BH; base += 64) ncand += __popcll(__ballot(helper_cand(base + lane)));
+            for (int base = 0, seen = 0; base < BH; base += 64) {
+                const int i = base + lane;
+                const bool nh = needs_help(i);
+                const unsigned long long m = __ballot(nh);
+                const unsigned long long me = __ballot(nh && s_first[i] == (uint32_t)ww && own_helper(i));
+                if (me) {
+                    const int bit = __ffsll((long long)me) - 1;
+                    return seen + __popcll(m & ((1ull << bit) - 1ull)) >= ncand ? base + bit : -1;
+                }
+                seen += __popcll(m);
+            }
+            return -1;
+        }
         for (int base = 0, seen = 0; base < BH; base += 64) {
             const unsigned long long m = __ballot(needs_help(base + lane));
             const int c = __popcll(m);
