@@ -1799,7 +1799,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     //    ranking); the normaliser parts of the head's workgroups, merged in
     //    slot order into Z (slot tags restored to zero);
     // 2. shares exp(.)/Z as 52-bit fixed point (integer sums do not depend
-    //    on order); a set holding less than p stays as it is;
+    //    on order); a set holding less than p stays as it is (decided from
+    //    Z alone, before the set is read, when k_eff shares of the largest
+    //    pooled sum stay below p);
     // 3. an MSD radix of 8-bit digits from the highest bit where the
     //    composites differ, share-weighted, until a digit's group holds one
     //    composite: the cut;
@@ -1811,20 +1813,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         unsigned long long* cp = p.ws.cand + (size_t)hb * p.max_ctx;   // free once the set is resolved
         const uint32_t ke = (uint32_t)min(p.k, max(n, 0));
         const float cl = p.scale_log2 * (1.0f / (float)G);             // key units -> log2 of a share
-        wait_stores_complete();                                        // the row's coherent stores
-        __syncthreads();
-        const uint32_t per = (ke + kAttendThreads - 1u) / kAttendThreads;
-        const uint32_t e0 = (uint32_t)tid * per;
-        unsigned long long cr[kToppSlots];
-        unsigned long long clo = ~0ull, chi = 0ull;
-        bool bad = false;
-        uint32_t iv[kToppSlots];
-        // Every load is issued on every path (indices clamped, results masked):
-        // loads under per-slot branches each get a wait of their own, which
-        // serialises the rounds.  ke >= 1 and nw >= 1 here.
-#pragma unroll
-        for (int e = 0; e < kToppSlots; ++e)
-            iv[e] = (uint32_t)coherent_load(&srow[min(e0 + (uint32_t)e, ke - 1u)]);
+        // The parts of the head's workgroups first: their loads travel while
+        // the row's coherent stores are acknowledged (vmcnt counts both).
         constexpr int kZPer = kMaxWG / kAttendThreads;                 // part slots per thread
         uint32_t zt[kZPer], zm_[kZPer], zlo[kZPer], zhi[kZPer];
 #pragma unroll
@@ -1837,6 +1827,61 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             zhi[e] = coherent_load(&zw[3]);
             if (i >= nw) zt[e] = 0u;                                   // not this head's part
         }
+        wait_stores_complete();                                        // the row's coherent stores
+        __syncthreads();
+        const uint32_t per = (ke + kAttendThreads - 1u) / kAttendThreads;
+        const uint32_t e0 = (uint32_t)tid * per;
+        uint32_t iv[kToppSlots];
+        // Every load is issued on every path (indices clamped, results masked):
+        // loads under per-slot branches each get a wait of their own, which
+        // serialises the rounds.  ke >= 1 and nw >= 1 here.
+#pragma unroll
+        for (int e = 0; e < kToppSlots; ++e)
+            iv[e] = (uint32_t)coherent_load(&srow[min(e0 + (uint32_t)e, ke - 1u)]);
+        // the largest pooled sum over the parts
+        float fmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kZPer; ++e)
+            if (zt[e] == (uint32_t)hb + 1u) fmax = fmaxf(fmax, __builtin_bit_cast(float, zm_[e]));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) fmax = fmaxf(fmax, __shfl_xor(fmax, o));
+        if (lane == 0) u.tp.fm[wave] = fmax;
+        __syncthreads();
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) fmax = fmaxf(fmax, u.tp.fm[wv]);
+        // Z = sum of z_w 2^((m_w - fmax) c), the parts in slot order
+        double z = 0.0;
+        {
+            double zs = 0.0;
+#pragma unroll
+            for (int e = 0; e < kZPer; ++e) {
+                if (zt[e] == (uint32_t)hb + 1u) {
+                    const double zw = __builtin_bit_cast(double, ((unsigned long long)zhi[e] << 32) | zlo[e]);
+                    zs += zw * (double)exp2f((__builtin_bit_cast(float, zm_[e]) - fmax) * cl);
+                    coherent_store(&p.ws.zpart[4 * (size_t)(wf + hb + tid + kAttendThreads * e)], 0u);   // free again
+                }
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) zs += __shfl_xor(zs, o);
+            if (lane == 0) u.tp.zd[wave] = zs;
+            __syncthreads();
+#pragma unroll
+            for (int wv = 0; wv < kWaves; ++wv) z += u.tp.zd[wv];
+        }
+        const double inv_z = 1.0 / z;
+        // No cut possible: no pooled sum exceeds fmax, so every share is at
+        // most 1 / Z (2^-16 of slack covers exp2f's rounding at arguments
+        // <= 0), and ke such shares stay below p.  The row stays as the
+        // resolver wrote it, exactly as the share sums below would decide.
+        // (z, inv_z and the parts are the same in every thread: the
+        // decision is uniform.)
+        if (cl > 0.0f && (double)ke * ((1.0 + 0x1p-16) * inv_z * 0x1p52) < (double)p.topp_P) {
+            __syncthreads();
+            return;
+        }
+        unsigned long long cr[kToppSlots];
+        unsigned long long clo = ~0ull, chi = 0ull;
+        bool bad = false;
         uint32_t kk[kToppSlots];
 #pragma unroll
         for (int e = 0; e < kToppSlots; ++e) kk[e] = coherent_load(&sc[iv[e] < (uint32_t)n ? iv[e] : 0u]);
@@ -1866,14 +1911,9 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
         }
         if (bad) atomicOr(p.ws.err, 2u);
-        // the composites' range and the largest pooled sum over the parts
-        float fmax = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < kZPer; ++e)
-            if (zt[e] == (uint32_t)hb + 1u) fmax = fmaxf(fmax, __builtin_bit_cast(float, zm_[e]));
+        // the composites' range
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
-            fmax = fmaxf(fmax, __shfl_xor(fmax, o));
             const unsigned long long ylo = __shfl_xor(clo, o), yhi = __shfl_xor(chi, o);
             clo = ylo < clo ? ylo : clo;
             chi = yhi > chi ? yhi : chi;
@@ -1881,35 +1921,13 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         if (lane == 0) {
             u.tp.lo[wave] = clo;
             u.tp.hi[wave] = chi;
-            u.tp.fm[wave] = fmax;
         }
         __syncthreads();
 #pragma unroll
         for (int wv = 0; wv < kWaves; ++wv) {
             clo = u.tp.lo[wv] < clo ? u.tp.lo[wv] : clo;
             chi = u.tp.hi[wv] > chi ? u.tp.hi[wv] : chi;
-            fmax = fmaxf(fmax, u.tp.fm[wv]);
         }
-        // Z = sum of z_w 2^((m_w - fmax) c), the parts in slot order
-        double z = 0.0;
-        {
-            double zs = 0.0;
-#pragma unroll
-            for (int e = 0; e < kZPer; ++e) {
-                if (zt[e] == (uint32_t)hb + 1u) {
-                    const double zw = __builtin_bit_cast(double, ((unsigned long long)zhi[e] << 32) | zlo[e]);
-                    zs += zw * (double)exp2f((__builtin_bit_cast(float, zm_[e]) - fmax) * cl);
-                    coherent_store(&p.ws.zpart[4 * (size_t)(wf + hb + tid + kAttendThreads * e)], 0u);   // free again
-                }
-            }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) zs += __shfl_xor(zs, o);
-            if (lane == 0) u.tp.zd[wave] = zs;
-            __syncthreads();
-#pragma unroll
-            for (int wv = 0; wv < kWaves; ++wv) z += u.tp.zd[wv];
-        }
-        const double inv_z = 1.0 / z;
         auto weight = [&](unsigned long long c) -> unsigned long long {
             const float f = key_float((uint32_t)(c >> kIdxBits));
             return (unsigned long long)((double)exp2f((f - fmax) * cl) * inv_z * 0x1p52);

@@ -227,3 +227,25 @@ def test_block_rule_tied_block_maxima(n):
         assert np.all(S[0, g, m * bs:] == -1)
     compare_layer(out, S, x, role, None, lens, k, "bf16", rule="block", param=bs)
     handle.check_device_errors()
+
+
+def test_topp_rule_no_cut_decided_from_the_normaliser():
+    """p above k_eff / Z for every head, with Z the pooled softmax's
+    normaliser relative to its largest term: no share exceeds 1 / Z, so no
+    prefix of the top-k set reaches p and the cut keeps the whole set.  The
+    kernel decides this from the normaliser alone, before reading the set
+    back.  The case is checked to satisfy the bound (oracle scores), then S
+    and the outputs are compared with the oracle as for every rule, and
+    every retrieval head keeps min(k, n) tokens."""
+    lens = synth.n_ctx(RAGGED)
+    for layer in (0, 1):
+        x = synth.layer_inputs(RAGGED, layer)
+        _, _, s = oracle.layer(x["q"], x["k"], x["v"], np.ones(RAGGED.n_kv_heads, np.uint8), None, lens,
+                               RAGGED.k, want_scores=True)
+        for b, n in enumerate(lens):
+            sb = s[b, :, :int(n)]
+            z = np.exp(sb - sb.max(axis=1, keepdims=True)).sum(axis=1)
+            assert np.all(min(RAGGED.k, int(n)) / z < 0.25), "the case must satisfy the no-cut bound at p = 0.3"
+    S0, _ = _two_layers(RAGGED, "topp", 0.3)
+    for b, n in enumerate(lens):
+        assert np.all((S0[b] != -1).sum(axis=1) == min(RAGGED.k, int(n)))
