@@ -27,7 +27,8 @@
 // that bound up to the head's global histogram and appends its keys from the
 // bound up, in position order, to its own region of the head's candidate
 // list.  The head's last selection arrival hands the resolve to a paired idle
-// workgroup (or does it itself): from the final histogram it takes the
+// workgroup (a gathered-rows one, else the head's own first workgroup) or
+// does it itself: from the final histogram it takes the
 // threshold digit T; if a workgroup's bound lies above T its rows are
 // recounted and its candidates replaced (every key re-read as a last
 // resort); the candidates above T win, and those in digit T are ranked by

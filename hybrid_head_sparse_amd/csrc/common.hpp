@@ -165,8 +165,9 @@ struct Workspace {
                                  //                           and the sum of 2^((f - m) c) as a double
                                  //                           (tags restored to 0 by the Top-p cut)
     uint32_t* hready;            // [BH]                      helper hand-off of a retrieval head's
-                                 //                           resolve: 1 arrivals complete (the helper
-                                 //                           resolves), 2 the helper withdrew
+                                 //                           resolve: 0 idle, 3 helper waiting, 6
+                                 //                           offered, 1 the helper's, 4 the last
+                                 //                           arrival's, 5 the helper withdrew
     uint32_t* err;               // [4]
     void* zero_begin;
     size_t zero_bytes;
