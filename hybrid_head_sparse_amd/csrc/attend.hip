@@ -412,6 +412,7 @@ __device__ __forceinline__ unsigned long long digit_first_key(uint32_t d) {
 constexpr int kWords = kMaxCtx / 32;                     // context bitmap words
 constexpr int kHistPerThread = kHistBins / kAttendThreads;
 constexpr int kToppBins = 256;                           // Top-p cut: 8-bit radix digits
+constexpr int kToppCopies = 4;                           // Top-p cut: interleaved histogram copies (lane & 3)
 constexpr int kToppSlots = 16;                           // Top-p cut: set entries a thread holds in registers
 constexpr int kCandPerThread = kCandLds / kAttendThreads;
 
@@ -588,14 +589,13 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         alignas(16) unsigned long long comp[HYBRID ? kFastGroup : 1];   // the threshold digit's composites
     };
     struct ToppLds {                          // the Top-p cut (topp_cut)
-        unsigned long long hist[HYBRID ? kToppBins : 1];   // a digit's share-weighted counts
-        uint32_t hcnt[HYBRID ? kToppBins : 1];             // and plain counts
+        unsigned long long hist[HYBRID ? kToppBins * kToppCopies : 1];   // a digit's share-weighted counts
         unsigned long long lo[kWaves], hi[kWaves], tot[kWaves];
         double zd[kWaves];
         float fm[kWaves];
         uint32_t cnt[kWaves];
         unsigned long long above, cutv;
-        uint32_t digit, found, single;
+        uint32_t digit, found;
     };
     union Lds {
         StreamLds st;
@@ -1967,16 +1967,16 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             const int bits = shift >= 8 ? 8 : shift;
             const int nshift = shift - bits;
             const uint32_t nbin = 1u << bits;
-            for (int i = tid; i < kToppBins; i += kAttendThreads) {
-                u.tp.hist[i] = 0ull;
-                u.tp.hcnt[i] = 0u;
-            }
+            for (int i = tid; i < kToppBins * kToppCopies; i += kAttendThreads) u.tp.hist[i] = 0ull;
             __syncthreads();
+            // the set's keys share their leading digits, so most lanes of a
+            // wavefront add to one or two bins: lane & 3 picks one of four
+            // interleaved copies, so fewer lanes meet on one address
+            const uint32_t cpy = (uint32_t)lane & (uint32_t)(kToppCopies - 1);
             for_each_elem([&](unsigned long long c, unsigned long long wt) {
                 if ((c >> shift) == prefix) {
                     const uint32_t dg = (uint32_t)(c >> nshift) & (nbin - 1u);
-                    atomicAdd(&u.tp.hist[dg], wt);
-                    atomicAdd(&u.tp.hcnt[dg], 1u);
+                    atomicAdd(&u.tp.hist[dg * kToppCopies + cpy], wt);
                 }
             });
             __syncthreads();
@@ -1987,7 +1987,11 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t t = 4u * (uint32_t)lane + (uint32_t)r;
-                    h[r] = t < nbin ? u.tp.hist[nbin - 1u - t] : 0ull;
+                    h[r] = 0ull;
+                    if (t < nbin) {
+#pragma unroll
+                        for (int q = 0; q < kToppCopies; ++q) h[r] += u.tp.hist[(nbin - 1u - t) * kToppCopies + q];
+                    }
                     ls += h[r];
                 }
                 unsigned long long inc = ls;
@@ -2014,7 +2018,6 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                     u.tp.found = 1u;
                     u.tp.digit = dg;
                     u.tp.above = before;
-                    u.tp.single = u.tp.hcnt[dg] == 1u;
                 }
             }
             __syncthreads();
@@ -2025,9 +2028,20 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             prefix = (prefix << bits) | u.tp.digit;
             above = u.tp.above;
             shift = nshift;
-            const bool single = u.tp.single;
-            __syncthreads();                           // the digit's words are rewritten by the next pass
-            if (single && shift > 0) {
+            // the composites of the new prefix, counted (one is the cut)
+            if (shift > 0) {
+                uint32_t mine = 0;
+                for_each_elem([&](unsigned long long c, unsigned long long) { mine += (c >> shift) == prefix ? 1u : 0u; });
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) mine += (uint32_t)__shfl_xor((int)mine, o);
+                if (lane == 0) u.tp.cnt[wave] = mine;
+            }
+            __syncthreads();                           // (and the digit's words are rewritten by the next pass)
+            uint32_t grp = 0;
+#pragma unroll
+            for (int wv = 0; wv < kWaves; ++wv) grp += u.tp.cnt[wv];
+            const bool single = shift > 0 && grp == 1u;
+            if (single) {
                 // the digit's group is one composite: it is the cut
                 for_each_elem([&](unsigned long long c, unsigned long long) {
                     if ((c >> shift) == prefix) u.tp.cutv = c;
