@@ -113,3 +113,17 @@ def test_qwen3_ties_full_steps_with_planted_boundary_groups():
             del x
     for h in handles:
         h.check_device_errors()
+
+
+# Many short heads: batch 16 x 8 KV heads, contexts 2000-8192.  In layer 0
+# (all retrieval) a head gets one to three workgroups, so a head's top-k is
+# resolved by its own first workgroup (the last arrival elsewhere, or that
+# workgroup itself when it arrives last) or, on a one-workgroup head, by its
+# only workgroup; in layer 1 no sparse head has the two workgroups a
+# gathered-rows helper needs, so every retrieval head uses its own.
+MANY_HEADS = synth.Workload("many_heads_b16", 41, 16, 2, 32, 8, 128, 8192, 512, "bf16", 3,
+                            ctx_range=(2000, 8192))
+
+
+def test_many_short_heads_resolved_on_their_own_workgroups():
+    _chain(MANY_HEADS, MANY_HEADS.layers)

@@ -249,3 +249,15 @@ def test_topp_rule_no_cut_decided_from_the_normaliser():
     S0, _ = _two_layers(RAGGED, "topp", 0.3)
     for b, n in enumerate(lens):
         assert np.all((S0[b] != -1).sum(axis=1) == min(RAGGED.k, int(n)))
+
+
+@pytest.mark.parametrize("rule,param", [("topp", 0.02), ("topp", 0.3), ("block", 16), ("ratio", 0.05)])
+def test_rules_on_many_short_heads(rule, param):
+    """Batch 16 x 8 KV heads, contexts 2000-8192: the Top-p cut (p = 0.02
+    cuts; p = 0.3 is decided from the normaliser) and the block cut run on
+    heads of one to three workgroups, resolved by the head's own first
+    workgroup or its last arrival."""
+    w = synth.Workload("select_many_heads", 42, 16, 2, 32, 8, 128, 8192, 512, "bf16", 4, ctx_range=(2000, 8192))
+    S0, _ = _two_layers(w, rule, param)
+    kept = (S0 != -1).sum(axis=2)
+    assert kept.min() >= 1 and kept.max() <= w.k
