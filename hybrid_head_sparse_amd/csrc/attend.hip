@@ -591,8 +591,6 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     struct ToppLds {                          // the Top-p cut (topp_cut)
         unsigned long long hist[HYBRID ? kToppBins * kToppCopies : 1];   // a digit's share-weighted counts
         unsigned long long lo[kWaves], hi[kWaves], tot[kWaves];
-        double zd[kWaves];
-        float fm[kWaves];
         uint32_t cnt[kWaves];
         unsigned long long above, cutv;
         uint32_t digit, found;
@@ -617,6 +615,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
     __shared__ int s_rel;
     __shared__ uint32_t s_ceq;        // resolver: threshold-digit composites appended so far
     __shared__ unsigned long long s_cut;   // resolver: the smallest winning full_order of the threshold digit
+    __shared__ uint32_t s_lds_set;         // Top-p build: the resolved set is in LDS (one batch; see topp_cut)
     __shared__ uint32_t s_zk[kWaves];      // Top-p normaliser: per-wavefront largest key, then sum
     __shared__ double s_zd[kWaves];
 
@@ -1315,6 +1314,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             r0 = (max(s_bound[wf + i], h0) - h0) / kCostRetrieval;
             r1 = (min(s_bound[wf + i + 1], hh1) - h0) / kCostRetrieval;
         };
+        if (TOPP && tid == 0) s_lds_set = 0u;
         __syncthreads();
         // 1. histogram (restored to zero once read) and words
         {
@@ -1554,7 +1554,8 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                             const uint32_t fl = f + 64u * e2 + (uint32_t)lane;
                             const bool wv = fl < f1 && full_order(kk[e2], ii[e2]) >= cut;
                             const unsigned long long bw = __ballot(wv);
-                            if (wv) sbuf[wcnt + (uint32_t)__popcll(bw & lt_mask)] = ii[e2];
+                            // (the Top-p build keeps the entry, so the set's keys stay at hand)
+                            if (wv) sbuf[wcnt + (uint32_t)__popcll(bw & lt_mask)] = TOPP ? fl : ii[e2];
                             wcnt += (uint32_t)__popcll(bw);
                         }
                     }
@@ -1569,7 +1570,7 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
                         tot += c;
                     }
                     for (uint32_t i = (uint32_t)lane; i < wcnt; i += 64u)
-                        put_s(srow, min(total + base + i, last), (int32_t)sbuf[i]);
+                        put_s(srow, min(total + base + i, last), (int32_t)(TOPP ? u.fr.idx[sbuf[i]] : sbuf[i]));
                     total += tot;
                     __syncthreads();
                 }
@@ -1629,6 +1630,10 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         const uint32_t kept = min(total, ke);
         for (int i = (int)kept + tid; i < p.k; i += kAttendThreads) put_s(srow, i, -1);
         if (tid == 0 && (tkey ? total > ke : total != ke)) atomicOr(p.ws.err, 2u);
+        // one batch: its winners' entries stay in u.fr.map (wavefront v's at
+        // v kFastBatch / kWaves, u.fr.jc[v] of them) beside their keys and
+        // indices in u.fr.key / u.fr.idx, in the order of S
+        if (TOPP && tid == 0) s_lds_set = (nbatch == 1u && total == ke) ? 1u : 0u;
         __syncthreads();
         LYCHEE_STAMP(kTrResolve0 + 7);
         return false;
@@ -1814,6 +1819,10 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         unsigned long long* cp = p.ws.cand + (size_t)hb * p.max_ctx;   // free once the set is resolved
         const uint32_t ke = (uint32_t)min(p.k, max(n, 0));
         const float cl = p.scale_log2 * (1.0f / (float)G);             // key units -> log2 of a share
+        // The set from the resolver's LDS when it resolved in one batch (no
+        // wait for the row's stores, no load rounds for S and its keys), else
+        // read back from S and the score buffer.
+        const bool lds_set = s_lds_set != 0u && ke <= (uint32_t)(kToppSlots * kAttendThreads);
         // The parts of the head's workgroups first: their loads travel while
         // the row's coherent stores are acknowledged (vmcnt counts both).
         constexpr int kZPer = kMaxWG / kAttendThreads;                 // part slots per thread
@@ -1828,17 +1837,21 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             zhi[e] = coherent_load(&zw[3]);
             if (i >= nw) zt[e] = 0u;                                   // not this head's part
         }
-        wait_stores_complete();                                        // the row's coherent stores
+        if (!lds_set) wait_stores_complete();                         // the row's coherent stores
         __syncthreads();
         const uint32_t per = (ke + kAttendThreads - 1u) / kAttendThreads;
         const uint32_t e0 = (uint32_t)tid * per;
-        uint32_t iv[kToppSlots];
-        // Every load is issued on every path (indices clamped, results masked):
-        // loads under per-slot branches each get a wait of their own, which
-        // serialises the rounds.  ke >= 1 and nw >= 1 here.
+        uint32_t iv[kToppSlots], kk[kToppSlots];
+        if (!lds_set) {
+            // Every load is issued on every path (indices clamped, results
+            // masked): loads under per-slot branches each get a wait of their
+            // own, which serialises the rounds.  ke >= 1 and nw >= 1 here.
 #pragma unroll
-        for (int e = 0; e < kToppSlots; ++e)
-            iv[e] = (uint32_t)coherent_load(&srow[min(e0 + (uint32_t)e, ke - 1u)]);
+            for (int e = 0; e < kToppSlots; ++e)
+                iv[e] = (uint32_t)coherent_load(&srow[min(e0 + (uint32_t)e, ke - 1u)]);
+        }
+        // (up to the decision below, only the per-wavefront words s_zk and
+        // s_zd are written: u.fr, where the set may be, stays as it is)
         // the largest pooled sum over the parts
         float fmax = -INFINITY;
 #pragma unroll
@@ -1846,10 +1859,10 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             if (zt[e] == (uint32_t)hb + 1u) fmax = fmaxf(fmax, __builtin_bit_cast(float, zm_[e]));
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) fmax = fmaxf(fmax, __shfl_xor(fmax, o));
-        if (lane == 0) u.tp.fm[wave] = fmax;
+        if (lane == 0) s_zk[wave] = __builtin_bit_cast(uint32_t, fmax);
         __syncthreads();
 #pragma unroll
-        for (int wv = 0; wv < kWaves; ++wv) fmax = fmaxf(fmax, u.tp.fm[wv]);
+        for (int wv = 0; wv < kWaves; ++wv) fmax = fmaxf(fmax, __builtin_bit_cast(float, s_zk[wv]));
         // Z = sum of z_w 2^((m_w - fmax) c), the parts in slot order
         double z = 0.0;
         {
@@ -1864,10 +1877,10 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             }
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) zs += __shfl_xor(zs, o);
-            if (lane == 0) u.tp.zd[wave] = zs;
+            if (lane == 0) s_zd[wave] = zs;
             __syncthreads();
 #pragma unroll
-            for (int wv = 0; wv < kWaves; ++wv) z += u.tp.zd[wv];
+            for (int wv = 0; wv < kWaves; ++wv) z += s_zd[wv];
         }
         const double inv_z = 1.0 / z;
         // No cut possible: no pooled sum exceeds fmax, so every share is at
@@ -1880,12 +1893,29 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
             __syncthreads();
             return;
         }
+        if (lds_set) {
+            // entry i of S: wavefront v's part of u.fr.map, after the parts
+            // of the wavefronts before it
+            constexpr uint32_t kQ = kFastBatch / kWaves;
+            const uint32_t b1 = u.fr.jc[0], b2 = b1 + u.fr.jc[1], b3 = b2 + u.fr.jc[2];
+#pragma unroll
+            for (int e = 0; e < kToppSlots; ++e) {
+                const uint32_t i = min(e0 + (uint32_t)e, ke - 1u);
+                const uint32_t v = (i >= b1 ? 1u : 0u) + (i >= b2 ? 1u : 0u) + (i >= b3 ? 1u : 0u);
+                const uint32_t base = v == 0u ? 0u : (v == 1u ? b1 : (v == 2u ? b2 : b3));
+                const uint32_t f = u.fr.map[v * kQ + (i - base)];
+                iv[e] = u.fr.idx[f];
+                kk[e] = u.fr.key[f];
+            }
+            __syncthreads();                                           // (the cut's words reuse u.fr.map)
+        }
         unsigned long long cr[kToppSlots];
         unsigned long long clo = ~0ull, chi = 0ull;
         bool bad = false;
-        uint32_t kk[kToppSlots];
+        if (!lds_set) {
 #pragma unroll
-        for (int e = 0; e < kToppSlots; ++e) kk[e] = coherent_load(&sc[iv[e] < (uint32_t)n ? iv[e] : 0u]);
+            for (int e = 0; e < kToppSlots; ++e) kk[e] = coherent_load(&sc[iv[e] < (uint32_t)n ? iv[e] : 0u]);
+        }
 #pragma unroll
         for (int e = 0; e < kToppSlots; ++e) {
             const uint32_t i = e0 + (uint32_t)e;
@@ -2053,7 +2083,12 @@ __global__ void __launch_bounds__(kAttendThreads) attend_kernel(const AttendPara
         }
         if (cut) {
             // the kept tokens (composites >= prefix) in their ascending order,
-            // compacted to the front of the row
+            // compacted to the front of the row (after the resolver's stores
+            // to it are complete: the same words are written again)
+            if (lds_set) {
+                wait_stores_complete();
+                __syncthreads();
+            }
             uint32_t mine = 0;
             for_each_elem([&](unsigned long long c, unsigned long long) { mine += c >= prefix ? 1u : 0u; });
             uint32_t total;
